@@ -1,0 +1,274 @@
+"""CPU oracle for the ring collectives -- TEST INFRASTRUCTURE ONLY.
+
+This package is the yardstick the GPU library is checked against.  It is
+plain, slow and single-threaded on purpose, shares no code with the GPU path
+and never imports it.  Only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the product path must never
+route through it.
+
+The ring arithmetic lives in ``ring_oracle.c`` (plain C, built with
+``-ffp-contract=off`` and without fast-math so every fp32 addition is one
+IEEE-754 round-to-nearest-even addition).  This module loads it with ctypes
+and wraps it for NumPy arrays shaped ``(P, n)`` (rank-major, rank r in row r).
+
+The GEMM part of the GEMM + reduce-scatter oracle uses NumPy's float64 matrix
+product as a library step (products of bf16 values are exact in fp64; the
+4096-term sums carry ~1e-16 relative error), rounds once to fp32, and then runs
+the same fp32 ring reduce-scatter as the collectives.
+
+Sources followed (page title, section):
+  * "Pallas TPU Distributed Collectives 复习文档": 0.1 ring model, 1 right
+    shift (ppermute), 2 all_gather, 4.4 psum_scatter semantics.
+  * "TPU 与分布式通信原语": reduce-scatter / all-gather ring kernels;
+    collective matmul (matmul then reduce-scatter over row blocks).
+  * "全归约 3：Ring——每步大小恒定": The idea; Walkthrough (index arithmetic,
+    one signal row per round); Edge cases.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ring_oracle.c")
+_LIB = os.path.join(_HERE, "libring_oracle.so")
+
+_CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+           "-fno-unsafe-math-optimizations", "-shared", "-fPIC"]
+
+
+def build(force: bool = False) -> str:
+    """Compile ring_oracle.c with gcc into libring_oracle.so (in place)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        for name, args in {
+            "oracle_ppermute": [vp, vp, i32, sz],
+            "oracle_reduce_scatter_f32": [vp, vp, i32, sz, i32],
+            "oracle_reduce_scatter_i32": [vp, vp, i32, sz, i32],
+            "oracle_all_gather": [vp, i32, sz, sz, i32],
+            "oracle_all_gather_place": [vp, vp, i32, sz, sz],
+            "oracle_all_reduce_f32": [vp, vp, i32, sz],
+            "oracle_all_reduce_i32": [vp, vp, i32, sz],
+            "oracle_reduce_scatter_bf16": [vp, vp, vp, i32, sz, i32],
+            "oracle_all_reduce_bf16": [vp, vp, vp, i32, sz],
+            "oracle_bf16_from_f32_array": [vp, vp, sz],
+            "oracle_rank_sum_f64_f32": [vp, i32, sz, vp, vp],
+            "oracle_rank_sum_f64_bf16": [vp, i32, sz, vp, vp],
+        }.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        lib.oracle_bf16_from_f32_array.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError("oracle: invalid arguments to %s" % what)
+
+
+def _ranks(x: np.ndarray, dtype) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.dtype != dtype or x.ndim < 2:
+        raise TypeError("expected a (P, ...) array of %s, got %s %s" % (dtype, x.dtype, x.shape))
+    return x
+
+
+# --------------------------------------------------------------------------
+# collectives on (P, n) arrays
+# --------------------------------------------------------------------------
+def ppermute(x: np.ndarray) -> np.ndarray:
+    """Right shift: out[r] = x[left(r)] (every rank sends its buffer right)."""
+    x = np.ascontiguousarray(x)
+    P = x.shape[0]
+    out = np.empty_like(x)
+    _check(_load().oracle_ppermute(_ptr(x), _ptr(out), P, x[0].nbytes), "ppermute")
+    return out
+
+
+def reduce_scatter(x: np.ndarray, rounds: int | None = None) -> np.ndarray:
+    """Ring reduce-scatter state after `rounds` rounds (default P-1).
+
+    fp32 and int32 inputs.  Returns the whole (P, n) state; after all P-1
+    rounds chunk r of row r is the sum over ranks (the other chunks hold
+    partial sums)."""
+    x = np.ascontiguousarray(x)
+    P = x.shape[0]
+    n = x[0].size
+    rounds = P - 1 if rounds is None else rounds
+    out = np.empty_like(x)
+    lib = _load()
+    if x.dtype == np.float32:
+        rc = lib.oracle_reduce_scatter_f32(_ptr(x), _ptr(out), P, n, rounds)
+    elif x.dtype == np.int32:
+        rc = lib.oracle_reduce_scatter_i32(_ptr(x), _ptr(out), P, n, rounds)
+    else:
+        raise TypeError("reduce_scatter: fp32 or int32 (bf16: reduce_scatter_bf16)")
+    _check(rc, "reduce_scatter")
+    return out
+
+
+def all_gather(state: np.ndarray, rounds: int | None = None) -> np.ndarray:
+    """Ring all-gather applied to `state` (chunk r of row r is rank r's piece)."""
+    out = np.array(state, copy=True, order="C")
+    P = out.shape[0]
+    rounds = P - 1 if rounds is None else rounds
+    _check(_load().oracle_all_gather(_ptr(out), P, out[0].size, out.itemsize, rounds),
+           "all_gather")
+    return out
+
+
+def all_gather_pieces(pieces: np.ndarray, fill=0) -> np.ndarray:
+    """All-gather from compact pieces (P, C): returns (P, P*C)."""
+    pieces = np.ascontiguousarray(pieces)
+    P = pieces.shape[0]
+    C = pieces[0].size
+    state = np.full((P, P * C), fill, dtype=pieces.dtype)
+    _check(_load().oracle_all_gather_place(_ptr(pieces), _ptr(state), P, P * C,
+                                           pieces.itemsize), "all_gather_place")
+    return all_gather(state)
+
+
+def all_reduce(x: np.ndarray) -> np.ndarray:
+    """Ring all-reduce: reduce-scatter then all-gather (fp32 / int32)."""
+    x = np.ascontiguousarray(x)
+    P = x.shape[0]
+    out = np.empty_like(x)
+    lib = _load()
+    if x.dtype == np.float32:
+        rc = lib.oracle_all_reduce_f32(_ptr(x), _ptr(out), P, x[0].size)
+    elif x.dtype == np.int32:
+        rc = lib.oracle_all_reduce_i32(_ptr(x), _ptr(out), P, x[0].size)
+    else:
+        raise TypeError("all_reduce: fp32 or int32 (bf16: all_reduce_bf16)")
+    _check(rc, "all_reduce")
+    return out
+
+
+# --------------------------------------------------------------------------
+# bf16 (stored as uint16 bit patterns)
+# --------------------------------------------------------------------------
+def bf16_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even) -> uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_bf16_from_f32_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def reduce_scatter_bf16(x: np.ndarray, rounds: int | None = None):
+    """bf16 ring reduce-scatter with an fp32 carry; returns (dst, carry)."""
+    x = _ranks(x, np.uint16)
+    P = x.shape[0]
+    rounds = P - 1 if rounds is None else rounds
+    dst = np.empty_like(x)
+    carry = np.empty(x.shape, dtype=np.float32)
+    _check(_load().oracle_reduce_scatter_bf16(_ptr(x), _ptr(dst), _ptr(carry), P,
+                                              x[0].size, rounds), "reduce_scatter_bf16")
+    return dst, carry
+
+
+def all_reduce_bf16(x: np.ndarray) -> np.ndarray:
+    """bf16 ring all-reduce: fp32 carry, one rounding at the owner, bf16 gather."""
+    x = _ranks(x, np.uint16)
+    P = x.shape[0]
+    dst = np.empty_like(x)
+    carry = np.empty(x.shape, dtype=np.float32)
+    _check(_load().oracle_all_reduce_bf16(_ptr(x), _ptr(dst), _ptr(carry), P, x[0].size),
+           "all_reduce_bf16")
+    return dst
+
+
+# --------------------------------------------------------------------------
+# plain references for tolerance checks
+# --------------------------------------------------------------------------
+def rank_sum_f64(x: np.ndarray, bf16: bool = False):
+    """(sum, sum of magnitudes) over ranks in rank order, in fp64."""
+    x = np.ascontiguousarray(x)
+    P = x.shape[0]
+    n = x[0].size
+    s = np.empty(n, dtype=np.float64)
+    m = np.empty(n, dtype=np.float64)
+    lib = _load()
+    if bf16:
+        rc = lib.oracle_rank_sum_f64_bf16(_ptr(_ranks(x, np.uint16)), P, n, _ptr(s), _ptr(m))
+    else:
+        rc = lib.oracle_rank_sum_f64_f32(_ptr(_ranks(x, np.float32)), P, n, _ptr(s), _ptr(m))
+    _check(rc, "rank_sum_f64")
+    return s.reshape(x.shape[1:]), m.reshape(x.shape[1:])
+
+
+# --------------------------------------------------------------------------
+# GEMM + reduce-scatter
+# --------------------------------------------------------------------------
+def gemm_products_f32(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """C_q = A_q @ B_q for every rank q: bf16 inputs (uint16 bits), fp64
+    product, one rounding to fp32.  A: (P, M, K), B: (P, K, N) -> (P, M, N)."""
+    A = _ranks(A, np.uint16)
+    B = _ranks(B, np.uint16)
+    P = A.shape[0]
+    out = np.empty((P, A.shape[1], B.shape[2]), dtype=np.float32)
+    for q in range(P):
+        a = bf16_to_f32(A[q]).astype(np.float64)
+        b = bf16_to_f32(B[q]).astype(np.float64)
+        out[q] = (a @ b).astype(np.float32)
+    return out
+
+
+def gemm_reduce_scatter(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """Rank r's output: rows [r*M/P, (r+1)*M/P) of sum_q A_q B_q, where the
+    per-rank products are fp32 and the sum over ranks follows the fp32 ring
+    reduce-scatter over row-block chunks ("TPU 与分布式通信原语", collective
+    matmul: full local matmul, then the ring reduce-scatter).  Returns
+    (P, M/P, N) fp32."""
+    Cq = gemm_products_f32(A, B)
+    P, M, N = Cq.shape
+    if M % P:
+        raise ValueError("M must be divisible by P")
+    st = reduce_scatter(Cq.reshape(P, M * N))
+    rows = M // P
+    return np.stack([st[r].reshape(M, N)[r * rows:(r + 1) * rows] for r in range(P)])
+
+
+def gemm_reduce_scatter_rows_f64(A: np.ndarray, B: np.ndarray, r: int, rows) -> tuple:
+    """Sampled reference: for output rank r and local row indices `rows`,
+    the fp64 value of sum_q A_q[i,:] @ B_q and the magnitude denominator
+    sum_q |A_q[i,:]| @ |B_q| (each exact product is counted once)."""
+    A = _ranks(A, np.uint16)
+    B = _ranks(B, np.uint16)
+    P, M, _ = A.shape
+    g = np.asarray(rows) + r * (M // P)
+    s = 0.0
+    m = 0.0
+    for q in range(P):
+        a = bf16_to_f32(A[q][g]).astype(np.float64)
+        b = bf16_to_f32(B[q]).astype(np.float64)
+        s = s + a @ b
+        m = m + np.abs(a) @ np.abs(b)
+    return s, m

@@ -1,0 +1,126 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module only draws random numbers and lays them out; it holds none of the
+collectives' arithmetic.  Everything is NumPy ``default_rng(seed)`` (PCG64),
+drawn in rank order as if one array of shape ``(P, ...)`` were drawn at once.
+Large draws are made rank by rank from the same generator, which yields the
+same stream as one draw (NumPy fills arrays sequentially).
+
+bf16 values are the round-to-nearest-even images of fp32 draws, produced with
+torch's fp32 -> bf16 conversion and handled here as uint16 bit patterns.
+
+Workloads (the pages draw their inputs with JAX keys that cannot be replayed
+here, so only shape, type and distribution follow them):
+  * small fp32 ring: P ranks, each an fp32 (8, 512) array, uniform [0, 1),
+    seed 0 -- the (8, 128 * devices) shape of "Pallas TPU Distributed
+    Collectives 复习文档" section 1.3 at four devices;
+  * int32 ring: P ranks, each int32 (8, 128 * P), uniform integers in
+    [-1000, 1000], seed 1;
+  * fp32 bandwidth workload: P = 8, 64 Mi fp32 per rank, normal(0, 1), seed 2;
+  * bf16 gradient-bucket workload: P = 16, 128 Mi bf16 per rank,
+    normal(0, 0.01), seed 3;
+  * GEMM + reduce-scatter: P = 4, A_q and B_q bf16 4096 x 4096,
+    normal(0, 1/64), seed 4 (all A's first, then all B's).
+
+Two-dimensional per-rank arrays of shape (R, w * P) are stored chunk-major:
+chunk c (a flat, contiguous run of R * w elements) is column block c of the
+logical array, as in the chunk-major layout helpers of "TPU 与分布式通信原语"
+(collective matmul section).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SEED_SMALL_F32 = 0
+SEED_I32 = 1
+SEED_F32_BW = 2
+SEED_BF16 = 3
+SEED_GEMM = 4
+
+
+# ---------------------------------------------------------------- layout
+def to_chunk_major(x: np.ndarray, P: int) -> np.ndarray:
+    """(ranks, R, w*P) logical arrays -> (ranks, P*R*w) flat chunk-major."""
+    ranks, R, W = x.shape
+    w = W // P
+    return np.ascontiguousarray(x.reshape(ranks, R, P, w).transpose(0, 2, 1, 3)).reshape(ranks, -1)
+
+
+def from_chunk_major(flat: np.ndarray, P: int, R: int) -> np.ndarray:
+    """(ranks, P*R*w) chunk-major -> (ranks, R, w*P) logical arrays."""
+    ranks = flat.shape[0]
+    w = flat.shape[1] // (P * R)
+    return np.ascontiguousarray(flat.reshape(ranks, P, R, w).transpose(0, 2, 1, 3)).reshape(ranks, R, P * w)
+
+
+def bf16_bits(x_f32: np.ndarray) -> np.ndarray:
+    """fp32 array -> bf16 (RNE) as uint16 bit patterns, via torch."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x_f32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------- workloads
+def small_f32(P: int, shape=(8, 512)) -> np.ndarray:
+    """Logical per-rank fp32 arrays, uniform [0, 1), seed 0 -> (P, R, W)."""
+    rng = np.random.default_rng(SEED_SMALL_F32)
+    return rng.random((P, *shape), dtype=np.float32)
+
+
+def ring_i32(P: int, rows: int = 8, width_per_rank: int = 128) -> np.ndarray:
+    """Logical per-rank int32 arrays (rows, width_per_rank * P), uniform
+    integers in [-1000, 1000], seed 1 -> (P, rows, width_per_rank * P)."""
+    rng = np.random.default_rng(SEED_I32)
+    return rng.integers(-1000, 1000, size=(P, rows, width_per_rank * P),
+                        endpoint=True, dtype=np.int32)
+
+
+def normal_f32(P: int, n: int, seed: int = SEED_F32_BW, std: float = 1.0,
+               out: np.ndarray | None = None) -> np.ndarray:
+    """(P, n) fp32 normal(0, std) drawn rank by rank from one generator."""
+    rng = np.random.default_rng(seed)
+    if out is None:
+        out = np.empty((P, n), dtype=np.float32)
+    for r in range(P):
+        rng.standard_normal(n, dtype=np.float32, out=out[r])
+        if std != 1.0:
+            out[r] *= np.float32(std)
+    return out
+
+
+def normal_bf16(P: int, n: int, seed: int = SEED_BF16, std: float = 1e-2,
+                slab: int = 1 << 24) -> np.ndarray:
+    """(P, n) bf16 bit patterns: RNE of fp32 normal(0, std) draws, made in
+    slabs from one generator (same stream as one (P, n) draw)."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((P, n), dtype=np.uint16)
+    buf = np.empty(min(slab, max(n, 1)), dtype=np.float32)
+    for r in range(P):
+        for lo in range(0, n, slab):
+            m = min(slab, n - lo)
+            rng.standard_normal(m, dtype=np.float32, out=buf[:m])
+            buf[:m] *= np.float32(std)
+            out[r, lo:lo + m] = bf16_bits(buf[:m])
+    return out
+
+
+def gemm_operands(P: int = 4, M: int = 4096, N: int = 4096, K: int = 4096,
+                  std: float = 1.0 / 64, seed: int = SEED_GEMM):
+    """(A, B) as bf16 bit patterns: A (P, M, K), B (P, K, N), normal(0, std);
+    all A's are drawn first, then all B's."""
+    rng = np.random.default_rng(seed)
+    A = np.empty((P, M, K), dtype=np.uint16)
+    B = np.empty((P, K, N), dtype=np.uint16)
+    for q in range(P):
+        a = rng.standard_normal((M, K), dtype=np.float32) * np.float32(std)
+        A[q] = bf16_bits(a)
+    for q in range(P):
+        b = rng.standard_normal((K, N), dtype=np.float32) * np.float32(std)
+        B[q] = bf16_bits(b)
+    return A, B
+
+
+def small_int_bf16(rng: np.random.Generator, shape, lo: int = -4, hi: int = 4) -> np.ndarray:
+    """Integer-valued bf16 bit patterns (uniform integers in [lo, hi]); every
+    such value is exact in bf16."""
+    return bf16_bits(rng.integers(lo, hi, size=shape, endpoint=True).astype(np.float32))

@@ -1,0 +1,397 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself --
+a worked example printed on the pages, a brute-force or library definition, an
+invariant of the schedule, a closed form, or a proven error bound.
+
+Pages (title, section):
+  * "Pallas TPU Distributed Collectives 复习文档" -- 1.4 right-shift table,
+    2.5 all_gather slot table, 4.4 psum_scatter semantics.
+  * "全归约 3：Ring——每步大小恒定" -- The idea (after P-1 rounds each rank
+    holds the chunk it owns), Walkthrough (the partial a rank stores is what
+    it forwards in the next round; the left neighbour index), Edge cases
+    (P = 2 masks rotation bugs; run P >= 4 and check every chunk position;
+    results differ from a plain sum only by reduction order).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from ring_collectives_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+PS = [1, 2, 3, 4, 5, 8, 16]
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _rank_id_data(P, n, dtype=np.int32):
+    """x[r] filled with r + 1: any value names the rank it came from."""
+    return np.repeat(np.arange(1, P + 1, dtype=dtype)[:, None], n, axis=1)
+
+
+# ---------------------------------------------------------------- ppermute
+def test_ppermute_matches_page_table():
+    rows = _golden_rows("ppermute_p4.txt")
+    P = len(rows)
+    out = oracle.ppermute(_rank_id_data(P, 64))
+    for dev, init, to, final in rows:
+        d = int(dev[1:])
+        assert init == "x%d" % d
+        # the device it sends to receives its data
+        assert np.all(out[int(to[1:])] == d + 1)
+        assert np.all(out[d] == int(final[1:]) + 1)
+
+
+@pytest.mark.parametrize("P", PS)
+def test_ppermute_is_roll(P):
+    x = inputs.small_f32(P).reshape(P, -1)
+    np.testing.assert_array_equal(oracle.ppermute(x), np.roll(x, 1, axis=0))
+
+
+def test_ppermute_p2_swaps():
+    x = _rank_id_data(2, 8)
+    out = oracle.ppermute(x)
+    assert np.all(out[0] == 2) and np.all(out[1] == 1)
+
+
+# ---------------------------------------------------------------- all-gather
+def test_all_gather_matches_page_slot_table():
+    rows = _golden_rows("all_gather_p4_slots.txt")
+    P, C = 4, 16
+    pieces = (np.arange(P, dtype=np.int32) + 1)[:, None].repeat(C, axis=1)
+    for after, *devs in rows:
+        if after == "init":
+            state = np.zeros((P, P * C), dtype=np.int32)
+        else:
+            t = int(after[4:])
+            # page's step 0 = local copy of the own shard + the first round
+            state = np.zeros((P, P * C), dtype=np.int32)
+            state = oracle.all_gather(_placed(pieces, state), rounds=t + 1)
+        for d, slots in enumerate(devs):
+            for c, want in enumerate(slots.split(",")):
+                got = state[d, c * C:(c + 1) * C]
+                if want == "-":
+                    assert np.all(got == 0), (after, d, c)
+                else:
+                    assert np.all(got == int(want[1:]) + 1), (after, d, c)
+
+
+def _placed(pieces, state):
+    P, C = pieces.shape
+    st = state.copy()
+    for r in range(P):
+        st[r, r * C:(r + 1) * C] = pieces[r]
+    return st
+
+
+@pytest.mark.parametrize("P", PS)
+def test_all_gather_is_concatenation(P):
+    x = inputs.ring_i32(P)                       # logical (P, 8, 128 P)
+    pieces = x[:, :, :128].reshape(P, -1)        # any per-rank piece
+    out = oracle.all_gather_pieces(pieces)
+    want = np.concatenate(list(pieces))
+    for r in range(P):
+        np.testing.assert_array_equal(out[r], want)
+
+
+# ---------------------------------------------------------------- reduce-scatter
+@pytest.mark.parametrize("P", PS)
+def test_reduce_scatter_is_psum_scatter_int32(P):
+    """Owner r ends with block r of the sum over devices (psum_scatter's
+    meaning, section 4.4 of the Pallas page); brute force in int64."""
+    x = inputs.ring_i32(P)                       # logical (P, 8, 128 P)
+    flat = inputs.to_chunk_major(x, P)
+    st = oracle.reduce_scatter(flat)
+    total = x.astype(np.int64).sum(axis=0)       # (8, 128 P)
+    C = flat.shape[1] // P
+    for r in range(P):
+        block = total[:, r * 128:(r + 1) * 128]  # column block r
+        got = st[r, r * C:(r + 1) * C].reshape(8, 128)
+        np.testing.assert_array_equal(got.astype(np.int64), block)
+
+
+@pytest.mark.parametrize("P", [2, 3, 4, 5, 8, 16])
+def test_reduce_scatter_contributor_sets(P):
+    """With x_q = 2^q every partial sum is the bit set of its contributors.
+
+    Checks, round by round, the facts the ring page states in words: each rank
+    changes exactly one chunk per round; the new value is the chunk its left
+    neighbour stored in the previous round plus its own contribution (at round
+    0 the neighbour's input); after P-1 rounds chunk c is complete at exactly
+    one rank, rank c, and every (rank, chunk) was visited at most once."""
+    C = 3
+    x = np.repeat((1 << np.arange(P, dtype=np.int64)).astype(np.int32)[:, None], P * C, axis=1)
+    full = (1 << P) - 1
+    prev = x.copy()
+    prev_changed = {}
+    for s in range(P - 1):
+        cur = oracle.reduce_scatter(x, rounds=s + 1)
+        changed = {}
+        for r in range(P):
+            diff = [c for c in range(P)
+                    if np.any(cur[r, c * C:(c + 1) * C] != prev[r, c * C:(c + 1) * C])]
+            assert len(diff) == 1, (s, r, diff)
+            c = diff[0]
+            changed[r] = c
+            left = (r - 1 + P) % P
+            if s > 0:
+                assert prev_changed[left] == c   # forwards what it stored last round
+            want = prev[left, c * C] | (1 << r)
+            assert prev[left, c * C] & (1 << r) == 0
+            assert np.all(cur[r, c * C:(c + 1) * C] == want)
+        prev, prev_changed = cur, changed
+    for r in range(P):
+        for c in range(P):
+            v = prev[r, c * C]
+            assert (v == full) == (r == c), (r, c, v)
+
+
+def test_reduce_scatter_p1_is_identity():
+    x = inputs.ring_i32(1).reshape(1, -1)
+    np.testing.assert_array_equal(oracle.reduce_scatter(x), x)
+    np.testing.assert_array_equal(oracle.all_reduce(x), x)
+
+
+def test_reduce_scatter_rejects_indivisible():
+    with pytest.raises(ValueError):
+        oracle.reduce_scatter(np.zeros((4, 10), dtype=np.float32))
+
+
+def test_fp32_association_order_owner_last():
+    """The owner adds its own contribution last.  With x_owner = 2^24 and
+    every other rank contributing 1, the three 1's are summed first (exactly
+    3) and 2^24 + 3 rounds to 2^24 + 4 (tie to even); adding the owner first
+    would give 2^24 (each +1 ties back to 2^24)."""
+    P, C = 4, 2
+    x = np.ones((P, P * C), dtype=np.float32)
+    for c in range(P):
+        x[c, c * C:(c + 1) * C] = 2.0 ** 24
+    st = oracle.reduce_scatter(x)
+    for r in range(P):
+        assert np.all(st[r, r * C:(r + 1) * C] == np.float32(2.0 ** 24 + 4))
+
+
+def test_fp32_association_order_chain_direction():
+    """Partial sums travel to the right, so chunk c is accumulated starting at
+    rank c+1, then c+2, ...; with x_{c+1} = 2^24 and x_{c+2} = x_{c+3} = 1,
+    x_c = 0 the sum is ((2^24 + 1) + 1) + 0 = 2^24 (two ties to even); the
+    opposite direction would give ((1 + 1) + 2^24) + 0 = 2^24 + 2."""
+    P, C = 4, 2
+    x = np.zeros((P, P * C), dtype=np.float32)
+    for c in range(P):
+        x[(c + 1) % P, c * C:(c + 1) * C] = 2.0 ** 24
+        x[(c + 2) % P, c * C:(c + 1) * C] = 1.0
+        x[(c + 3) % P, c * C:(c + 1) * C] = 1.0
+    st = oracle.reduce_scatter(x)
+    for r in range(P):
+        assert np.all(st[r, r * C:(r + 1) * C] == np.float32(2.0 ** 24))
+
+
+def test_p2_single_round():
+    """P = 2: one round; rank 0 owns chunk 0 = x1 + x0, rank 1 chunk 1."""
+    x = inputs.small_f32(2).reshape(2, -1)
+    st = oracle.reduce_scatter(x)
+    C = x.shape[1] // 2
+    np.testing.assert_array_equal(st[0, :C], x[1, :C] + x[0, :C])
+    np.testing.assert_array_equal(st[1, C:], x[0, C:] + x[1, C:])
+
+
+# ---------------------------------------------------------------- all-reduce
+@pytest.mark.parametrize("P", PS)
+def test_all_reduce_int32_brute_force(P):
+    x = inputs.to_chunk_major(inputs.ring_i32(P), P)
+    out = oracle.all_reduce(x)
+    want = x.astype(np.int64).sum(axis=0)
+    for r in range(P):
+        np.testing.assert_array_equal(out[r].astype(np.int64), want)
+
+
+@pytest.mark.parametrize("P", PS)
+def test_all_reduce_is_rs_then_ag(P):
+    x = inputs.to_chunk_major(inputs.small_f32(P, (8, 128 * P)), P)
+    a = oracle.all_reduce(x)
+    b = oracle.all_gather(oracle.reduce_scatter(x))
+    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    # every rank holds the same bits
+    for r in range(1, P):
+        np.testing.assert_array_equal(a[r].view(np.uint32), a[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("P", [2, 4, 8, 16])
+def test_all_reduce_int_valued_fp32_exact(P):
+    rng = np.random.default_rng(11)
+    x = rng.integers(-1000, 1000, size=(P, 64 * P), endpoint=True).astype(np.float32)
+    out = oracle.all_reduce(x)
+    want = x.astype(np.float64).sum(axis=0)
+    for r in range(P):
+        np.testing.assert_array_equal(out[r].astype(np.float64), want)
+
+
+@pytest.mark.parametrize("P", [2, 4, 8, 16])
+def test_all_reduce_fp32_within_recursive_sum_bound(P):
+    """Recursive summation of P terms: |fl - exact| <= (P-1) u sum|x| (to
+    first order), u = 2^-24; the componentwise bound of Higham, Accuracy and
+    Stability of Numerical Algorithms, section 4.2."""
+    x = inputs.normal_f32(P, 4096 * P, seed=5)
+    out = oracle.all_reduce(x)
+    ref, mag = oracle.rank_sum_f64(x)
+    bound = (P - 1) * 2.0 ** -24 * (1 + 1e-6)
+    err = np.abs(out[0].astype(np.float64) - ref) / np.maximum(mag, 1e-300)
+    assert err.max() <= bound
+    assert err.max() <= 1e-6 * P
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8])
+def test_rank_sum_f64_matches_numpy(P):
+    x = inputs.normal_f32(P, 1000, seed=6)
+    s, m = oracle.rank_sum_f64(x)
+    np.testing.assert_allclose(s, x.astype(np.float64).sum(axis=0), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m, np.abs(x.astype(np.float64)).sum(axis=0), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- bf16
+def _f32_from_bits(u):
+    return np.array([u], dtype=np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("bits,want", [
+    (0x3F800000, 0x3F80),   # 1.0
+    (0x3F808000, 0x3F80),   # 1 + 2^-8: tie, kept bit 0 -> down
+    (0x3F818000, 0x3F82),   # 1 + 3*2^-8: tie, kept bit 1 -> up (1 + 2^-6)
+    (0x3F808001, 0x3F81),   # just above the tie -> up
+    (0x3F807FFF, 0x3F80),   # just below the tie -> down
+    (0x00000000, 0x0000),   # +0
+    (0x80000000, 0x8000),   # -0
+    (0x7F800000, 0x7F80),   # +inf
+    (0xFF800000, 0xFF80),   # -inf
+    (0x7F7FFFFF, 0x7F80),   # max finite fp32 rounds to +inf in bf16
+    (0x00000001, 0x0000),   # smallest subnormal rounds to 0
+    (0x00008000, 0x0000),   # subnormal tie -> even (0)
+    (0x00018000, 0x0002),   # subnormal tie -> even (up)
+])
+def test_bf16_rne_hand_cases(bits, want):
+    assert int(oracle.bf16_from_f32(_f32_from_bits(bits))[0]) == want
+
+
+def test_bf16_rne_nan_stays_nan():
+    h = int(oracle.bf16_from_f32(_f32_from_bits(0x7F800001))[0])
+    assert (h & 0x7F80) == 0x7F80 and (h & 0x7F) != 0
+
+
+def test_bf16_rne_matches_torch():
+    import torch
+    rng = np.random.default_rng(7)
+    u = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    f = u.view(np.float32)
+    f = f[~np.isnan(f)]
+    ours = oracle.bf16_from_f32(f)
+    theirs = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, theirs)
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 16])
+def test_bf16_all_reduce_int_valued_exact(P):
+    rng = np.random.default_rng(8)
+    x = inputs.small_int_bf16(rng, (P, 32 * P), -8, 8)
+    out = oracle.all_reduce_bf16(x)
+    want = oracle.bf16_to_f32(x).astype(np.float64).sum(axis=0)
+    for r in range(P):
+        np.testing.assert_array_equal(oracle.bf16_to_f32(out[r]).astype(np.float64), want)
+
+
+@pytest.mark.parametrize("P", [2, 4, 16])
+def test_bf16_all_reduce_one_rounding_bound(P):
+    """fp32 carry then one rounding to bf16 (8 significant bits, unit
+    roundoff 2^-8): error <= 2^-8 |sum| + (P-1) 2^-24 sum|x| (first order)."""
+    x = inputs.normal_bf16(P, 2048 * P, seed=9)
+    out = oracle.all_reduce_bf16(x)
+    ref, mag = oracle.rank_sum_f64(x, bf16=True)
+    got = oracle.bf16_to_f32(out[0]).astype(np.float64)
+    err = np.abs(got - ref) / np.maximum(mag, 1e-300)
+    assert err.max() <= 2.0 ** -8 + (P - 1) * 2.0 ** -24 + 1e-9
+    assert err.max() <= 1e-2
+    # every rank ends with the same bits
+    for r in range(1, P):
+        np.testing.assert_array_equal(out[r], out[0])
+
+
+def test_bf16_carry_is_fp32_until_owner():
+    """Before the last round nothing is rounded: the carry equals the fp32
+    reduce-scatter of the widened inputs, bit for bit."""
+    P = 4
+    x = inputs.normal_bf16(P, 64 * P, seed=10)
+    _, carry = oracle.reduce_scatter_bf16(x)
+    st = oracle.reduce_scatter(oracle.bf16_to_f32(x).copy())
+    np.testing.assert_array_equal(carry.view(np.uint32), st.view(np.uint32))
+
+
+# ---------------------------------------------------------------- GEMM + RS
+def test_gemm_rs_integer_valued_exact():
+    """Integer-valued bf16 inputs in [-4, 4]: every product and sum is an
+    integer below 2^24, so any order is exact; compare with int64."""
+    rng = np.random.default_rng(12)
+    P, M, N, K = 4, 64, 48, 32
+    A = inputs.small_int_bf16(rng, (P, M, K))
+    B = inputs.small_int_bf16(rng, (P, K, N))
+    out = oracle.gemm_reduce_scatter(A, B)
+    Ai = oracle.bf16_to_f32(A).astype(np.int64)
+    Bi = oracle.bf16_to_f32(B).astype(np.int64)
+    total = sum(Ai[q] @ Bi[q] for q in range(P))
+    rows = M // P
+    for r in range(P):
+        np.testing.assert_array_equal(out[r].astype(np.int64), total[r * rows:(r + 1) * rows])
+
+
+def test_gemm_rs_identity_a_gives_sum_of_b():
+    rng = np.random.default_rng(13)
+    P, M = 4, 32
+    eye = inputs.bf16_bits(np.eye(M, dtype=np.float32))
+    A = np.stack([eye] * P)
+    B = inputs.small_int_bf16(rng, (P, M, 40))
+    out = oracle.gemm_reduce_scatter(A, B)
+    total = oracle.bf16_to_f32(B).astype(np.float64).sum(axis=0)
+    rows = M // P
+    for r in range(P):
+        np.testing.assert_array_equal(out[r].astype(np.float64), total[r * rows:(r + 1) * rows])
+
+
+def test_gemm_rs_sampled_rows_reference():
+    rng = np.random.default_rng(14)
+    P, M, N, K = 4, 64, 32, 48
+    A = inputs.bf16_bits(rng.standard_normal((P, M, K)).astype(np.float32) / 8)
+    B = inputs.bf16_bits(rng.standard_normal((P, K, N)).astype(np.float32) / 8)
+    out = oracle.gemm_reduce_scatter(A, B)
+    for r in range(P):
+        rows = np.arange(M // P)
+        s, m = oracle.gemm_reduce_scatter_rows_f64(A, B, r, rows)
+        err = np.abs(out[r].astype(np.float64) - s) / m
+        # one fp32 rounding per product matrix + P-1 fp32 ring additions
+        assert err.max() <= (P + 1) * 2.0 ** -24
+
+
+# ---------------------------------------------------------------- generators
+def test_chunked_draw_equals_single_draw():
+    P, n = 3, 1000
+    a = inputs.normal_f32(P, n, seed=2)
+    b = np.random.default_rng(2).standard_normal((P, n), dtype=np.float32)
+    np.testing.assert_array_equal(a, b)
+    h = inputs.normal_bf16(P, n, seed=3, slab=256)
+    f = np.random.default_rng(3).standard_normal((P, n), dtype=np.float32) * np.float32(1e-2)
+    np.testing.assert_array_equal(h, inputs.bf16_bits(f))
+
+
+def test_chunk_major_roundtrip():
+    x = inputs.ring_i32(4)
+    flat = inputs.to_chunk_major(x, 4)
+    np.testing.assert_array_equal(inputs.from_chunk_major(flat, 4, 8), x)
+    # chunk c is column block c
+    np.testing.assert_array_equal(flat[2, 128 * 8:2 * 128 * 8].reshape(8, 128), x[2, :, 128:256])
