@@ -1,0 +1,235 @@
+"""Benchmark of the ring collectives on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one ring all-reduce (the reduce-scatter rounds and the all-gather
+rounds, 2(P-1) rounds in one launch) over P virtual ranks whose buffers all
+sit in this GPU's HBM; inputs are resident before the timed region starts.
+Prints one JSON line.
+
+Default workload (the headline): P = 8 ranks, 64 Mi fp32 per rank (256 MiB
+per rank, 2 GiB in all), normal(0, 1), seed 2, out of place.
+
+`value` is algorithmic GB/s: bytes the ring must move (reduce-scatter round:
+2 reads + 1 write of a chunk; all-gather round: 1 read + 1 write; at the
+widths actually used) divided by the measured time per step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+
+WORKLOADS = {
+    "ar_f32_p8_64Mi": dict(op="all_reduce", P=8, n=64 << 20, kind="f32", seed=2, std=1.0),
+    "ar_bf16_p16_128Mi": dict(op="all_reduce", P=16, n=128 << 20, kind="bf16", seed=3, std=1e-2),
+    "ar_f32_p4_small": dict(op="all_reduce", P=4, n=4096, kind="f32", seed=0, std=None),
+}
+DEFAULT = "ar_f32_p8_64Mi"
+
+
+def moved_bytes(op: str, P: int, n: int, kind: str) -> int:
+    """Algorithmic bytes of one call (reads + writes the ring must make)."""
+    C = n // P
+    if P == 1:
+        return 0
+    if kind == "bf16":
+        # carry in fp32: round 0 reads two bf16 and writes fp32; middle rounds
+        # read bf16 + fp32 and write fp32; the owner's last round writes bf16.
+        rs = 0
+        for s in range(P - 1):
+            rd = 2 + (2 if s == 0 else 4)
+            wr = 2 if s == P - 2 else 4
+            rs += rd + wr
+        rs *= C * P
+        ag = (P - 1) * 4 * C * P
+    else:
+        rs = (P - 1) * 12 * C * P
+        ag = (P - 1) * 8 * C * P
+    if op == "reduce_scatter":
+        return rs
+    if op == "all_gather":
+        return ag
+    return rs + ag
+
+
+def _sha_kernels() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "ring_collectives_amd", "csrc", "ring_kernels.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def _traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "ring_step_kernel_%s_counters.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != _sha_kernels():
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def _make_inputs(w):
+    import numpy as np
+    from ring_collectives_amd import inputs
+    if w["kind"] == "f32" and w["std"] is None:
+        return inputs.to_chunk_major(inputs.small_f32(w["P"], (8, 512)), w["P"])
+    if w["kind"] == "f32":
+        return inputs.normal_f32(w["P"], w["n"], seed=w["seed"], std=w["std"])
+    if w["kind"] == "bf16":
+        return inputs.normal_bf16(w["P"], w["n"], seed=w["seed"], std=w["std"])
+    raise ValueError(w)
+
+
+def _to_dev(x, kind):
+    import numpy as np
+    import torch
+    out = []
+    for r in range(x.shape[0]):
+        row = x[r]
+        if kind == "bf16":
+            out.append(torch.from_numpy(row.view(np.int16)).cuda().view(torch.bfloat16))
+        else:
+            out.append(torch.from_numpy(row).cuda())
+    return out
+
+
+def _cpu_baseline(w, x):
+    """The oracle as it stands, single-threaded, on the same inputs."""
+    import oracle
+    P, n = x.shape
+    t0 = time.perf_counter()
+    if w["kind"] == "bf16":
+        want = oracle.all_reduce_bf16(x)
+    else:
+        want = oracle.all_reduce(x)
+    dt = time.perf_counter() - t0
+    gbs = moved_bytes(w["op"], P, n, w["kind"]) / dt / 1e9
+    return want, {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                  "seconds": round(dt, 3),
+                  "sample": "the whole workload (%d ranks x %d elements), one thread" % (P, n)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs P virtual ranks on ONE GPU; --gpus %d is not "
+              "supported (the multi-GPU ring is a design note only)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from ring_collectives_amd import _native as N
+    from ring_collectives_amd import collectives as rc
+
+    w = WORKLOADS[args.workload]
+    P, n, kind = w["P"], w["n"], w["kind"]
+    print("[bench] workload %s: generating inputs" % args.workload, file=sys.stderr, flush=True)
+    x = _make_inputs(w)
+    torch.cuda.set_device(0)
+    src = _to_dev(x, kind)
+    dst = [torch.empty_like(t) for t in src]
+    ws = rc.workspace(N.OP_ALL_REDUCE, P, n, src[0].dtype)
+    stream = torch.cuda.current_stream()
+
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        rc.all_reduce(src, dst, ws=ws)
+    torch.cuda.synchronize()
+    code, info = rc.last_error(ws)
+    if code != 0:
+        raise SystemExit("ring_all_reduce reported %s (info %#x)" % (N.strerror(code), info))
+
+    # timed region: K steps, one launch each; events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        rc.all_reduce(src, dst, ws=ws)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    code, info = rc.last_error(ws)
+    if code != 0:
+        raise SystemExit("ring_all_reduce reported %s (info %#x)" % (N.strerror(code), info))
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    avg_kern_ms = sum(kern_ms) / len(kern_ms)
+    mb = moved_bytes(w["op"], P, n, kind)
+    value = mb / (ms_step * 1e-3) / 1e9
+    achieved = mb / (avg_kern_ms * 1e-3) / 1e9
+    print("[bench] %d steps: %.4f ms/step (wall), kernel avg %.4f ms min %.4f max %.4f"
+          % (args.steps, ms_step, avg_kern_ms, min(kern_ms), max(kern_ms)),
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        print("[bench] cpu_baseline: oracle on the same inputs", file=sys.stderr, flush=True)
+        want, cpu = _cpu_baseline(w, x)
+        if kind == "bf16":
+            got = np.stack([t.view(torch.int16).cpu().numpy().view(np.uint16) for t in dst])
+        else:
+            got = np.stack([t.cpu().numpy() for t in dst]).view(np.uint32)
+            want = want.view(np.uint32)
+        parity = bool(np.array_equal(got, want))
+        print("[bench] GPU output bit-exact vs oracle: %s" % parity, file=sys.stderr, flush=True)
+
+    traffic = _traffic(args.workload)
+    line = {
+        "metric": "ring all-reduce HBM GB/s & % of peak, P=%d virtual ranks, %d MiB %s/rank"
+                  % (P, n * (2 if kind == "bf16" else 4) >> 20, "fp32" if kind == "f32" else kind),
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16 (f32 accumulate)", "i32": "int32"}[kind],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "P": P, "elems_per_rank": n,
+                   "bytes_per_rank": n * (2 if kind == "bf16" else 4),
+                   "moved_bytes_per_step": mb, "parallelism": "P virtual ranks on 1 GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "ring_step_kernel",
+                     "kernel_ms_avg": round(avg_kern_ms, 5)},
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+/*
+ * ring_collectives.h -- C ABI of libring_collectives.so: ring collectives over
+ * P virtual ranks whose buffers all live in the HBM of one MI355X (gfx950).
+ *
+ * Virtual rank r's buffer is bufs[r]; a kernel working for rank r touches
+ * only its own buffers and those of its left neighbour (r - 1 + P) mod P, and
+ * it synchronises with that neighbour through per-tile flags in device memory
+ * (no barrier across ranks).  This is the symmetric-buffer picture of the
+ * "Triton-distributed 语义" page ("对称内存模型": the same buffer exists on
+ * every rank and a rank may address a peer's copy), with "the peer's copy"
+ * being another slice of the same HBM.
+ *
+ * Conventions shared by every entry point
+ *   - P        number of ranks, 1 <= P <= RING_MAX_RANKS.
+ *   - n        elements per rank.  The ring splits a rank buffer into P equal
+ *              chunks of C = n / P elements, so P must divide n ("全归约 3：
+ *              Ring——每步大小恒定", section "Run it").  Chunk c is the flat,
+ *              contiguous run [c*C, (c+1)*C).  n == 0 is a no-op.
+ *   - src/dst  host arrays of P device pointers (read during the call only).
+ *              Device pointers must be 4-byte aligned (2 for bf16); 16-byte
+ *              alignment of every chunk start enables the 128-bit path.
+ *   - dtype    RING_F32, RING_BF16 or RING_I32.  fp32 additions are IEEE
+ *              round-to-nearest-even in the ring's fixed order; int32 adds
+ *              wrap modulo 2^32; bf16 is added in fp32 (see below).
+ *   - ws       device workspace of at least ring_workspace_bytes(...) bytes,
+ *              owned by the caller.  It must be zero-filled once before its
+ *              first use (ring_workspace_init, or any zero fill); every call
+ *              that completes normally leaves its flag table zero again, so
+ *              back-to-back calls on one stream need no re-initialisation.
+ *              Calls that share a workspace must be ordered (same stream).
+ *   - stream   a hipStream_t passed as void* (NULL = the default stream).
+ *              Every call is asynchronous on that stream; nothing is
+ *              allocated, printed or thrown by the library.
+ *
+ * Errors: argument errors are returned synchronously (RING_EINVAL,
+ * RING_EUNSUPPORTED, RING_EWORKSPACE); a failed HIP launch returns RING_EHIP.
+ * A rank that waits for its neighbour longer than the watchdog limit
+ * (default 5 s) stops, records RING_ETIMEOUT in the workspace and makes the
+ * other ranks stop too; ring_last_error() reports it.  After a timeout the
+ * output is undefined and the workspace must be re-initialised.
+ */
+#ifndef RING_COLLECTIVES_H
+#define RING_COLLECTIVES_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RING_MAX_RANKS 64
+
+typedef enum { RING_F32 = 0, RING_BF16 = 1, RING_I32 = 2 } ring_dtype_t;
+
+typedef enum {
+    RING_OP_PPERMUTE = 0,
+    RING_OP_REDUCE_SCATTER = 1,
+    RING_OP_ALL_GATHER = 2,
+    RING_OP_ALL_REDUCE = 3,
+    RING_OP_GEMM_REDUCE_SCATTER = 4
+} ring_op_t;
+
+enum {
+    RING_OK = 0,
+    RING_EINVAL = -1,       /* bad rank count, size, pointer or alignment   */
+    RING_EUNSUPPORTED = -2, /* bad dtype or a shape this version rejects    */
+    RING_EWORKSPACE = -3,   /* workspace missing or too small               */
+    RING_EHIP = -4,         /* a HIP runtime call failed                    */
+    RING_ETIMEOUT = -5      /* a rank waited past the watchdog limit        */
+};
+
+/*
+ * Bytes of workspace a call needs.  op is a ring_op_t.  For
+ * RING_OP_GEMM_REDUCE_SCATTER pass n = M * N (elements of one rank's product)
+ * and dtype RING_F32.  Returns 0 for invalid arguments (and for ppermute,
+ * which needs none).
+ */
+size_t ring_workspace_bytes(int op, int P, size_t n, int dtype);
+
+/* Zero-fill a workspace on `stream` (a fill kernel, usable under graph
+ * capture).  Returns RING_OK or RING_EINVAL / RING_EHIP. */
+int ring_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * ppermute (right shift): every rank sends its whole buffer to its right
+ * neighbour, so on return dst[r] holds what src[(r - 1 + P) mod P] held.
+ * "Pallas TPU Distributed Collectives 复习文档", section 1 (right-shift
+ * example, checked against lax.ppermute with perm (i, i+1 mod P)).
+ * n elements per rank of `dtype` (a bit copy; dtype only sets the element
+ * size).  dst and src buffers must not overlap.  No workspace.
+ */
+int ring_ppermute(const void *const *src, void *const *dst, int P, size_t n,
+                  int dtype, void *stream);
+
+/*
+ * Ring reduce-scatter, P-1 rounds ("全归约 3：Ring——每步大小恒定",
+ * Walkthrough, first loop; the same schedule as the reduce-scatter kernel of
+ * "TPU 与分布式通信原语").  In round s = 0..P-2 rank r takes chunk
+ * c = (r - s - 2) mod P from its left neighbour -- the neighbour's input at
+ * s = 0, otherwise the partial sum the neighbour stored in round s-1 -- adds
+ * its own input chunk c and stores the result as its chunk c.
+ *
+ * On return chunk r of dst[r] holds the sum over all ranks of chunk r
+ * (psum_scatter's result: "Pallas TPU Distributed Collectives 复习文档",
+ * section 4.4).  The other chunks of dst[r] hold partial sums (unspecified).
+ * fp32 order: chunk c is ((x_{c+1} + x_{c+2}) + ...) + x_c, indices mod P.
+ * bf16: partial sums travel in fp32 through the workspace; the owner rounds
+ * its final fp32 sum once to bf16 (nearest, ties to even).
+ * In place (dst[r] == src[r] for every r) is allowed; otherwise src and dst
+ * must not overlap.
+ */
+int ring_reduce_scatter(const void *const *src, void *const *dst, int P, size_t n,
+                        int dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Ring all-gather, P-1 rounds ("全归约 3", Walkthrough, second phase; the
+ * slot rule of "Pallas TPU Distributed Collectives 复习文档", section 2).
+ * In round t = 0..P-2 rank r copies chunk (r - t - 1) mod P of its left
+ * neighbour into the same chunk of its own buffer.
+ *
+ * If src_or_null is NULL, chunk r of dst[r] must already hold rank r's piece
+ * (the in-place form that follows a reduce-scatter).  Otherwise src_or_null[r]
+ * points at rank r's compact piece of C = n / P elements, which is placed at
+ * chunk r of dst[r] (the pieces must not overlap dst).  On return every
+ * dst[r] is the concatenation of the P pieces in rank order.
+ */
+int ring_all_gather(const void *const *src_or_null, void *const *dst, int P, size_t n,
+                    int dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Ring all-reduce = reduce-scatter then all-gather, 2(P-1) rounds in one
+ * launch ("全归约 3", The idea and Walkthrough: one signal row per round,
+ * rows 0..P-2 for the first phase and P-1..2P-3 for the second).  On return
+ * every dst[r] holds the sum over ranks of src[q] (every rank the same bits).
+ * In place allowed as for ring_reduce_scatter.
+ */
+int ring_all_reduce(const void *const *src, void *const *dst, int P, size_t n,
+                    int dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * GEMM + reduce-scatter with tile-level overlap ("Triton-distributed 语义",
+ * "GEMM + ReduceScatter 重叠": the GEMM produces output tiles and signals each
+ * one; the reduce-scatter consumes tiles as their signals arrive; and
+ * "TPU 与分布式通信原语", collective matmul, for the unfused meaning).
+ *
+ * A[r]: bf16 M x K row-major, B[r]: bf16 K x N row-major, for every rank r.
+ * out[r]: fp32 (M / P) x N row-major = rows [r M/P, (r+1) M/P) of
+ * sum_q A[q] B[q].  The per-rank products are accumulated in fp32 on the
+ * matrix cores; the sum over ranks follows the fp32 ring reduce-scatter over
+ * row-block chunks (chunk c = rows [c M/P, (c+1) M/P)).
+ * Shapes this version accepts: M % (256 P) == 0, N % 256 == 0, K % 64 == 0.
+ */
+int gemm_reduce_scatter(const void *const *A, const void *const *B, void *const *out,
+                        int P, int M, int N, int K, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/*
+ * Synchronises `stream` and returns the error word a kernel left in `ws`
+ * (RING_OK if none).  If info is not NULL it receives the stuck rank, round
+ * and tile packed as rank | round << 8 | tile << 16 (tile saturates).
+ */
+int ring_last_error(const void *ws, size_t ws_bytes, void *stream, int *info);
+
+/* Static description of an error code. */
+const char *ring_strerror(int code);
+
+/*
+ * Tuning and debug knobs of the chunk-step kernel, process-wide.  Changing
+ * them while calls are in flight is not supported.  Results never depend on
+ * them (fp32 bits included); only speed does, except for the debug hooks.
+ *   tile_vecs      16-byte vectors per lane per tile: 4, 8 or 16 (a tile is
+ *                  the unit of one flag: 64 lanes x tile_vecs x 16 bytes).
+ *   waves_per_cu   resident wavefronts to aim for per compute unit (>= 4).
+ *   map_mode       wavefront -> (rank, tile) mapping: 0 interleaved ranks,
+ *                  1 rank-contiguous, 2 a tile's whole ring chain on one XCD.
+ *   timeout_s      watchdog for one wait, seconds (> 0).
+ *   stepwise       1: one launch per round, ordered by the stream instead of
+ *                  flags (the "inject a barrier between steps" debugging aid
+ *                  of "Triton-distributed 语义", best practice 8).
+ *   drop_round     test hook: if >= 1, rank 0 never signals round drop_round,
+ *                  so its right neighbour's wait must end in RING_ETIMEOUT.
+ */
+typedef struct {
+    int tile_vecs;
+    int waves_per_cu;
+    int map_mode;
+    double timeout_s;
+    int stepwise;
+    int drop_round;
+} ring_tuning_t;
+
+void ring_get_tuning(ring_tuning_t *t);
+int ring_set_tuning(const ring_tuning_t *t);   /* RING_EINVAL on bad values */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RING_COLLECTIVES_H */

@@ -1,0 +1,152 @@
+"""Python entry points of the ring collectives, one per C-ABI call.
+
+Each takes lists of per-rank torch tensors (device memory supplied by torch),
+turns them into pointer arrays and calls the library on torch's current HIP
+stream.  Nothing here computes: every step runs in the library's kernels.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+import torch
+
+from . import _native as N
+
+_DT = {torch.float32: N.RING_F32, torch.bfloat16: N.RING_BF16, torch.int32: N.RING_I32}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError("ring collectives take float32, bfloat16 or int32, got %s" % t.dtype)
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ranks(ts: Sequence[torch.Tensor], what: str, numel: int | None = None, dtype=None):
+    if len(ts) < 1 or len(ts) > N.MAX_RANKS:
+        raise ValueError("%s: 1..%d rank buffers, got %d" % (what, N.MAX_RANKS, len(ts)))
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("%s: rank buffers must be contiguous device tensors" % what)
+        if numel is not None and t.numel() != numel:
+            raise ValueError("%s: every rank buffer needs %d elements" % (what, numel))
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError("%s: mixed dtypes" % what)
+    return [t.data_ptr() for t in ts]
+
+
+def workspace_bytes(op: int, P: int, n: int, dtype: torch.dtype = torch.float32) -> int:
+    return int(N.lib().ring_workspace_bytes(op, P, n, _DT[dtype]))
+
+
+def workspace(op: int, P: int, n: int, dtype: torch.dtype, device=None) -> torch.Tensor:
+    """A zero-filled workspace of the size the library asks for."""
+    nb = workspace_bytes(op, P, n, dtype)
+    return torch.zeros(max(nb, 256), dtype=torch.uint8,
+                       device=device if device is not None else "cuda")
+
+
+def _ws(ws, op, P, n, dtype, device):
+    if ws is None:
+        ws = workspace(op, P, n, dtype, device)
+    return ws
+
+
+def ppermute(src: Sequence[torch.Tensor], dst: Sequence[torch.Tensor], stream=None) -> None:
+    """dst[r] <- src[(r - 1 + P) mod P] (right shift)."""
+    n = src[0].numel()
+    ps = _ranks(src, "ppermute", n, src[0].dtype)
+    pd = _ranks(dst, "ppermute", n, src[0].dtype)
+    if len(ps) != len(pd):
+        raise ValueError("ppermute: src and dst rank counts differ")
+    a, ka = N.ptr_array(ps)
+    b, kb = N.ptr_array(pd)
+    N.check(N.lib().ring_ppermute(a, b, len(ps), n, _dtype(src[0]), _stream(stream)),
+            "ring_ppermute")
+
+
+def _rs_ar(fn, name, op, src, dst, ws, stream):
+    n = src[0].numel()
+    P = len(src)
+    ps = _ranks(src, name, n, src[0].dtype)
+    pd = _ranks(dst, name, n, src[0].dtype)
+    if len(pd) != P:
+        raise ValueError("%s: src and dst rank counts differ" % name)
+    ws = _ws(ws, op, P, n, src[0].dtype, src[0].device)
+    a, ka = N.ptr_array(ps)
+    b, kb = N.ptr_array(pd)
+    N.check(fn(a, b, P, n, _dtype(src[0]), ws.data_ptr(), ws.numel(), _stream(stream)), name)
+    return ws
+
+
+def reduce_scatter(src, dst, ws=None, stream=None):
+    """Ring reduce-scatter: chunk r of dst[r] <- sum over ranks of chunk r."""
+    return _rs_ar(N.lib().ring_reduce_scatter, "ring_reduce_scatter", N.OP_REDUCE_SCATTER,
+                  src, dst, ws, stream)
+
+
+def all_reduce(src, dst, ws=None, stream=None):
+    """Ring all-reduce: every dst[r] <- sum over ranks of src."""
+    return _rs_ar(N.lib().ring_all_reduce, "ring_all_reduce", N.OP_ALL_REDUCE,
+                  src, dst, ws, stream)
+
+
+def all_gather(dst, src=None, ws=None, stream=None):
+    """Ring all-gather.  src=None: chunk r of dst[r] already holds rank r's
+    piece; otherwise src[r] is rank r's compact piece (numel = n / P)."""
+    n = dst[0].numel()
+    P = len(dst)
+    pd = _ranks(dst, "ring_all_gather", n, dst[0].dtype)
+    keep = []
+    if src is not None:
+        if len(src) != P:
+            raise ValueError("ring_all_gather: src and dst rank counts differ")
+        ps = _ranks(src, "ring_all_gather", n // P if n % P == 0 else -1, dst[0].dtype)
+        a, ka = N.ptr_array(ps)
+        keep.append(ka)
+    else:
+        a = None
+    ws = _ws(ws, N.OP_ALL_GATHER, P, n, dst[0].dtype, dst[0].device)
+    b, kb = N.ptr_array(pd)
+    N.check(N.lib().ring_all_gather(a, b, P, n, _dtype(dst[0]), ws.data_ptr(), ws.numel(),
+                                    _stream(stream)), "ring_all_gather")
+    return ws
+
+
+def gemm_reduce_scatter(A, B, out, ws=None, stream=None):
+    """out[r] <- rows [r M/P, (r+1) M/P) of sum_q A[q] @ B[q] (bf16 in, fp32 out)."""
+    P = len(A)
+    M, K = A[0].shape
+    K2, Nn = B[0].shape
+    if K2 != K or len(B) != P or len(out) != P:
+        raise ValueError("gemm_reduce_scatter: shape mismatch")
+    pa = _ranks(A, "gemm_reduce_scatter", M * K, torch.bfloat16)
+    pb = _ranks(B, "gemm_reduce_scatter", K * Nn, torch.bfloat16)
+    po = _ranks(out, "gemm_reduce_scatter", (M // P) * Nn, torch.float32)
+    if ws is None:
+        nb = int(N.lib().ring_workspace_bytes(N.OP_GEMM_REDUCE_SCATTER, P, M * Nn, N.RING_F32))
+        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=A[0].device)
+    a, ka = N.ptr_array(pa)
+    b, kb = N.ptr_array(pb)
+    o, ko = N.ptr_array(po)
+    N.check(N.lib().gemm_reduce_scatter(a, b, o, P, M, Nn, K, ws.data_ptr(), ws.numel(),
+                                        _stream(stream)), "gemm_reduce_scatter")
+    return ws
+
+
+def last_error(ws: torch.Tensor, stream=None):
+    """(code, info) left in a workspace by the last kernel (synchronises)."""
+    import ctypes
+    info = ctypes.c_int(0)
+    code = N.lib().ring_last_error(ws.data_ptr(), ws.numel(), _stream(stream), ctypes.byref(info))
+    return int(code), int(info.value)
+
+
+def workspace_init(ws: torch.Tensor, stream=None) -> None:
+    N.check(N.lib().ring_workspace_init(ws.data_ptr(), ws.numel(), _stream(stream)),
+            "ring_workspace_init")

@@ -1,0 +1,340 @@
+// ring_api.hip -- the C ABI of libring_collectives.so: argument checking,
+// workspace layout and launch configuration for the ring collectives.  The
+// semantics of every entry point are stated in include/ring_collectives.h.
+#include "ring_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <stdlib.h>
+#include <string.h>
+
+namespace ringc {
+
+int elem_bytes(int dtype) {
+    switch (dtype) {
+        case RING_F32: return 4;
+        case RING_I32: return 4;
+        case RING_BF16: return 2;
+        default: return 0;
+    }
+}
+
+int elems_per_vec(int dtype) { return elem_bytes(dtype) ? 16 / elem_bytes(dtype) : 0; }
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+RingWs ring_ws_layout(int P, size_t n, int dtype) {
+    RingWs w;
+    const size_t C = n / (size_t)P;
+    const size_t tile_min = (size_t)kWave * kMinTileVecs * elems_per_vec(dtype);
+    const size_t T = (C + tile_min - 1) / tile_min;
+    const size_t rows = P > 1 ? 2 * (size_t)(P - 1) : 1;
+    w.flags_off = kStatusBytes;
+    w.flags_bytes = align_up(rows * (size_t)P * (T ? T : 1) * kFlagStride * sizeof(int), 256);
+    w.carry_off = w.flags_off + w.flags_bytes;
+    w.carry_bytes = dtype == RING_BF16 ? align_up((size_t)P * n * sizeof(float), 256) : 0;
+    w.total = w.carry_off + w.carry_bytes;
+    return w;
+}
+
+static int env_int(const char* name, int dflt) {
+    const char* v = getenv(name);
+    return v && *v ? atoi(v) : dflt;
+}
+
+static bool tuning_valid(const ring_tuning_t& x) {
+    return (x.tile_vecs == 4 || x.tile_vecs == 8 || x.tile_vecs == 16) && x.waves_per_cu >= 4 &&
+           x.waves_per_cu <= 64 && x.map_mode >= 0 && x.map_mode <= 2 && x.timeout_s > 0 &&
+           x.timeout_s < 3600 && (x.stepwise == 0 || x.stepwise == 1) && x.drop_round >= 0;
+}
+
+static ring_tuning_t& tuning_ref() {
+    static ring_tuning_t t = [] {
+        ring_tuning_t d;
+        d.tile_vecs = 8;
+        d.waves_per_cu = 8;
+        d.map_mode = 0;
+        d.timeout_s = 5.0;
+        d.stepwise = 0;
+        d.drop_round = 0;
+        ring_tuning_t x = d;
+        x.tile_vecs = env_int("RING_TILE_VECS", d.tile_vecs);
+        x.waves_per_cu = env_int("RING_WAVES_PER_CU", d.waves_per_cu);
+        x.map_mode = env_int("RING_MAP", d.map_mode);
+        const char* to = getenv("RING_TIMEOUT_S");
+        if (to && *to) x.timeout_s = atof(to);
+        x.stepwise = env_int("RING_STEPWISE", 0);
+        return tuning_valid(x) ? x : d;
+    }();
+    return t;
+}
+
+ring_tuning_t tuning() { return tuning_ref(); }
+
+DevInfo dev_info() {
+    static DevInfo cache[64];
+    static int valid[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!valid[dev]) {
+        DevInfo d;
+        int v = 0;
+        d.cus = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0 ? v : 256;
+        v = 0;
+        d.wall_khz = hipDeviceGetAttribute(&v, hipDeviceAttributeWallClockRate, dev) == hipSuccess && v > 0 ? v : 100000;
+        cache[dev] = d;
+        valid[dev] = 1;
+    }
+    return cache[dev];
+}
+
+}  // namespace ringc
+
+using namespace ringc;
+
+// ------------------------------------------------------------------ checks
+static int check_common(const void* const* a, int P, size_t n, int dtype, size_t esz_override) {
+    if (P < 1 || P > RING_MAX_RANKS) return RING_EINVAL;
+    if (!elem_bytes(dtype)) return RING_EUNSUPPORTED;
+    if (n % (size_t)P) return RING_EINVAL;
+    if (!a) return RING_EINVAL;
+    const size_t al = esz_override ? esz_override : (size_t)elem_bytes(dtype);
+    for (int r = 0; r < P; ++r)
+        if (!a[r] || ((uintptr_t)a[r] % al)) return RING_EINVAL;
+    return RING_OK;
+}
+
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// 0: disjoint, 1: exactly in place (dst[r] == src[r] for all r), -1: bad overlap.
+static int overlap_kind(const void* const* src, size_t src_bytes, void* const* dst,
+                        size_t dst_bytes, int P, bool allow_in_place) {
+    if (!src_bytes || !dst_bytes) return 0;
+    bool in_place = allow_in_place;
+    for (int r = 0; r < P && in_place; ++r) in_place = (src[r] == dst[r]);
+    for (int a = 0; a < P; ++a)
+        for (int b = a + 1; b < P; ++b)
+            if (overlap(dst[a], dst_bytes, dst[b], dst_bytes)) return -1;
+    if (in_place) {
+        for (int a = 0; a < P; ++a)
+            for (int b = 0; b < P; ++b)
+                if (a != b && overlap(src[a], src_bytes, dst[b], dst_bytes)) return -1;
+        return 1;
+    }
+    for (int a = 0; a < P; ++a)
+        for (int b = 0; b < P; ++b)
+            if (overlap(src[a], src_bytes, dst[b], dst_bytes)) return -1;
+    return 0;
+}
+
+static hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+// Launch the chunk-step kernel over global rounds [k_begin, k_end).
+static int run_ring(const void* const* src, void* const* dst, int P, size_t n, int dtype,
+                    void* ws, size_t ws_bytes, void* stream, int k_begin, int k_end,
+                    int compact_src) {
+    const RingWs lay = ring_ws_layout(P, n, dtype);
+    const bool need_carry = dtype == RING_BF16 && k_begin < P - 1;   // reduce-scatter rounds
+    if (!ws || ((uintptr_t)ws & 255)) return RING_EWORKSPACE;
+    if (ws_bytes < (need_carry ? lay.total : lay.total - lay.carry_bytes)) return RING_EWORKSPACE;
+    const ring_tuning_t tu = tuning();
+    const DevInfo di = dev_info();
+    const int esz = elem_bytes(dtype);
+    const long long C = (long long)(n / (size_t)P);
+    const int tile = kWave * tu.tile_vecs * elems_per_vec(dtype);
+    const int T = (int)((C + tile - 1) / tile);
+
+    RingParams prm;
+    memset(&prm, 0, sizeof prm);
+    int vec_ok = ((C * esz) % 16) == 0;
+    for (int r = 0; r < P; ++r) {
+        prm.src[r] = src ? src[r] : nullptr;
+        prm.dst[r] = dst[r];
+        if ((uintptr_t)dst[r] & 15) vec_ok = 0;
+        if (src && ((uintptr_t)src[r] & 15)) vec_ok = 0;
+    }
+    prm.carry = need_carry ? (float*)((char*)ws + lay.carry_off) : nullptr;
+    prm.flags = (int*)((char*)ws + lay.flags_off);
+    prm.status = (Status*)ws;
+    prm.n = (long long)n;
+    prm.C = C;
+    prm.spin_limit = (long long)(tu.timeout_s * (double)di.wall_khz * 1000.0);
+    prm.P = P;
+    prm.T = T;
+    prm.tile = tile;
+    prm.k_begin = k_begin;
+    prm.k_end = k_end;
+    prm.vec_ok = vec_ok;
+    prm.compact_src = compact_src;
+
+    // Grid: every wave must be resident at once (waves wait on each other).
+    int occ = ring_blocks_per_cu(dtype, tu.tile_vecs);
+    if (occ < 1) return RING_EHIP;
+    int bpc = (tu.waves_per_cu + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (bpc > occ) bpc = occ;
+    const long long max_blocks = (long long)di.cus * bpc;
+    const long long max_waves = max_blocks * kWavesPerBlock;
+    int map_mode = tu.map_mode;
+    long long blocks = 0;
+    int W = 0;
+    if (map_mode == 2) {
+        long long m = ((long long)T + 7) / 8;
+        const long long cap = max_waves / (8LL * P);
+        if (m > cap) m = cap;
+        while (m >= 1 && 8 * (((long long)P * m + kWavesPerBlock - 1) / kWavesPerBlock) > max_blocks) --m;
+        if (m >= 1) {
+            W = (int)(8 * m);
+            blocks = 8 * (((long long)P * m + kWavesPerBlock - 1) / kWavesPerBlock);
+        } else {
+            map_mode = 0;
+        }
+    }
+    if (map_mode != 2) {
+        long long w = max_waves / P;
+        if (w > T) w = T;
+        if (w < 1) return RING_EUNSUPPORTED;   // more ranks than resident waves
+        W = (int)w;
+        blocks = ((long long)P * W + kWavesPerBlock - 1) / kWavesPerBlock;
+    }
+    prm.waves_per_rank = W;
+    prm.map_mode = map_mode;
+    prm.drop_round = tu.drop_round;
+    if (tu.stepwise) {
+        // One launch per round: stream order replaces the flags (no waits,
+        // no signals inside a launch of a single round).
+        for (int k = k_begin; k < k_end; ++k) {
+            prm.k_begin = k;
+            prm.k_end = k + 1;
+            if (launch_ring(prm, dtype, tu.tile_vecs, (int)blocks, as_stream(stream)) != hipSuccess)
+                return RING_EHIP;
+        }
+        return RING_OK;
+    }
+    if (launch_ring(prm, dtype, tu.tile_vecs, (int)blocks, as_stream(stream)) != hipSuccess)
+        return RING_EHIP;
+    return RING_OK;
+}
+
+// ------------------------------------------------------------------ C ABI
+extern "C" {
+
+size_t ring_workspace_bytes(int op, int P, size_t n, int dtype) {
+    if (P < 1 || P > RING_MAX_RANKS) return 0;
+    switch (op) {
+        case RING_OP_PPERMUTE: return 0;
+        case RING_OP_REDUCE_SCATTER:
+        case RING_OP_ALL_REDUCE:
+            if (!elem_bytes(dtype) || n % (size_t)P) return 0;
+            return ring_ws_layout(P, n, dtype).total;
+        case RING_OP_ALL_GATHER: {
+            if (!elem_bytes(dtype) || n % (size_t)P) return 0;
+            RingWs w = ring_ws_layout(P, n, dtype);
+            return w.total - w.carry_bytes;   // a copy needs no carry
+        }
+        case RING_OP_GEMM_REDUCE_SCATTER:
+            return gemm_rs_workspace_bytes(P, n);
+        default: return 0;
+    }
+}
+
+int ring_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws) return RING_EINVAL;
+    if (!ws_bytes) return RING_OK;
+    return launch_fill_zero(ws, ws_bytes, as_stream(stream)) == hipSuccess ? RING_OK : RING_EHIP;
+}
+
+int ring_ppermute(const void* const* src, void* const* dst, int P, size_t n, int dtype,
+                  void* stream) {
+    int rc = check_common(src, P, n, dtype, 0);
+    if (rc) return rc;
+    if ((rc = check_common(dst, P, n, dtype, 0))) return rc;
+    const size_t bytes = n * (size_t)elem_bytes(dtype);
+    if (overlap_kind(src, bytes, dst, bytes, P, false) != 0) return RING_EINVAL;
+    if (n == 0) return RING_OK;
+    return launch_copy(src, dst, P, bytes, 1, as_stream(stream)) == hipSuccess ? RING_OK : RING_EHIP;
+}
+
+static int rs_or_ar(const void* const* src, void* const* dst, int P, size_t n, int dtype,
+                    void* ws, size_t ws_bytes, void* stream, bool all_reduce) {
+    int rc = check_common(src, P, n, dtype, 0);
+    if (rc) return rc;
+    if ((rc = check_common(dst, P, n, dtype, 0))) return rc;
+    const size_t bytes = n * (size_t)elem_bytes(dtype);
+    const int ov = overlap_kind(src, bytes, dst, bytes, P, true);
+    if (ov < 0) return RING_EINVAL;
+    if (n == 0) return RING_OK;
+    if (P == 1) {   // no rounds: the sum over one rank is its input
+        if (ov == 1) return RING_OK;
+        return launch_copy(src, dst, 1, bytes, 0, as_stream(stream)) == hipSuccess ? RING_OK : RING_EHIP;
+    }
+    return run_ring(src, dst, P, n, dtype, ws, ws_bytes, stream, 0,
+                    all_reduce ? 2 * (P - 1) : P - 1, 0);
+}
+
+int ring_reduce_scatter(const void* const* src, void* const* dst, int P, size_t n, int dtype,
+                        void* ws, size_t ws_bytes, void* stream) {
+    return rs_or_ar(src, dst, P, n, dtype, ws, ws_bytes, stream, false);
+}
+
+int ring_all_reduce(const void* const* src, void* const* dst, int P, size_t n, int dtype,
+                    void* ws, size_t ws_bytes, void* stream) {
+    return rs_or_ar(src, dst, P, n, dtype, ws, ws_bytes, stream, true);
+}
+
+int ring_all_gather(const void* const* src_or_null, void* const* dst, int P, size_t n, int dtype,
+                    void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_common(dst, P, n, dtype, 0);
+    if (rc) return rc;
+    const size_t esz = (size_t)elem_bytes(dtype);
+    const size_t bytes = n * esz;
+    if (src_or_null) {
+        if ((rc = check_common(src_or_null, P, n, dtype, 0))) return rc;
+        if (overlap_kind(src_or_null, (n / (size_t)P) * esz, dst, bytes, P, false) != 0)
+            return RING_EINVAL;
+    } else if (overlap_kind(dst, 0, dst, bytes, P, false) < 0) {
+        return RING_EINVAL;
+    }
+    if (n == 0) return RING_OK;
+    if (P == 1) {
+        if (!src_or_null) return RING_OK;
+        return launch_copy(src_or_null, dst, 1, bytes, 0, as_stream(stream)) == hipSuccess ? RING_OK : RING_EHIP;
+    }
+    // the all-gather rounds are global rounds P-1 .. 2P-3 of the all-reduce
+    return run_ring(src_or_null, dst, P, n, dtype, ws, ws_bytes, stream, P - 1, 2 * (P - 1),
+                    src_or_null ? 1 : 0);
+}
+
+int ring_last_error(const void* ws, size_t ws_bytes, void* stream, int* info) {
+    if (!ws || ws_bytes < sizeof(Status)) return RING_EINVAL;
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return RING_EHIP;
+    Status st;
+    if (hipMemcpy(&st, ws, sizeof st, hipMemcpyDeviceToHost) != hipSuccess) return RING_EHIP;
+    if (info) *info = st.info;
+    return st.code;
+}
+
+void ring_get_tuning(ring_tuning_t* t) {
+    if (t) *t = tuning_ref();
+}
+
+int ring_set_tuning(const ring_tuning_t* t) {
+    if (!t || !tuning_valid(*t)) return RING_EINVAL;
+    tuning_ref() = *t;
+    return RING_OK;
+}
+
+const char* ring_strerror(int code) {
+    switch (code) {
+        case RING_OK: return "ok";
+        case RING_EINVAL: return "invalid argument (rank count, size, pointer, alignment or overlap)";
+        case RING_EUNSUPPORTED: return "unsupported dtype or shape";
+        case RING_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case RING_EHIP: return "HIP runtime call failed";
+        case RING_ETIMEOUT: return "a rank waited for its neighbour past the watchdog limit";
+        default: return "unknown error";
+    }
+}
+
+}  // extern "C"

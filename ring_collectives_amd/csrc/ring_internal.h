@@ -1,0 +1,81 @@
+// ring_internal.h -- internal declarations shared by the HIP translation units
+// of libring_collectives.so (kernel parameter blocks, workspace layout,
+// launchers).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ring_collectives.h"
+
+namespace ringc {
+
+constexpr int kWave = 64;            // CDNA wavefront width
+constexpr int kBlock = 256;          // threads per workgroup of the ring kernels
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kFlagStride = 16;      // ints between flags: one flag per 64 bytes
+constexpr size_t kStatusBytes = 256; // error word + info, at offset 0 of a workspace
+constexpr int kMinTileVecs = 4;      // smallest tile: 4 vectors of 16 B per lane
+
+// The error header every workspace starts with.
+struct Status {
+    int code;   // RING_OK or RING_ETIMEOUT
+    int info;   // rank | round << 8 | min(tile, 32767) << 16
+};
+
+// Parameters of one launch of the persistent chunk-step kernel.
+struct RingParams {
+    const void* src[RING_MAX_RANKS];  // per-rank inputs (AG: compact pieces or null)
+    void* dst[RING_MAX_RANKS];        // per-rank outputs
+    float* carry;                     // bf16 only: P * n fp32 partial sums
+    int* flags;                       // [2(P-1)][P][T] flags, kFlagStride apart
+    Status* status;                   // error word
+    long long n;                      // elements per rank
+    long long C;                      // elements per chunk (n / P)
+    long long spin_limit;             // watchdog, in wall-clock ticks
+    int P;                            // ranks
+    int T;                            // tiles per chunk
+    int tile;                         // elements per tile
+    int k_begin, k_end;               // global rounds [k_begin, k_end)
+    int waves_per_rank;               // waves working for one rank
+    int vec_ok;                       // 1: every chunk/tile start is 16-byte aligned
+    int compact_src;                  // all-gather from compact pieces
+    int map_mode;                     // wave -> (rank, lane) mapping
+    int drop_round;                   // test hook: rank 0 skips this signal (0 = off)
+};
+
+// Workspace layout of the ring collectives for (P, n, dtype).
+struct RingWs {
+    size_t flags_off, flags_bytes;
+    size_t carry_off, carry_bytes;
+    size_t total;
+};
+
+int elem_bytes(int dtype);
+int elems_per_vec(int dtype);
+RingWs ring_ws_layout(int P, size_t n, int dtype);
+
+// Tuning knobs: defaults, overridable by RING_* environment variables at
+// first use and by ring_set_tuning().
+ring_tuning_t tuning();
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_copy(const void* const* src, void* const* dst, int P, size_t bytes,
+                       int shift, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_ring(RingParams& prm, int dtype, int tile_vecs, int grid_blocks,
+                       hipStream_t s);
+int ring_blocks_per_cu(int dtype, int tile_vecs);   // occupancy of the ring kernel
+
+// GEMM + reduce-scatter workspace size (n = M * N per rank).
+size_t gemm_rs_workspace_bytes(int P, size_t n);
+
+// Device properties cached per device.
+struct DevInfo {
+    int cus;
+    long long wall_khz;
+};
+DevInfo dev_info();
+
+}  // namespace ringc

@@ -1,10 +1,13 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the bench.
 
 This module only draws random numbers and lays them out; it holds none of the
-collectives' arithmetic.  Everything is NumPy ``default_rng(seed)`` (PCG64),
-drawn in rank order as if one array of shape ``(P, ...)`` were drawn at once.
-Large draws are made rank by rank from the same generator, which yields the
-same stream as one draw (NumPy fills arrays sequentially).
+collectives' arithmetic.  Everything is NumPy PCG64:
+  * small workloads: ``default_rng(seed)``, one draw of shape (P, ...) in rank
+    order;
+  * large workloads (fp32/bf16 normal rank buffers, GEMM operands): rank r
+    draws from its own child stream ``default_rng(SeedSequence(seed).spawn(P)[r])``
+    so the ranks can be drawn in parallel threads; bf16 data is drawn in
+    slabs, which continue the same per-rank stream.
 
 bf16 values are the round-to-nearest-even images of fp32 draws, produced with
 torch's fp32 -> bf16 conversion and handled here as uint16 bit patterns.
@@ -20,7 +23,7 @@ here, so only shape, type and distribution follow them):
   * bf16 gradient-bucket workload: P = 16, 128 Mi bf16 per rank,
     normal(0, 0.01), seed 3;
   * GEMM + reduce-scatter: P = 4, A_q and B_q bf16 4096 x 4096,
-    normal(0, 1/64), seed 4 (all A's first, then all B's).
+    normal(0, 1/64), seed 4.
 
 Two-dimensional per-rank arrays of shape (R, w * P) are stored chunk-major:
 chunk c (a flat, contiguous run of R * w elements) is column block c of the
@@ -28,6 +31,9 @@ logical array, as in the chunk-major layout helpers of "TPU ä¸Žåˆ†å¸ƒå¼é€šä¿¡åŽ
 (collective matmul section).
 """
 from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -75,48 +81,70 @@ def ring_i32(P: int, rows: int = 8, width_per_rank: int = 128) -> np.ndarray:
                         endpoint=True, dtype=np.int32)
 
 
-def normal_f32(P: int, n: int, seed: int = SEED_F32_BW, std: float = 1.0,
-               out: np.ndarray | None = None) -> np.ndarray:
-    """(P, n) fp32 normal(0, std) drawn rank by rank from one generator."""
-    rng = np.random.default_rng(seed)
-    if out is None:
-        out = np.empty((P, n), dtype=np.float32)
-    for r in range(P):
-        rng.standard_normal(n, dtype=np.float32, out=out[r])
+def rank_streams(seed: int, P: int):
+    """One independent PCG64 generator per rank, spawned from `seed`."""
+    return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(P)]
+
+
+def _threads(P: int) -> int:
+    try:
+        cpus = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cpus = os.cpu_count() or 1
+    return max(1, min(P, cpus, 16))
+
+
+def normal_f32(P: int, n: int, seed: int = SEED_F32_BW, std: float = 1.0) -> np.ndarray:
+    """(P, n) fp32 normal(0, std); rank r from its own child stream."""
+    out = np.empty((P, n), dtype=np.float32)
+    gens = rank_streams(seed, P)
+
+    def draw(r):
+        gens[r].standard_normal(n, dtype=np.float32, out=out[r])
         if std != 1.0:
             out[r] *= np.float32(std)
+
+    with ThreadPoolExecutor(_threads(P)) as ex:
+        list(ex.map(draw, range(P)))
     return out
 
 
 def normal_bf16(P: int, n: int, seed: int = SEED_BF16, std: float = 1e-2,
                 slab: int = 1 << 24) -> np.ndarray:
-    """(P, n) bf16 bit patterns: RNE of fp32 normal(0, std) draws, made in
-    slabs from one generator (same stream as one (P, n) draw)."""
-    rng = np.random.default_rng(seed)
+    """(P, n) bf16 bit patterns: RNE of fp32 normal(0, std) draws; rank r
+    from its own child stream, drawn in slabs of `slab` values."""
     out = np.empty((P, n), dtype=np.uint16)
-    buf = np.empty(min(slab, max(n, 1)), dtype=np.float32)
-    for r in range(P):
+    gens = rank_streams(seed, P)
+
+    def draw(r):
+        buf = np.empty(min(slab, max(n, 1)), dtype=np.float32)
         for lo in range(0, n, slab):
             m = min(slab, n - lo)
-            rng.standard_normal(m, dtype=np.float32, out=buf[:m])
+            gens[r].standard_normal(m, dtype=np.float32, out=buf[:m])
             buf[:m] *= np.float32(std)
             out[r, lo:lo + m] = bf16_bits(buf[:m])
+
+    with ThreadPoolExecutor(_threads(P)) as ex:
+        list(ex.map(draw, range(P)))
     return out
 
 
 def gemm_operands(P: int = 4, M: int = 4096, N: int = 4096, K: int = 4096,
                   std: float = 1.0 / 64, seed: int = SEED_GEMM):
-    """(A, B) as bf16 bit patterns: A (P, M, K), B (P, K, N), normal(0, std);
-    all A's are drawn first, then all B's."""
-    rng = np.random.default_rng(seed)
+    """(A, B) as bf16 bit patterns: A (P, M, K), B (P, K, N), normal(0, std).
+    Rank q draws A_q and then B_q from its own child stream."""
     A = np.empty((P, M, K), dtype=np.uint16)
     B = np.empty((P, K, N), dtype=np.uint16)
-    for q in range(P):
-        a = rng.standard_normal((M, K), dtype=np.float32) * np.float32(std)
+    gens = rank_streams(seed, P)
+
+    def draw(q):
+        a = gens[q].standard_normal((M, K), dtype=np.float32) * np.float32(std)
         A[q] = bf16_bits(a)
-    for q in range(P):
-        b = rng.standard_normal((K, N), dtype=np.float32) * np.float32(std)
+        b = gens[q].standard_normal((K, N), dtype=np.float32) * np.float32(std)
         B[q] = bf16_bits(b)
+
+    with ThreadPoolExecutor(_threads(P)) as ex:
+        list(ex.map(draw, range(P)))
     return A, B
 
 

@@ -1,0 +1,166 @@
+"""Host-side checks of libring_collectives.so that need no GPU: the library
+loads, exports every function include/ring_collectives.h declares, sizes
+workspaces, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from ring_collectives_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(HEADER_DIR):
+        if not fn.endswith(".h"):
+            continue
+        src = open(os.path.join(HEADER_DIR, fn)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        src = re.sub(r"#[^\n]*", " ", src)
+        for m in re.finditer(r"\b([A-Za-z_]\w*)\s*\(([^;{}]*)\)\s*;", src):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_loads():
+    assert N.lib() is not None
+
+
+def test_every_declared_symbol_is_exported():
+    decl = _declared_functions()
+    assert {"ring_ppermute", "ring_reduce_scatter", "ring_all_gather", "ring_all_reduce",
+            "gemm_reduce_scatter"} <= decl
+    out = subprocess.check_output(["nm", "-D", "--defined-only", N.LIB_PATH], text=True)
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = sorted(decl - exported)
+    assert not missing, missing
+    for name in decl:
+        assert hasattr(N.lib(), name)
+
+
+def test_binding_covers_the_header():
+    assert _declared_functions() <= set(N.SIGNATURES)
+
+
+def test_strerror():
+    for code in (N.RING_OK, N.RING_EINVAL, N.RING_EUNSUPPORTED, N.RING_EWORKSPACE,
+                 N.RING_EHIP, N.RING_ETIMEOUT):
+        assert N.strerror(code)
+    assert N.strerror(12345) == "unknown error"
+
+
+def test_workspace_bytes():
+    L = N.lib()
+    assert L.ring_workspace_bytes(N.OP_PPERMUTE, 4, 4096, N.RING_F32) == 0
+    assert L.ring_workspace_bytes(N.OP_ALL_REDUCE, 0, 4096, N.RING_F32) == 0
+    assert L.ring_workspace_bytes(N.OP_ALL_REDUCE, 4, 4097, N.RING_F32) == 0
+    assert L.ring_workspace_bytes(N.OP_ALL_REDUCE, 4, 4096, 9) == 0
+    f = L.ring_workspace_bytes(N.OP_ALL_REDUCE, 8, 64 << 20, N.RING_F32)
+    assert f > 0 and f % 256 == 0
+    # bf16 needs an fp32 carry of P * n floats for the reduce-scatter rounds
+    b = L.ring_workspace_bytes(N.OP_ALL_REDUCE, 16, 128 << 20, N.RING_BF16)
+    assert b >= 16 * (128 << 20) * 4
+    ag = L.ring_workspace_bytes(N.OP_ALL_GATHER, 16, 128 << 20, N.RING_BF16)
+    assert ag < 16 * (128 << 20) * 4
+    # P = 1: a status header and a minimal flag table
+    assert L.ring_workspace_bytes(N.OP_ALL_REDUCE, 1, 100, N.RING_I32) >= 256
+
+
+def _fake(ptrs):
+    return N.ptr_array(ptrs)
+
+
+def _call_rs(P, n, dtype=N.RING_F32, src=None, dst=None, ws=0x100000, ws_bytes=1 << 40):
+    src = src if src is not None else [0x10000000 + r * 0x1000000 for r in range(P)]
+    dst = dst if dst is not None else [0x80000000 + r * 0x1000000 for r in range(P)]
+    a, ka = _fake(src)
+    b, kb = _fake(dst)
+    return N.lib().ring_reduce_scatter(a, b, P, n, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("P", [0, -1, 65])
+def test_bad_rank_count(P):
+    a, ka = _fake([0x1000] * 70)
+    assert N.lib().ring_reduce_scatter(a, a, P, 64, N.RING_F32, 0x100000, 1 << 30, None) == N.RING_EINVAL
+
+
+def test_indivisible_size():
+    assert _call_rs(4, 4097) == N.RING_EINVAL
+
+
+def test_bad_dtype():
+    assert _call_rs(4, 4096, dtype=7) == N.RING_EUNSUPPORTED
+
+
+def test_null_pointers():
+    assert N.lib().ring_reduce_scatter(None, None, 4, 4096, N.RING_F32, 0x100000, 1 << 30, None) == N.RING_EINVAL
+    src = [0x10000000, 0, 0x30000000, 0x40000000]
+    assert _call_rs(4, 4096, src=src) == N.RING_EINVAL
+
+
+def test_misaligned_pointer():
+    src = [0x10000000, 0x20000002, 0x30000000, 0x40000000]
+    assert _call_rs(4, 4096, src=src) == N.RING_EINVAL
+    # 2-byte alignment is enough for bf16
+    assert _call_rs(4, 0, dtype=N.RING_BF16, src=src) == N.RING_OK
+
+
+def test_overlap_rejected():
+    src = [0x10000000 + r * 0x100000 for r in range(4)]
+    dst = [0x10000000 + 0x100000 * (r + 1) for r in range(4)]   # dst[r] == src[r+1]
+    assert _call_rs(4, 4096, src=src, dst=dst) == N.RING_EINVAL
+    dst = [0x90000000 + r * 0x100 for r in range(4)]            # dst buffers overlap each other
+    assert _call_rs(4, 4096, src=src, dst=dst) == N.RING_EINVAL
+
+
+def test_workspace_checks():
+    L = N.lib()
+    need = L.ring_workspace_bytes(N.OP_REDUCE_SCATTER, 4, 4096, N.RING_F32)
+    assert _call_rs(4, 4096, ws_bytes=need - 1) == N.RING_EWORKSPACE
+    assert _call_rs(4, 4096, ws=0) == N.RING_EWORKSPACE
+    assert _call_rs(4, 4096, ws=0x100010) == N.RING_EWORKSPACE      # not 256-byte aligned
+
+
+def test_zero_size_is_noop():
+    assert _call_rs(8, 0) == N.RING_OK
+    a, ka = _fake([0x10000000 + r * 0x1000000 for r in range(4)])
+    b, kb = _fake([0x80000000 + r * 0x1000000 for r in range(4)])
+    L = N.lib()
+    assert L.ring_ppermute(a, b, 4, 0, N.RING_F32, None) == N.RING_OK
+    assert L.ring_all_gather(a, b, 4, 0, N.RING_I32, 0x100000, 1 << 30, None) == N.RING_OK
+    assert L.ring_all_gather(None, b, 4, 0, N.RING_I32, 0x100000, 1 << 30, None) == N.RING_OK
+    assert L.ring_all_reduce(a, b, 4, 0, N.RING_BF16, 0x100000, 1 << 30, None) == N.RING_OK
+
+
+def test_ppermute_rejects_in_place():
+    a, ka = _fake([0x10000000 + r * 0x1000000 for r in range(4)])
+    assert N.lib().ring_ppermute(a, a, 4, 64, N.RING_F32, None) == N.RING_EINVAL
+
+
+def test_all_gather_piece_overlap():
+    dst = [0x80000000 + r * 0x1000000 for r in range(4)]
+    pieces = [d + 16 for d in dst]
+    a, ka = _fake(pieces)
+    b, kb = _fake(dst)
+    assert N.lib().ring_all_gather(a, b, 4, 4096, N.RING_F32, 0x100000, 1 << 30, None) == N.RING_EINVAL
+
+
+def test_tuning_roundtrip_and_validation():
+    old = N.get_tuning()
+    try:
+        prev = N.set_tuning(tile_vecs=16, map_mode=2)
+        assert prev == old
+        assert N.get_tuning()["tile_vecs"] == 16
+        for bad in ({"tile_vecs": 5}, {"waves_per_cu": 1}, {"map_mode": 7},
+                    {"timeout_s": 0.0}, {"stepwise": 2}, {"drop_round": -1}):
+            with pytest.raises(N.RingError):
+                N.set_tuning(**bad)
+    finally:
+        t = N.Tuning(**old)
+        assert N.lib().ring_set_tuning(ctypes.byref(t)) == N.RING_OK

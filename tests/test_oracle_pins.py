@@ -379,14 +379,18 @@ def test_gemm_rs_sampled_rows_reference():
 
 
 # ---------------------------------------------------------------- generators
-def test_chunked_draw_equals_single_draw():
+def test_rank_streams_are_reproducible():
+    """Rank r's data is its own child stream drawn in one go, whatever the
+    slab size or thread count."""
     P, n = 3, 1000
     a = inputs.normal_f32(P, n, seed=2)
-    b = np.random.default_rng(2).standard_normal((P, n), dtype=np.float32)
-    np.testing.assert_array_equal(a, b)
+    for r, g in enumerate(inputs.rank_streams(2, P)):
+        np.testing.assert_array_equal(a[r], g.standard_normal(n, dtype=np.float32))
     h = inputs.normal_bf16(P, n, seed=3, slab=256)
-    f = np.random.default_rng(3).standard_normal((P, n), dtype=np.float32) * np.float32(1e-2)
-    np.testing.assert_array_equal(h, inputs.bf16_bits(f))
+    for r, g in enumerate(inputs.rank_streams(3, P)):
+        f = g.standard_normal(n, dtype=np.float32) * np.float32(1e-2)
+        np.testing.assert_array_equal(h[r], inputs.bf16_bits(f))
+    np.testing.assert_array_equal(inputs.normal_f32(P, n, seed=2), a)
 
 
 def test_chunk_major_roundtrip():
