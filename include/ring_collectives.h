@@ -87,7 +87,8 @@ int ring_workspace_init(void *ws, size_t ws_bytes, void *stream);
  * "Pallas TPU Distributed Collectives 复习文档", section 1 (right-shift
  * example, checked against lax.ppermute with perm (i, i+1 mod P)).
  * n elements per rank of `dtype` (a bit copy; dtype only sets the element
- * size).  dst and src buffers must not overlap.  No workspace.
+ * size); P need not divide n here.  dst and src buffers must not overlap.
+ * No workspace.
  */
 int ring_ppermute(const void *const *src, void *const *dst, int P, size_t n,
                   int dtype, void *stream);

@@ -92,12 +92,12 @@ DevInfo dev_info() {
 using namespace ringc;
 
 // ------------------------------------------------------------------ checks
-static int check_common(const void* const* a, int P, size_t n, int dtype, size_t esz_override) {
+static int check_common(const void* const* a, int P, size_t n, int dtype, bool chunked) {
     if (P < 1 || P > RING_MAX_RANKS) return RING_EINVAL;
     if (!elem_bytes(dtype)) return RING_EUNSUPPORTED;
-    if (n % (size_t)P) return RING_EINVAL;
+    if (chunked && n % (size_t)P) return RING_EINVAL;
     if (!a) return RING_EINVAL;
-    const size_t al = esz_override ? esz_override : (size_t)elem_bytes(dtype);
+    const size_t al = (size_t)elem_bytes(dtype);
     for (int r = 0; r < P; ++r)
         if (!a[r] || ((uintptr_t)a[r] % al)) return RING_EINVAL;
     return RING_OK;
@@ -247,9 +247,10 @@ int ring_workspace_init(void* ws, size_t ws_bytes, void* stream) {
 
 int ring_ppermute(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                   void* stream) {
-    int rc = check_common(src, P, n, dtype, 0);
+    // a whole-buffer shift: no chunking, so P need not divide n
+    int rc = check_common(src, P, n, dtype, false);
     if (rc) return rc;
-    if ((rc = check_common(dst, P, n, dtype, 0))) return rc;
+    if ((rc = check_common(dst, P, n, dtype, false))) return rc;
     const size_t bytes = n * (size_t)elem_bytes(dtype);
     if (overlap_kind(src, bytes, dst, bytes, P, false) != 0) return RING_EINVAL;
     if (n == 0) return RING_OK;
@@ -258,9 +259,9 @@ int ring_ppermute(const void* const* src, void* const* dst, int P, size_t n, int
 
 static int rs_or_ar(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream, bool all_reduce) {
-    int rc = check_common(src, P, n, dtype, 0);
+    int rc = check_common(src, P, n, dtype, true);
     if (rc) return rc;
-    if ((rc = check_common(dst, P, n, dtype, 0))) return rc;
+    if ((rc = check_common(dst, P, n, dtype, true))) return rc;
     const size_t bytes = n * (size_t)elem_bytes(dtype);
     const int ov = overlap_kind(src, bytes, dst, bytes, P, true);
     if (ov < 0) return RING_EINVAL;
@@ -285,12 +286,12 @@ int ring_all_reduce(const void* const* src, void* const* dst, int P, size_t n, i
 
 int ring_all_gather(const void* const* src_or_null, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream) {
-    int rc = check_common(dst, P, n, dtype, 0);
+    int rc = check_common(dst, P, n, dtype, true);
     if (rc) return rc;
     const size_t esz = (size_t)elem_bytes(dtype);
     const size_t bytes = n * esz;
     if (src_or_null) {
-        if ((rc = check_common(src_or_null, P, n, dtype, 0))) return rc;
+        if ((rc = check_common(src_or_null, P, n, dtype, true))) return rc;
         if (overlap_kind(src_or_null, (n / (size_t)P) * esz, dst, bytes, P, false) != 0)
             return RING_EINVAL;
     } else if (overlap_kind(dst, 0, dst, bytes, P, false) < 0) {
