@@ -205,7 +205,7 @@ def main():
 
     traffic = _traffic(args.workload)
     line = {
-        "metric": "ring all-reduce HBM GB/s & % of peak, P=%d virtual ranks, %d MiB %s/rank"
+        "metric": "ring all-reduce HBM GB/s & %% of peak, P=%d virtual ranks, %d MiB %s/rank"
                   % (P, n * (2 if kind == "bf16" else 4) >> 20, "fp32" if kind == "f32" else kind),
         "value": round(value, 2),
         "unit": "GB/s",

@@ -171,9 +171,11 @@ const char *ring_strerror(int code);
  * them (fp32 bits included); only speed does, except for the debug hooks.
  *   tile_vecs      16-byte vectors per lane per tile: 4, 8 or 16 (a tile is
  *                  the unit of one flag: 64 lanes x tile_vecs x 16 bytes).
- *   waves_per_cu   resident wavefronts to aim for per compute unit (>= 4).
- *   map_mode       wavefront -> (rank, tile) mapping: 0 interleaved ranks,
- *                  1 rank-contiguous, 2 a tile's whole ring chain on one XCD.
+ *   waves_per_cu   resident wavefronts to aim for per compute unit (4..16;
+ *                  never more than half the occupancy limit is used).
+ *   map_mode       wavefront -> (rank, tile) mapping: 0 the P ranks of a tile
+ *                  position in consecutive wavefronts, 2 a tile position's
+ *                  whole ring on one XCD.
  *   timeout_s      watchdog for one wait, seconds (> 0).
  *   stepwise       1: one launch per round, ordered by the stream instead of
  *                  flags (the "inject a barrier between steps" debugging aid

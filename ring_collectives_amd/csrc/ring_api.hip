@@ -43,7 +43,7 @@ static int env_int(const char* name, int dflt) {
 
 static bool tuning_valid(const ring_tuning_t& x) {
     return (x.tile_vecs == 4 || x.tile_vecs == 8 || x.tile_vecs == 16) && x.waves_per_cu >= 4 &&
-           x.waves_per_cu <= 64 && x.map_mode >= 0 && x.map_mode <= 2 && x.timeout_s > 0 &&
+           x.waves_per_cu <= 16 && (x.map_mode == 0 || x.map_mode == 2) && x.timeout_s > 0 &&
            x.timeout_s < 3600 && (x.stepwise == 0 || x.stepwise == 1) && x.drop_round >= 0;
 }
 
@@ -170,10 +170,11 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
     prm.compact_src = compact_src;
 
     // Grid: every wave must be resident at once (waves wait on each other).
+    // Stay within half the occupancy limit: margin for anything else resident.
     int occ = ring_blocks_per_cu(dtype, tu.tile_vecs);
     if (occ < 1) return RING_EHIP;
     int bpc = (tu.waves_per_cu + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (bpc > occ) bpc = occ;
+    if (bpc > occ / 2) bpc = occ / 2 > 0 ? occ / 2 : 1;
     const long long max_blocks = (long long)di.cus * bpc;
     const long long max_waves = max_blocks * kWavesPerBlock;
     int map_mode = tu.map_mode;

@@ -21,21 +21,27 @@
 // consume_token sections: store, then signal; wait, then load).  The unit of
 // work is a tile: `tile` consecutive elements of one chunk, handled by one
 // wavefront.  Flag (k, r, j) in HBM says "rank r has finished tile j of its
-// round k-1".  The producer wave makes its stores visible at agent scope
-// (release fence: L2 write-back so other XCDs see them) and adds 1 to the flag;
-// the consumer wave polls the flag until it is >= 1, then takes an
-// agent-scope acquire fence (L2/L1 invalidate) before it loads its
-// neighbour's data.  Each flag is set by one wave and read by one wave per
-// launch, so the reader clears it after use and a finished launch leaves the
-// table zeroed for the next one.
+// round k-1".  Ranks on different XCDs do not share an L2, so every access
+// that crosses ranks carries device scope on the instruction itself: the
+// producer's stores are written through to the device coherence point and
+// the consumer's loads of its neighbour's data bypass stale L1/L2 copies.
+// The producer waits for all its memory operations to complete, then adds 1
+// to the flag; the consumer polls the flag until it is >= 1 and only then
+// issues the loads of its neighbour's data.  This is the ordering an
+// agent-scope release/acquire pair gives, without the whole-L2 write-back and
+// invalidate those fences cost per tile.  Each flag is set by one wave and
+// read by one wave per launch, so the reader clears it after use and a
+// finished launch leaves the table zeroed for the next one.
 //
 // Work assignment.  Each rank gets `waves_per_rank` waves; wave w of rank r
 // takes tile positions j = w, w + W, w + 2W, ... and for each position runs
 // every round k in order.  A wave only ever waits for (k-1, left, j), which
 // belongs to the left rank's wave with the same w and an earlier place in
-// that wave's own order (same j, smaller k), so as long as all waves are
-// resident at once the dependencies always drain: the host sizes the grid
-// from the occupancy query so that they are.  A watchdog bounds every wait.
+// that wave's own order (same j, smaller k).  The P waves sharing a w form a
+// closed ring and are placed in consecutive workgroups (or on one XCD), so
+// the rings that are resident can always finish and free room for the rest;
+// the host also keeps the grid within half the occupancy limit, so normally
+// every wave is resident from the start.  A watchdog bounds every wait.
 #include "ring_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -81,11 +87,59 @@ __device__ void report_timeout(const RingParams& p, int r, int k, int j) {
     }
 }
 
-// Wait until flag (k, left, j) is set, then acquire.  Returns false if the
-// launch is being abandoned (this wave timed out, or another one did).
-__device__ bool wait_flag(const RingParams& p, int k, int left, int r, int j, int lane) {
+// ---------------------------------------------------------------- memory access
+// Every access goes through a buffer descriptor over exactly one tile, so the
+// hardware drops any store and zeroes any load that falls outside it (the
+// ragged last tile of a chunk needs no separate path).
+//
+// Cache policy (CDNA3/4 scope bits on the instruction itself):
+//   DEV  (sc1) device scope: a store is written through to the device's
+//        coherence point and a load does not return a stale copy from this
+//        CU's L1 or this XCD's L2.  Used for every access that crosses ranks
+//        (what a rank stores for its neighbour, what it loads from it).
+//   PLAIN      default caching: a rank's own input, and the final all-gather
+//        round whose result no other wave reads before the launch ends.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw (unformatted) 32-bit buffer
+enum { POL_PLAIN = 0, POL_NT = 2, POL_DEV = 16 };
+
+__device__ __forceinline__ rsrc_t tile_view(const void* base, long long bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+template <int POL> __device__ __forceinline__ u32x4 ld16(rsrc_t v, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(v, off, 0, POL);
+}
+template <int POL> __device__ __forceinline__ void st16(u32x4 x, rsrc_t v, unsigned off) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, v, off, 0, POL);
+}
+template <int POL> __device__ __forceinline__ unsigned ld4(rsrc_t v, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(v, off, 0, POL);
+}
+template <int POL> __device__ __forceinline__ void st4(unsigned x, rsrc_t v, unsigned off) {
+    __builtin_amdgcn_raw_buffer_store_b32(x, v, off, 0, POL);
+}
+template <int POL> __device__ __forceinline__ unsigned short ld2(rsrc_t v, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(v, off, 0, POL);
+}
+template <int POL> __device__ __forceinline__ void st2(unsigned short x, rsrc_t v, unsigned off) {
+    __builtin_amdgcn_raw_buffer_store_b16(x, v, off, 0, POL);
+}
+// ---------------------------------------------------------------- flags
+// First look at flag (k, left, j); the caller issues its independent loads
+// before it spins on the result.
+__device__ __forceinline__ int peek_flag(const RingParams& p, int k, int left, int j) {
+    return __hip_atomic_load(flag_at(p, k, left, j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin until flag (k, left, j) is set (unless `seen` already is), then clear
+// it.  Returns false if the launch is being abandoned (this wave timed out,
+// or another one did).  The loads of the neighbour's data that follow are
+// device-scope and are issued only after the flag was seen (control
+// dependency; the empty asm keeps the compiler from hoisting them).
+__device__ bool wait_flag(const RingParams& p, int k, int left, int r, int j, int lane, int seen) {
     int* f = flag_at(p, k, left, j);
-    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < 1) {
+    if (seen < 1) {
         const long long t0 = wall_clock64();
         unsigned spins = 0;
         while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < 1) {
@@ -100,109 +154,120 @@ __device__ bool wait_flag(const RingParams& p, int k, int left, int r, int j, in
             }
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    asm volatile("" ::: "memory");
     // This wave is the flag's only reader in this launch: clear it for the next.
     if (lane == 0) __hip_atomic_store(f, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
 }
 
-// Publish this wave's stores of round k-1 and set flag (k, r, j).
+// Publish this wave's round: wait until all its memory operations are
+// complete (its device-scope stores are at the coherence point, its loads of
+// the neighbour's data have returned), then set flag (k, r, j).
 __device__ __forceinline__ void signal_flag(const RingParams& p, int k, int r, int j, int lane) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (lane == 0)
         __hip_atomic_fetch_add(flag_at(p, k, r, j), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- tile bodies
-// Element types.
 template <int DT> struct Elem;
 template <> struct Elem<DT_F32> { typedef float T; static constexpr int VPE = 4; };
 template <> struct Elem<DT_I32> { typedef int T; static constexpr int VPE = 4; };
 template <> struct Elem<DT_BF16> { typedef unsigned short T; static constexpr int VPE = 8; };
 
-template <int DT> __device__ __forceinline__ u32x4 add_vec(u32x4 a, u32x4 b);
-template <> __device__ __forceinline__ u32x4 add_vec<DT_F32>(u32x4 a, u32x4 b) {
-    f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
-    return __builtin_bit_cast(u32x4, x + y);
+template <int DT> __device__ __forceinline__ unsigned add1(unsigned a, unsigned b);
+template <> __device__ __forceinline__ unsigned add1<DT_F32>(unsigned a, unsigned b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
 }
-template <> __device__ __forceinline__ u32x4 add_vec<DT_I32>(u32x4 a, u32x4 b) {
-    return a + b;  // wraps modulo 2^32
+template <> __device__ __forceinline__ unsigned add1<DT_I32>(unsigned a, unsigned b) {
+    return a + b;   // wraps modulo 2^32
 }
-
-template <int DT> __device__ __forceinline__ void add_scalar(const void* own, const void* rcv,
-                                                              void* out, long long i);
-template <> __device__ __forceinline__ void add_scalar<DT_F32>(const void* own, const void* rcv,
-                                                                void* out, long long i) {
-    ((float*)out)[i] = ((const float*)own)[i] + ((const float*)rcv)[i];
-}
-template <> __device__ __forceinline__ void add_scalar<DT_I32>(const void* own, const void* rcv,
-                                                                void* out, long long i) {
-    ((unsigned*)out)[i] = ((const unsigned*)own)[i] + ((const unsigned*)rcv)[i];
+template <int DT> __device__ __forceinline__ u32x4 add4(u32x4 a, u32x4 b) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = add1<DT>(a[q], b[q]);
+    return o;
 }
 
-// One reduce-scatter round of one tile, fp32 / int32.
+// Where one tile of round k lives.
+struct TilePos {
+    long long e0;    // first element of the tile in a rank buffer
+    long long off;   // first element of the tile within its chunk
+    long long len;   // elements in the tile (the last tile of a chunk may be short)
+};
+__device__ __forceinline__ TilePos tile_pos(const RingParams& p, int c, int j) {
+    TilePos t;
+    t.off = (long long)j * p.tile;
+    t.e0 = (long long)c * p.C + t.off;
+    t.len = (p.C - t.off) < p.tile ? (p.C - t.off) : p.tile;
+    return t;
+}
+
+// One reduce-scatter round of one tile, fp32 / int32:
+//   dst[r][c] = src[r][c] + (s == 0 ? src[left][c] : dst[left][c])
 template <int DT, int U>
 __device__ bool rs_tile(const RingParams& p, int r, int left, int k, int j, int lane, bool wait) {
-    typedef typename Elem<DT>::T T;
     const int s = k;
     const int c = rs_chunk(r, s, p.P);
-    const long long off = (long long)j * p.tile;
-    const long long e0 = (long long)c * p.C + off;
-    const long long len = (p.C - off) < p.tile ? (p.C - off) : p.tile;
-    const T* own = (const T*)p.src[r] + e0;
-    const T* rcv = (s == 0 ? (const T*)p.src[left] : (const T*)p.dst[left]) + e0;
-    T* out = (T*)p.dst[r] + e0;
-    if (p.vec_ok && len == p.tile) {
+    const TilePos t = tile_pos(p, c, j);
+    const long long nb = t.len * 4;
+    const rsrc_t own = tile_view((const char*)p.src[r] + t.e0 * 4, nb);
+    const rsrc_t rcv = tile_view((const char*)(s == 0 ? p.src[left] : p.dst[left]) + t.e0 * 4, nb);
+    const rsrc_t out = tile_view((char*)p.dst[r] + t.e0 * 4, nb);
+    const int seen = wait ? peek_flag(p, k, left, j) : 1;
+    if (p.vec_ok) {
         u32x4 a[U], b[U];
-        const u32x4* ov = (const u32x4*)own;
 #pragma unroll
-        for (int i = 0; i < U; ++i) a[i] = ov[lane + i * kWave];
-        if (wait && !wait_flag(p, k, left, r, j, lane)) return false;
-        const u32x4* rv = (const u32x4*)rcv;
+        for (int i = 0; i < U; ++i) a[i] = ld16<POL_PLAIN>(own, (unsigned)(lane + i * kWave) * 16u);
+        if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
 #pragma unroll
-        for (int i = 0; i < U; ++i) b[i] = rv[lane + i * kWave];
-        u32x4* dv = (u32x4*)out;
+        for (int i = 0; i < U; ++i) b[i] = ld16<POL_DEV>(rcv, (unsigned)(lane + i * kWave) * 16u);
 #pragma unroll
-        for (int i = 0; i < U; ++i) dv[lane + i * kWave] = add_vec<DT>(a[i], b[i]);
+        for (int i = 0; i < U; ++i) st16<POL_DEV>(add4<DT>(a[i], b[i]), out, (unsigned)(lane + i * kWave) * 16u);
     } else {
-        if (wait && !wait_flag(p, k, left, r, j, lane)) return false;
-        for (long long i = lane; i < len; i += kWave) add_scalar<DT>(own, rcv, out, i);
+        if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
+        for (long long i = lane; i < t.len; i += kWave) {
+            const unsigned o = (unsigned)i * 4u;
+            st4<POL_DEV>(add1<DT>(ld4<POL_PLAIN>(own, o), ld4<POL_DEV>(rcv, o)), out, o);
+        }
     }
     return true;
 }
 
-// One reduce-scatter round of one tile, bf16 inputs with the fp32 carry.
+// One reduce-scatter round of one tile, bf16 inputs with the fp32 carry:
+//   round 0      : carry[r][c] = f32(src[r][c]) + f32(src[left][c])
+//   middle rounds: carry[r][c] = f32(src[r][c]) + carry[left][c]
+//   last (owner) : dst[r][r]   = bf16(f32(src[r][r]) + carry[left][r])
 template <int U>
 __device__ bool rs_tile_bf16(const RingParams& p, int r, int left, int k, int j, int lane, bool wait) {
     const int s = k;
     const int c = rs_chunk(r, s, p.P);
     const bool last = (s == p.P - 2);
-    const long long off = (long long)j * p.tile;
-    const long long e0 = (long long)c * p.C + off;
-    const long long len = (p.C - off) < p.tile ? (p.C - off) : p.tile;
-    const unsigned short* own = (const unsigned short*)p.src[r] + e0;
-    const unsigned short* rcv16 = (const unsigned short*)p.src[left] + e0;   // round 0
-    const float* rcv32 = p.carry + (size_t)left * p.n + e0;                  // rounds >= 1
-    float* out32 = p.carry + (size_t)r * p.n + e0;
-    unsigned short* out16 = (unsigned short*)p.dst[r] + e0;
-    if (p.vec_ok && len == p.tile) {
+    const TilePos t = tile_pos(p, c, j);
+    const rsrc_t own = tile_view((const unsigned short*)p.src[r] + t.e0, t.len * 2);
+    const rsrc_t rcv16 = tile_view((const unsigned short*)p.src[left] + t.e0, t.len * 2);
+    const rsrc_t rcv32 = tile_view(p.carry + (size_t)left * p.n + t.e0, t.len * 4);
+    const rsrc_t out32 = tile_view(p.carry + (size_t)r * p.n + t.e0, t.len * 4);
+    const rsrc_t out16 = tile_view((unsigned short*)p.dst[r] + t.e0, t.len * 2);
+    const int seen = wait ? peek_flag(p, k, left, j) : 1;
+    if (p.vec_ok) {
         u32x4 a[U];
 #pragma unroll
-        for (int i = 0; i < U; ++i) a[i] = ((const u32x4*)own)[lane + i * kWave];
-        if (wait && !wait_flag(p, k, left, r, j, lane)) return false;
+        for (int i = 0; i < U; ++i) a[i] = ld16<POL_PLAIN>(own, (unsigned)(lane + i * kWave) * 16u);
+        if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const long long v = lane + i * kWave;   // vector of 8 elements
+            const unsigned v = (unsigned)(lane + i * kWave);   // a vector of 8 elements
             float x[8];
             if (s == 0) {
-                const u32x4 b = ((const u32x4*)rcv16)[v];
+                const u32x4 b = ld16<POL_DEV>(rcv16, v * 16u);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) { x[2 * q] = bf16_lo(b[q]); x[2 * q + 1] = bf16_hi(b[q]); }
             } else {
-                const f32x4 b0 = ((const f32x4*)rcv32)[2 * v];
-                const f32x4 b1 = ((const f32x4*)rcv32)[2 * v + 1];
+                const u32x4 b0 = ld16<POL_DEV>(rcv32, v * 32u);
+                const u32x4 b1 = ld16<POL_DEV>(rcv32, v * 32u + 16u);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) { x[q] = b0[q]; x[4 + q] = b1[q]; }
+                for (int q = 0; q < 4; ++q) { x[q] = __uint_as_float(b0[q]); x[4 + q] = __uint_as_float(b1[q]); }
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -213,69 +278,86 @@ __device__ bool rs_tile_bf16(const RingParams& p, int r, int left, int k, int j,
                 u32x4 o;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) o[q] = pack_bf16(x[2 * q], x[2 * q + 1]);
-                ((u32x4*)out16)[v] = o;
+                st16<POL_DEV>(o, out16, v * 16u);
             } else {
-                ((f32x4*)out32)[2 * v] = f32x4{x[0], x[1], x[2], x[3]};
-                ((f32x4*)out32)[2 * v + 1] = f32x4{x[4], x[5], x[6], x[7]};
+                u32x4 o0, o1;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) { o0[q] = __float_as_uint(x[q]); o1[q] = __float_as_uint(x[4 + q]); }
+                st16<POL_DEV>(o0, out32, v * 32u);
+                st16<POL_DEV>(o1, out32, v * 32u + 16u);
             }
         }
     } else {
-        if (wait && !wait_flag(p, k, left, r, j, lane)) return false;
-        for (long long i = lane; i < len; i += kWave) {
-            const float recv = (s == 0) ? __uint_as_float((unsigned)rcv16[i] << 16) : rcv32[i];
-            const float x = __uint_as_float((unsigned)own[i] << 16) + recv;
-            if (last) out16[i] = (unsigned short)bf16_rne(x);
-            else out32[i] = x;
+        if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
+        for (long long i = lane; i < t.len; i += kWave) {
+            const unsigned o2 = (unsigned)i * 2u, o4 = (unsigned)i * 4u;
+            const float recv = (s == 0) ? __uint_as_float((unsigned)ld2<POL_DEV>(rcv16, o2) << 16)
+                                        : __uint_as_float(ld4<POL_DEV>(rcv32, o4));
+            const float x = __uint_as_float((unsigned)ld2<POL_PLAIN>(own, o2) << 16) + recv;
+            if (last) st2<POL_DEV>((unsigned short)bf16_rne(x), out16, o2);
+            else st4<POL_DEV>(__float_as_uint(x), out32, o4);
         }
     }
     return true;
 }
 
-// Copy `len` elements of `esz` bytes; vector path when aligned and full.
-template <int U>
-__device__ __forceinline__ void copy_elems(void* dst, const void* src, long long len, int esz,
-                                           bool full_vec, int lane) {
-    if (full_vec) {
+// Copy one tile (len elements of ESZ bytes) from `from` to `to`; the store
+// policy STORE_POL is POL_DEV when a neighbour reads the result in this launch.
+template <int U, int ESZ, int LOAD_POL, int STORE_POL>
+__device__ __forceinline__ void copy_tile_p(rsrc_t to, rsrc_t from, long long len, bool vec, int lane) {
+    if (vec) {
         u32x4 a[U];
 #pragma unroll
-        for (int i = 0; i < U; ++i) a[i] = ((const u32x4*)src)[lane + i * kWave];
+        for (int i = 0; i < U; ++i) a[i] = ld16<LOAD_POL>(from, (unsigned)(lane + i * kWave) * 16u);
 #pragma unroll
-        for (int i = 0; i < U; ++i) ((u32x4*)dst)[lane + i * kWave] = a[i];
-    } else if (esz == 4) {
-        for (long long i = lane; i < len; i += kWave) ((unsigned*)dst)[i] = ((const unsigned*)src)[i];
+        for (int i = 0; i < U; ++i) st16<STORE_POL>(a[i], to, (unsigned)(lane + i * kWave) * 16u);
+    } else if (ESZ == 4) {
+        for (long long i = lane; i < len; i += kWave)
+            st4<STORE_POL>(ld4<LOAD_POL>(from, (unsigned)i * 4u), to, (unsigned)i * 4u);
     } else {
         for (long long i = lane; i < len; i += kWave)
-            ((unsigned short*)dst)[i] = ((const unsigned short*)src)[i];
+            st2<STORE_POL>(ld2<LOAD_POL>(from, (unsigned)i * 2u), to, (unsigned)i * 2u);
     }
 }
+template <int U, int ESZ, int LOAD_POL>
+__device__ __forceinline__ void copy_tile(rsrc_t to, rsrc_t from, long long len, bool vec,
+                                          bool pub, int lane) {
+    if (pub) copy_tile_p<U, ESZ, LOAD_POL, POL_DEV>(to, from, len, vec, lane);
+    else copy_tile_p<U, ESZ, LOAD_POL, POL_PLAIN>(to, from, len, vec, lane);
+}
 
-// One all-gather round of one tile (a copy from the left neighbour).
+// One all-gather round of one tile: dst[r][c] = dst[left][c].
 template <int DT, int U>
 __device__ bool ag_tile(const RingParams& p, int r, int left, int k, int j, int lane, bool wait) {
     constexpr int ESZ = sizeof(typename Elem<DT>::T);
     const int t = k - (p.P - 1);
     const int c = ag_chunk(r, t, p.P);
-    const long long off = (long long)j * p.tile;
-    const long long len = (p.C - off) < p.tile ? (p.C - off) : p.tile;
-    const bool full_vec = p.vec_ok && len == p.tile;
-    char* out = (char*)p.dst[r] + ((long long)c * p.C + off) * ESZ;
+    const TilePos q = tile_pos(p, c, j);
+    const long long nb = q.len * ESZ;
+    // the right neighbour reads this round's result in the next round
+    const bool pub = (k + 1 < p.k_end);
+    const rsrc_t out = tile_view((char*)p.dst[r] + q.e0 * ESZ, nb);
     if (p.compact_src && t == 0) {
-        // Place this rank's own piece (input, no wait needed) ...
-        copy_elems<U>((char*)p.dst[r] + ((long long)r * p.C + off) * ESZ,
-                      (const char*)p.src[r] + off * ESZ, len, ESZ, full_vec, lane);
+        // Place this rank's own piece (input, no wait, read by nobody else:
+        // the right neighbour takes it from the input too) ...
+        copy_tile<U, ESZ, POL_PLAIN>(tile_view((char*)p.dst[r] + ((long long)r * p.C + q.off) * ESZ, nb),
+                                     tile_view((const char*)p.src[r] + q.off * ESZ, nb),
+                                     q.len, p.vec_ok, false, lane);
         // ... and take the left neighbour's piece straight from its input.
-        copy_elems<U>(out, (const char*)p.src[left] + off * ESZ, len, ESZ, full_vec, lane);
+        copy_tile<U, ESZ, POL_PLAIN>(out, tile_view((const char*)p.src[left] + q.off * ESZ, nb),
+                                     q.len, p.vec_ok, pub, lane);
         return true;
     }
-    if (wait && !wait_flag(p, k, left, r, j, lane)) return false;
-    copy_elems<U>(out, (const char*)p.dst[left] + ((long long)c * p.C + off) * ESZ, len, ESZ,
-                  full_vec, lane);
+    const int seen = wait ? peek_flag(p, k, left, j) : 1;
+    if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
+    copy_tile<U, ESZ, POL_DEV>(out, tile_view((const char*)p.dst[left] + q.e0 * ESZ, nb), q.len,
+                               p.vec_ok, pub, lane);
     return true;
 }
 
 // ---------------------------------------------------------------- the kernel
 __device__ __forceinline__ bool map_wave(const RingParams& p, int& r, int& w) {
-    const int wid = threadIdx.x / kWave;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int gw = blockIdx.x * kWavesPerBlock + wid;
     const int W = p.waves_per_rank;
     if (p.map_mode == 2) {
@@ -290,9 +372,12 @@ __device__ __forceinline__ bool map_wave(const RingParams& p, int& r, int& w) {
         w = (lw / p.P) * 8 + x;
         return true;
     }
+    // The P waves of one tile position are consecutive, so every prefix of
+    // the dispatch order holds complete rings: progress never depends on a
+    // workgroup that has not been dispatched yet.
     if (gw >= p.P * W) return false;
-    if (p.map_mode == 1) { r = gw / W; w = gw % W; }
-    else { r = gw % p.P; w = gw / p.P; }
+    r = gw % p.P;
+    w = gw / p.P;
     return true;
 }
 

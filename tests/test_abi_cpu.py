@@ -157,7 +157,8 @@ def test_tuning_roundtrip_and_validation():
         prev = N.set_tuning(tile_vecs=16, map_mode=2)
         assert prev == old
         assert N.get_tuning()["tile_vecs"] == 16
-        for bad in ({"tile_vecs": 5}, {"waves_per_cu": 1}, {"map_mode": 7},
+        for bad in ({"tile_vecs": 5}, {"waves_per_cu": 1}, {"waves_per_cu": 32}, {"map_mode": 1},
+                    {"map_mode": 7},
                     {"timeout_s": 0.0}, {"stepwise": 2}, {"drop_round": -1}):
             with pytest.raises(N.RingError):
                 N.set_tuning(**bad)

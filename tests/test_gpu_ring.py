@@ -192,7 +192,7 @@ def test_repeated_calls_reuse_workspace():
 
 
 @pytest.mark.parametrize("tile_vecs", [4, 8, 16])
-@pytest.mark.parametrize("map_mode", [0, 1, 2])
+@pytest.mark.parametrize("map_mode", [0, 2])
 def test_tuning_does_not_change_bits(tile_vecs, map_mode):
     P = 8
     x = inputs.normal_f32(P, P * (64 * 16 * 4 * 9 + 44), seed=60)
