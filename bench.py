@@ -33,6 +33,8 @@ WORKLOADS = {
     "ar_f32_p8_64Mi": dict(op="all_reduce", P=8, n=64 << 20, kind="f32", seed=2, std=1.0),
     "ar_bf16_p16_128Mi": dict(op="all_reduce", P=16, n=128 << 20, kind="bf16", seed=3, std=1e-2),
     "ar_f32_p4_small": dict(op="all_reduce", P=4, n=4096, kind="f32", seed=0, std=None),
+    # a plain copy of known size (2 x 256 MiB read + written): counter calibration
+    "ppermute_f32_p2_64Mi": dict(op="ppermute", P=2, n=64 << 20, kind="f32", seed=2, std=1.0),
 }
 DEFAULT = "ar_f32_p8_64Mi"
 
@@ -40,6 +42,8 @@ DEFAULT = "ar_f32_p8_64Mi"
 def moved_bytes(op: str, P: int, n: int, kind: str) -> int:
     """Algorithmic bytes of one call (reads + writes the ring must make)."""
     C = n // P
+    if op == "ppermute":
+        return 2 * P * n * (2 if kind == "bf16" else 4)
     if P == 1:
         return 0
     if kind == "bf16":
@@ -121,6 +125,8 @@ def _cpu_baseline(w, x):
     t0 = time.perf_counter()
     if w["kind"] == "bf16":
         want = oracle.all_reduce_bf16(x)
+    elif w["op"] == "ppermute":
+        want = oracle.ppermute(x)
     else:
         want = oracle.all_reduce(x)
     dt = time.perf_counter() - t0
@@ -157,10 +163,18 @@ def main():
     dst = [torch.empty_like(t) for t in src]
     ws = rc.workspace(N.OP_ALL_REDUCE, P, n, src[0].dtype)
     stream = torch.cuda.current_stream()
+    if w["op"] == "ppermute":
+        def step():
+            rc.ppermute(src, dst)
+        kernel = "copy_kernel_tab"
+    else:
+        def step():
+            rc.all_reduce(src, dst, ws=ws)
+        kernel = "ring_step_kernel"
 
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        rc.all_reduce(src, dst, ws=ws)
+        step()
     torch.cuda.synchronize()
     code, info = rc.last_error(ws)
     if code != 0:
@@ -173,7 +187,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        rc.all_reduce(src, dst, ws=ws)
+        step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -205,8 +219,9 @@ def main():
 
     traffic = _traffic(args.workload)
     line = {
-        "metric": "ring all-reduce HBM GB/s & %% of peak, P=%d virtual ranks, %d MiB %s/rank"
-                  % (P, n * (2 if kind == "bf16" else 4) >> 20, "fp32" if kind == "f32" else kind),
+        "metric": "ring %s HBM GB/s & %% of peak, P=%d virtual ranks, %d MiB %s/rank"
+                  % (w["op"].replace("_", "-"), P, n * (2 if kind == "bf16" else 4) >> 20,
+                     "fp32" if kind == "f32" else kind),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -223,7 +238,7 @@ def main():
                    "moved_bytes_per_step": mb, "parallelism": "P virtual ranks on 1 GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "ring_step_kernel",
+                     "traffic": traffic, "kernel": kernel,
                      "kernel_ms_avg": round(avg_kern_ms, 5)},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
