@@ -1,14 +1,319 @@
-// gemm_rs.hip -- GEMM + reduce-scatter (placeholder until the MFMA path lands).
-#include "ring_internal.h"
+// gemm_rs.hip -- GEMM + ring reduce-scatter with tile-level overlap.
+//
+// Every virtual rank q computes C_q = A_q B_q (bf16 in, fp32 out) and the
+// ranks reduce-scatter the products over row-block chunks: chunk c is rows
+// [c M/P, (c+1) M/P) and rank q keeps chunk q of sum_q C_q.  The unfused
+// meaning is the collective-matmul section of "TPU 与分布式通信原语" (a full
+// local matmul, then the ring reduce-scatter of its row blocks); the overlap
+// is the "GEMM + ReduceScatter 重叠" pattern of "Triton-distributed 语义": the
+// GEMM produces output tiles, signals each one, and the reduce-scatter
+// consumes each tile as soon as its signal arrives.
+//
+// Schedule.  Rank q walks its chunks in the order the ring needs them
+// ("全归约 3：Ring——每步大小恒定", Walkthrough: in round s rank q adds its own
+// chunk (q - s - 2) mod P to what its left neighbour sends):
+//   phase 0      : chunk (q - 1) mod P, the one its right neighbour needs
+//                  first; the raw fp32 tile goes to the workspace + flag;
+//   phase 1 + s  : chunk (q - s - 2) mod P; the tile is added to the left
+//                  neighbour's tile of the previous phase (its raw tile at
+//                  s = 0, its partial sum after) and stored + flagged, except
+//   phase P - 1  : chunk q itself, whose sum is final and goes to out[q].
+// So every rank starts on the tile its neighbour waits for and finishes on
+// its own chunk (the threadblock-swizzle idea of "Triton-distributed 语义",
+// "线程块交织", turned to the direction of this ring).  The fp32 additions
+// are exactly the ring reduce-scatter's: ((C_{c+1} + C_{c+2}) + ...) + C_c.
+//
+// Tiles.  One 256-thread workgroup computes one 256 x 256 fp32 output tile
+// with v_mfma_f32_32x32x16_bf16: wave w owns the 128 x 128 quarter (w / 2,
+// w % 2) as 4 x 4 MFMA blocks of 32 x 32.  K advances 64 at a time through a
+// double-buffered LDS stage (A as 256 rows x 64 k, B transposed in registers
+// to 256 columns x 64 k so both MFMA operands read 16 contiguous bytes).
+// Partial tiles travel through the workspace in MFMA fragment order (each
+// lane's 16 accumulators contiguous), and a flag guards each wave's quarter,
+// so producer wave w and consumer wave w of the next rank pair up directly.
+//
+// Work assignment: workgroup g serves rank g % P and tile positions
+// g / P, g / P + G / P, ... of every chunk, phase by phase.  A tile of phase
+// f waits only for the left rank's tile at the same position of phase f-1,
+// held by the neighbouring workgroup and earlier in its order, and the P
+// workgroups of a ring are consecutive, so resident rings always finish.
+#include "ring_device.h"
+
+#include <hip/hip_runtime.h>
+#include <string.h>
 
 namespace ringc {
-size_t gemm_rs_workspace_bytes(int P, size_t n) { (void)P; (void)n; return 0; }
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 256;                       // output tile rows
+constexpr int kBN = 256;                       // output tile columns
+constexpr int kBK = 64;                        // K per LDS stage
+constexpr int kLdsStride = kBK + 8;            // bf16 per LDS row (16 B pad vs bank conflicts)
+constexpr int kLdsOperand = kBM * kLdsStride;  // bf16 per operand per stage
+constexpr int kTileFloats = kBM * kBN;
+constexpr int kQuarterFloats = kTileFloats / 4;
+
+struct GemmParams {
+    const unsigned short* A[RING_MAX_RANKS];   // bf16 M x K, row-major
+    const unsigned short* B[RING_MAX_RANKS];   // bf16 K x N, row-major
+    float* out[RING_MAX_RANKS];                // fp32 (M / P) x N, row-major
+    float* work;                               // P x (M x N) fp32, tiles in fragment order
+    int* flags;                                // [P-1][P][tpc][4] flags
+    Status* status;
+    long long spin_limit;
+    int P, M, N, K;
+    int tm_chunk;                              // tile rows per chunk (M / P / 256)
+    int tn;                                    // tile columns (N / 256)
+    int tpc;                                   // tiles per chunk
+    int groups;                                // rings of workgroups (gridDim.x / P)
+};
+
+__device__ __forceinline__ int* gflag(const GemmParams& p, int row, int q, int pos, int wave) {
+    return p.flags + ((((size_t)row * p.P + q) * p.tpc + pos) * 4 + wave) * kFlagStride;
+}
+
+// One wave's quarter of tile (tr, tc) of rank q's workspace, fragment order.
+__device__ __forceinline__ float* work_quarter(const GemmParams& p, int q, int tr, int tc, int wave) {
+    return p.work + (size_t)q * p.M * p.N + ((size_t)tr * p.tn + tc) * kTileFloats +
+           (size_t)wave * kQuarterFloats;
+}
+
+// acc[mi][ni] of lane `lane` lives at float offset ((mi * 4 + ni) * 64 + lane) * 16
+// of a quarter: byte offset lane * 64 + frag_soff(mi, ni, part) for its part-th 4 floats.
+__device__ __forceinline__ unsigned frag_soff(int mi, int ni, int part) {
+    return (unsigned)((mi * 4 + ni) * 64 * 64 + part * 16);
+}
+
+// C tile (tr, tc) of A_q B_q into acc (wave's quarter).
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const unsigned short* __restrict__ A,
+                                          const unsigned short* __restrict__ B, int tr, int tc,
+                                          f32x16 (&acc)[4][4], unsigned short* lds, int tid,
+                                          int lane, int wr, int wc) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+
+    const int K = p.K, N = p.N;
+    // A panel: 256 rows x K; B panel: K rows x 256 columns (row stride N).
+    const rsrc_t Av = tile_view(A + (size_t)tr * kBM * K, (long long)kBM * K * 2);
+    const rsrc_t Bv = tile_view(B + (size_t)tc * kBN, ((long long)(K - 1) * N + kBN) * 2);
+    // global -> register staging: A as 2048 vectors of 8 k (row = v / 8),
+    // B as an 8 x 8 block of bf16 per thread (k block tid / 32, n block tid % 32)
+    const int kb = tid >> 5, nb = tid & 31;
+    const unsigned a_voff = (unsigned)(((tid >> 3) * K + (tid & 7) * 8) * 2);
+    const unsigned b_voff = (unsigned)((kb * 8 * N + nb * 8) * 2);
+    u32x4 ra[8], rb[8];
+    auto load = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(Av, a_voff, (i * 32 * K + kt * kBK) * 2, POL_PLAIN);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            rb[i] = __builtin_amdgcn_raw_buffer_load_b128(Bv, b_voff, (kt * kBK + i) * N * 2, POL_PLAIN);
+    };
+    auto stage = [&](int buf) {
+        unsigned short* As = lds + buf * 2 * kLdsOperand;
+        unsigned short* Bs = As + kLdsOperand;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *(u32x4*)(As + ((tid >> 3) + 32 * i) * kLdsStride + (tid & 7) * 8) = ra[i];
+        // transpose the 8 (k) x 8 (n) block: column n becomes 8 contiguous k
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            u32x4 o;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const unsigned lo = rb[2 * d][n >> 1], hi = rb[2 * d + 1][n >> 1];
+                o[d] = __builtin_amdgcn_perm(hi, lo, (n & 1) ? 0x07060302u : 0x05040100u);
+            }
+            *(u32x4*)(Bs + (nb * 8 + n) * kLdsStride + kb * 8) = o;
+        }
+    };
+    const int KT = K / kBK;
+    load(0);
+    stage(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) load(kt + 1);
+        const unsigned short* As = lds + (kt & 1) * 2 * kLdsOperand;
+        const unsigned short* Bs = As + kLdsOperand;
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            bf16x8 af[4], bfr[4];
+            const int koff = kk * 16 + (lane >> 5) * 8;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                af[mi] = *(const bf16x8*)(As + (wr * 128 + mi * 32 + (lane & 31)) * kLdsStride + koff);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                bfr[ni] = *(const bf16x8*)(Bs + (wc * 128 + ni * 32 + (lane & 31)) * kLdsStride + koff);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+        }
+        if (kt + 1 < KT) stage((kt + 1) & 1);
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned short lds[2 * 2 * kLdsOperand];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave >> 1, wc = wave & 1;
+    const int P = p.P;
+    const int q = blockIdx.x % P;
+    const int grp = blockIdx.x / P;
+    const int left = (q - 1 + P) % P;
+    const unsigned short* A = p.A[q];
+    const unsigned short* B = p.B[q];
+
+    for (int phase = 0; phase < P; ++phase) {
+        // chunk of this phase (see the schedule above); P = 1 has one phase
+        const int c = P == 1 ? 0 : (phase == 0 ? (q - 1 + P) % P : (q - phase - 1 + 2 * P) % P);
+        const bool final_phase = (phase == P - 1);
+        for (int pos = grp; pos < p.tpc; pos += p.groups) {
+            const int tr = c * p.tm_chunk + pos / p.tn;
+            const int tc = pos % p.tn;
+            f32x16 acc[4][4];
+            gemm_tile(p, A, B, tr, tc, acc, lds, tid, lane, wr, wc);
+
+            if (phase > 0) {
+                // add the left neighbour's tile of the previous phase
+                int* f = gflag(p, phase - 1, left, pos, wave);
+                const int seen = peek_flag(f);
+                if (!wait_flag(f, p.status, p.spin_limit, q, phase, pos, lane, seen)) return;
+                const rsrc_t rv = tile_view(work_quarter(p, left, tr, tc, wave), kQuarterFloats * 4);
+#pragma unroll
+                for (int b = 0; b < 16; ++b) {
+                    const int mi = b >> 2, ni = b & 3;
+                    u32x4 x[4];
+#pragma unroll
+                    for (int part = 0; part < 4; ++part)
+                        x[part] = ld16s<POL_DEV>(rv, lane * 64u, frag_soff(mi, ni, part));
+#pragma unroll
+                    for (int part = 0; part < 4; ++part)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[mi][ni][part * 4 + e] = __uint_as_float(x[part][e]) + acc[mi][ni][part * 4 + e];
+                }
+            }
+            if (!final_phase) {
+                const rsrc_t wv = tile_view(work_quarter(p, q, tr, tc, wave), kQuarterFloats * 4);
+#pragma unroll
+                for (int b = 0; b < 16; ++b) {
+                    const int mi = b >> 2, ni = b & 3;
+#pragma unroll
+                    for (int part = 0; part < 4; ++part) {
+                        u32x4 x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = __float_as_uint(acc[mi][ni][part * 4 + e]);
+                        st16s<POL_DEV>(x, wv, lane * 64u, frag_soff(mi, ni, part));
+                    }
+                }
+                signal_flag(gflag(p, phase, q, pos, wave), lane);
+            } else {
+                // final sum of chunk q: row-major into out[q]
+                const int lrow0 = (tr - q * p.tm_chunk) * kBM + wr * 128;
+                float* ob = p.out[q] + (size_t)lrow0 * p.N + tc * kBN + wc * 128;
+                const rsrc_t ov = tile_view(ob, ((long long)127 * p.N + 128) * 4);
+                const unsigned voff = (unsigned)((4 * (lane >> 5) * p.N + (lane & 31)) * 4);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int row = mi * 32 + 8 * (v >> 2) + (v & 3);   // + 4 (lane / 32)
+                            st4s<POL_PLAIN>(__float_as_uint(acc[mi][ni][v]), ov, voff,
+                                            (unsigned)((row * p.N + ni * 32) * 4));
+                        }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- host side
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct GemmWs {
+    size_t flags_off, flags_bytes, work_off, work_bytes, total;
+};
+
+static GemmWs gemm_ws_layout(int P, size_t MN) {
+    GemmWs w;
+    const size_t tpc = MN / (size_t)P / (size_t)kTileFloats;
+    const size_t rows = P > 1 ? (size_t)(P - 1) : 1;
+    w.flags_off = kStatusBytes;
+    w.flags_bytes = align256(rows * (size_t)P * (tpc ? tpc : 1) * 4 * kFlagStride * sizeof(int));
+    w.work_off = w.flags_off + w.flags_bytes;
+    w.work_bytes = P > 1 ? align256((size_t)P * MN * sizeof(float)) : 0;
+    w.total = w.work_off + w.work_bytes;
+    return w;
+}
+
+size_t gemm_rs_workspace_bytes(int P, size_t n) {
+    if (P < 1 || P > RING_MAX_RANKS || n == 0 || n % ((size_t)P * kTileFloats)) return 0;
+    return gemm_ws_layout(P, n).total;
+}
+
 }  // namespace ringc
+
+using namespace ringc;
 
 extern "C" int gemm_reduce_scatter(const void* const* A, const void* const* B, void* const* out,
                                    int P, int M, int N, int K, void* ws, size_t ws_bytes,
                                    void* stream) {
-    (void)A; (void)B; (void)out; (void)P; (void)M; (void)N; (void)K; (void)ws; (void)ws_bytes;
-    (void)stream;
-    return RING_EUNSUPPORTED;
+    if (P < 1 || P > RING_MAX_RANKS || M < 0 || N < 0 || K < 0) return RING_EINVAL;
+    if (!A || !B || !out) return RING_EINVAL;
+    if (M == 0 || N == 0) return RING_OK;
+    if (M % (kBM * P) || N % kBN || K % kBK || K == 0) return RING_EUNSUPPORTED;
+    for (int r = 0; r < P; ++r) {
+        if (!A[r] || !B[r] || !out[r]) return RING_EINVAL;
+        if (((uintptr_t)A[r] | (uintptr_t)B[r] | (uintptr_t)out[r]) & 15) return RING_EINVAL;
+    }
+    const size_t MN = (size_t)M * N;
+    const GemmWs lay = gemm_ws_layout(P, MN);
+    if (!ws || ((uintptr_t)ws & 255) || ws_bytes < lay.total) return RING_EWORKSPACE;
+
+    GemmParams prm;
+    memset(&prm, 0, sizeof prm);
+    for (int r = 0; r < P; ++r) {
+        prm.A[r] = (const unsigned short*)A[r];
+        prm.B[r] = (const unsigned short*)B[r];
+        prm.out[r] = (float*)out[r];
+    }
+    prm.work = (float*)((char*)ws + lay.work_off);
+    prm.flags = (int*)((char*)ws + lay.flags_off);
+    prm.status = (Status*)ws;
+    const DevInfo di = dev_info();
+    prm.spin_limit = (long long)(tuning().timeout_s * (double)di.wall_khz * 1000.0);
+    prm.P = P;
+    prm.M = M;
+    prm.N = N;
+    prm.K = K;
+    prm.tm_chunk = M / P / kBM;
+    prm.tn = N / kBN;
+    prm.tpc = prm.tm_chunk * prm.tn;
+
+    // one workgroup per CU at most, so every ring of P workgroups is resident
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_rs_kernel, 256, 0) != hipSuccess ||
+        occ < 1)
+        return RING_EHIP;
+    long long groups = di.cus / P;
+    if (groups > prm.tpc) groups = prm.tpc;
+    if (groups < 1) return RING_EUNSUPPORTED;   // more ranks than compute units
+    prm.groups = (int)groups;
+    hipLaunchKernelGGL(gemm_rs_kernel, dim3((unsigned)(groups * P)), dim3(256), 0,
+                       (hipStream_t)stream, prm);
+    return hipGetLastError() == hipSuccess ? RING_OK : RING_EHIP;
 }

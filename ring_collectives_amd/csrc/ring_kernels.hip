@@ -42,14 +42,11 @@
 // the rings that are resident can always finish and free room for the rest;
 // the host also keeps the grid within half the occupancy limit, so normally
 // every wave is resident from the start.  A watchdog bounds every wait.
-#include "ring_internal.h"
+#include "ring_device.h"
 
 #include <hip/hip_runtime.h>
 
 namespace ringc {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 enum { DT_F32 = RING_F32, DT_BF16 = RING_BF16, DT_I32 = RING_I32 };
 
@@ -77,96 +74,17 @@ __device__ __forceinline__ int* flag_at(const RingParams& p, int k, int r, int j
     return p.flags + ((size_t)(k * p.P + r) * p.T + j) * kFlagStride;
 }
 
-__device__ void report_timeout(const RingParams& p, int r, int k, int j) {
-    int expected = 0;
-    if (__hip_atomic_compare_exchange_strong(&p.status->code, &expected, (int)RING_ETIMEOUT,
-                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)) {
-        int info = (r & 0xFF) | ((k & 0xFF) << 8) | ((j < 32767 ? j : 32767) << 16);
-        __hip_atomic_store(&p.status->info, info, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
-
-// ---------------------------------------------------------------- memory access
-// Every access goes through a buffer descriptor over exactly one tile, so the
-// hardware drops any store and zeroes any load that falls outside it (the
-// ragged last tile of a chunk needs no separate path).
-//
-// Cache policy (CDNA3/4 scope bits on the instruction itself):
-//   DEV  (sc1) device scope: a store is written through to the device's
-//        coherence point and a load does not return a stale copy from this
-//        CU's L1 or this XCD's L2.  Used for every access that crosses ranks
-//        (what a rank stores for its neighbour, what it loads from it).
-//   PLAIN      default caching: a rank's own input, and the final all-gather
-//        round whose result no other wave reads before the launch ends.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kRsrcWord3 = 0x00020000;   // raw (unformatted) 32-bit buffer
-enum { POL_PLAIN = 0, POL_NT = 2, POL_DEV = 16 };
-
-__device__ __forceinline__ rsrc_t tile_view(const void* base, long long bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             kRsrcWord3);
-}
-template <int POL> __device__ __forceinline__ u32x4 ld16(rsrc_t v, unsigned off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(v, off, 0, POL);
-}
-template <int POL> __device__ __forceinline__ void st16(u32x4 x, rsrc_t v, unsigned off) {
-    __builtin_amdgcn_raw_buffer_store_b128(x, v, off, 0, POL);
-}
-template <int POL> __device__ __forceinline__ unsigned ld4(rsrc_t v, unsigned off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(v, off, 0, POL);
-}
-template <int POL> __device__ __forceinline__ void st4(unsigned x, rsrc_t v, unsigned off) {
-    __builtin_amdgcn_raw_buffer_store_b32(x, v, off, 0, POL);
-}
-template <int POL> __device__ __forceinline__ unsigned short ld2(rsrc_t v, unsigned off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(v, off, 0, POL);
-}
-template <int POL> __device__ __forceinline__ void st2(unsigned short x, rsrc_t v, unsigned off) {
-    __builtin_amdgcn_raw_buffer_store_b16(x, v, off, 0, POL);
-}
-// ---------------------------------------------------------------- flags
-// First look at flag (k, left, j); the caller issues its independent loads
-// before it spins on the result.
+// Wait for flag (k, left, j): the left neighbour finished tile j of round k-1.
 __device__ __forceinline__ int peek_flag(const RingParams& p, int k, int left, int j) {
-    return __hip_atomic_load(flag_at(p, k, left, j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return peek_flag(flag_at(p, k, left, j));
 }
-
-// Spin until flag (k, left, j) is set (unless `seen` already is), then clear
-// it.  Returns false if the launch is being abandoned (this wave timed out,
-// or another one did).  The loads of the neighbour's data that follow are
-// device-scope and are issued only after the flag was seen (control
-// dependency; the empty asm keeps the compiler from hoisting them).
-__device__ bool wait_flag(const RingParams& p, int k, int left, int r, int j, int lane, int seen) {
-    int* f = flag_at(p, k, left, j);
-    if (seen < 1) {
-        const long long t0 = wall_clock64();
-        unsigned spins = 0;
-        while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < 1) {
-            __builtin_amdgcn_s_sleep(2);
-            if ((++spins & 31u) == 0) {
-                if (__hip_atomic_load(&p.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
-                    return false;
-                if (wall_clock64() - t0 > p.spin_limit) {
-                    if (lane == 0) report_timeout(p, r, k, j);
-                    return false;
-                }
-            }
-        }
-    }
-    asm volatile("" ::: "memory");
-    // This wave is the flag's only reader in this launch: clear it for the next.
-    if (lane == 0) __hip_atomic_store(f, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
+__device__ __forceinline__ bool wait_flag(const RingParams& p, int k, int left, int r, int j,
+                                          int lane, int seen) {
+    return wait_flag(flag_at(p, k, left, j), p.status, p.spin_limit, r, k, j, lane, seen);
 }
-
-// Publish this wave's round: wait until all its memory operations are
-// complete (its device-scope stores are at the coherence point, its loads of
-// the neighbour's data have returned), then set flag (k, r, j).
+// Set flag (k, r, j): this rank finished tile j of round k-1.
 __device__ __forceinline__ void signal_flag(const RingParams& p, int k, int r, int j, int lane) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (lane == 0)
-        __hip_atomic_fetch_add(flag_at(p, k, r, j), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    signal_flag(flag_at(p, k, r, j), lane);
 }
 
 // ---------------------------------------------------------------- tile bodies

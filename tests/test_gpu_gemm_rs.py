@@ -1,0 +1,142 @@
+"""GPU parity of the fused GEMM + reduce-scatter against the CPU oracle.
+
+The per-rank products are accumulated by the matrix cores in an order the
+hardware fixes, so general inputs are compared within a bound: componentwise,
+|got - ref| <= (K + P) 2^-24 * sum_q sum_k |A_q[i,k] B_q[k,j]| (recursive
+summation of K products, then P - 1 ring additions; Higham, Accuracy and
+Stability of Numerical Algorithms, section 3.1), with ref the fp64 value.
+Two input families are exact in any order and compared bit for bit:
+integer-valued operands, and a diagonal A (each output is one exact product),
+which leaves only the ring's fp32 additions -- so the reduce-scatter order is
+checked bit for bit against the oracle's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_collectives_amd import _native as N
+from ring_collectives_amd import collectives as rc
+from ring_collectives_amd import inputs
+
+from _gpu_helpers import note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    N.lib()
+    yield
+
+
+def _dev_bf16(x):
+    return [torch.from_numpy(np.ascontiguousarray(x[q]).view(np.int16)).cuda().view(torch.bfloat16)
+            for q in range(x.shape[0])]
+
+
+def _run(A, B, ws=None):
+    P, M, K = A.shape
+    Nn = B.shape[2]
+    a, b = _dev_bf16(A), _dev_bf16(B)
+    out = [torch.full((M // P, Nn), float("nan"), dtype=torch.float32, device="cuda") for _ in range(P)]
+    ws = rc.gemm_reduce_scatter(a, b, out, ws=ws)
+    torch.cuda.synchronize()
+    assert rc.last_error(ws)[0] == 0
+    return np.stack([o.cpu().numpy() for o in out]), ws
+
+
+@pytest.mark.parametrize("P,M,N,K", [(1, 256, 256, 64), (2, 512, 256, 128), (4, 1024, 512, 64),
+                                     (4, 2048, 256, 192), (3, 768, 768, 64)])
+def test_integer_valued_exact(P, M, N, K):
+    note("gemm_rs integer P=%d M=%d N=%d K=%d" % (P, M, N, K))
+    rng = np.random.default_rng(200 + P)
+    A = inputs.small_int_bf16(rng, (P, M, K))
+    B = inputs.small_int_bf16(rng, (P, K, N))
+    got, _ = _run(A, B)
+    Ai = oracle.bf16_to_f32(A).astype(np.int64)
+    Bi = oracle.bf16_to_f32(B).astype(np.int64)
+    total = sum(Ai[q] @ Bi[q] for q in range(P))
+    rows = M // P
+    for r in range(P):
+        np.testing.assert_array_equal(got[r].astype(np.int64), total[r * rows:(r + 1) * rows],
+                                      err_msg="rank %d" % r)
+
+
+@pytest.mark.parametrize("P", [2, 3, 4])
+def test_diagonal_a_ring_order_bit_exact(P):
+    """A_q = diag(a_q): every product is exact in fp32, so only the ring's
+    fp32 additions round, and they must match the oracle bit for bit."""
+    note("gemm_rs diagonal P=%d" % P)
+    M = 256 * P * 2
+    rng = np.random.default_rng(300 + P)
+    a = inputs.bf16_bits(rng.standard_normal((P, M)).astype(np.float32))
+    A = np.zeros((P, M, M), dtype=np.uint16)
+    for q in range(P):
+        A[q][np.arange(M), np.arange(M)] = a[q]
+    # wide dynamic range so the association order shows in the bits
+    Bf = rng.standard_normal((P, M, 512)).astype(np.float32) * np.exp2(rng.integers(-12, 12, size=(P, M, 512))).astype(np.float32)
+    B = inputs.bf16_bits(Bf)
+    got, _ = _run(A, B)
+    want = oracle.gemm_reduce_scatter(A, B)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("P,M,N,K", [(1, 256, 512, 512), (2, 512, 512, 1024), (4, 1024, 768, 512)])
+def test_normal_within_bound(P, M, N, K):
+    note("gemm_rs normal P=%d M=%d N=%d K=%d" % (P, M, N, K))
+    A, B = inputs.gemm_operands(P, M, N, K, seed=400 + P)
+    got, _ = _run(A, B)
+    rows = M // P
+    for r in range(P):
+        ref, mag = oracle.gemm_reduce_scatter_rows_f64(A, B, r, np.arange(rows))
+        err = np.abs(got[r].astype(np.float64) - ref) / mag
+        assert err.max() <= (K + P) * 2.0 ** -24, (r, err.max())
+    # and against the oracle's fp32 pipeline (fp64 products rounded, ring adds)
+    want = oracle.gemm_reduce_scatter(A, B)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - want)) <= 1e-3 * np.max(np.abs(want))
+
+
+def test_full_size_sampled_rows():
+    """P = 4, A_q and B_q bf16 4096 x 4096, normal(0, 1/64), seed 4: sampled
+    output rows of every rank against the fp64 oracle."""
+    P, M, Nn, K = 4, 4096, 4096, 4096
+    note("gemm_rs full size generate")
+    A, B = inputs.gemm_operands(P, M, Nn, K)
+    note("gemm_rs full size run")
+    got, ws = _run(A, B)
+    rng = np.random.default_rng(5)
+    rows_local = np.unique(np.concatenate([[0, 1, 255, 256, 511, 1023],
+                                           rng.integers(0, M // P, size=10)]))
+    worst = 0.0
+    for r in range(P):
+        ref, mag = oracle.gemm_reduce_scatter_rows_f64(A, B, r, rows_local)
+        err = np.abs(got[r][rows_local].astype(np.float64) - ref) / mag
+        worst = max(worst, float(err.max()))
+    assert worst <= (K + P) * 2.0 ** -24, worst
+    print("max normalised error %.3e" % worst)
+
+
+def test_repeated_calls_and_errors():
+    P, M, Nn, K = 4, 1024, 256, 128
+    rng = np.random.default_rng(7)
+    A = inputs.small_int_bf16(rng, (P, M, K))
+    B = inputs.small_int_bf16(rng, (P, K, Nn))
+    got1, ws = _run(A, B)
+    got2, _ = _run(A, B, ws=ws)
+    np.testing.assert_array_equal(got1, got2)
+    a, b = _dev_bf16(A), _dev_bf16(B)
+    out = [torch.empty((M // P, Nn), dtype=torch.float32, device="cuda") for _ in range(P)]
+    # K = 96 is not a multiple of 64: rejected before any launch
+    a96 = [x[:, :96].contiguous() for x in a]
+    b96 = [x[:96].contiguous() for x in b]
+    with pytest.raises(N.RingError) as e:
+        rc.gemm_reduce_scatter(a96, b96, out)
+    assert e.value.code == N.RING_EUNSUPPORTED
+    small = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(N.RingError) as e:
+        rc.gemm_reduce_scatter(a, b, out, ws=small)
+    assert e.value.code == N.RING_EWORKSPACE
