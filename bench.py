@@ -33,6 +33,9 @@ WORKLOADS = {
     "ar_f32_p8_64Mi": dict(op="all_reduce", P=8, n=64 << 20, kind="f32", seed=2, std=1.0),
     "ar_bf16_p16_128Mi": dict(op="all_reduce", P=16, n=128 << 20, kind="bf16", seed=3, std=1e-2),
     "ar_f32_p4_small": dict(op="all_reduce", P=4, n=4096, kind="f32", seed=0, std=None),
+    # fused GEMM + reduce-scatter: P = 4, A_q, B_q bf16 4096 x 4096, normal(0, 1/64)
+    "gemm_rs_p4_4096": dict(op="gemm_rs", P=4, M=4096, N=4096, K=4096, kind="bf16", seed=4,
+                            std=1.0 / 64, n=4096 * 4096),
     # a plain copy of known size (2 x 256 MiB read + written): counter calibration
     "ppermute_f32_p2_64Mi": dict(op="ppermute", P=2, n=64 << 20, kind="f32", seed=2, std=1.0),
 }
@@ -96,6 +99,8 @@ def _traffic(workload: str):
 def _make_inputs(w):
     import numpy as np
     from ring_collectives_amd import inputs
+    if w["op"] == "gemm_rs":
+        return inputs.gemm_operands(w["P"], w["M"], w["N"], w["K"], std=w["std"], seed=w["seed"])
     if w["kind"] == "f32" and w["std"] is None:
         return inputs.to_chunk_major(inputs.small_f32(w["P"], (8, 512)), w["P"])
     if w["kind"] == "f32":
@@ -136,6 +141,81 @@ def _cpu_baseline(w, x):
                   "sample": "the whole workload (%d ranks x %d elements), one thread" % (P, n)}
 
 
+def _gemm_main(args, w):
+    """GEMM + reduce-scatter: TFLOP/s against the bf16 MFMA peak."""
+    import numpy as np
+    import torch
+    from ring_collectives_amd import _native as N
+    from ring_collectives_amd import collectives as rc
+    P, M, Nn, K = w["P"], w["M"], w["N"], w["K"]
+    print("[bench] workload %s: generating inputs" % args.workload, file=sys.stderr, flush=True)
+    A, B = _make_inputs(w)
+    torch.cuda.set_device(0)
+    a = [torch.from_numpy(A[q].view(np.int16)).cuda().view(torch.bfloat16) for q in range(P)]
+    b = [torch.from_numpy(B[q].view(np.int16)).cuda().view(torch.bfloat16) for q in range(P)]
+    out = [torch.empty((M // P, Nn), dtype=torch.float32, device="cuda") for _ in range(P)]
+    nb = N.lib().ring_workspace_bytes(N.OP_GEMM_REDUCE_SCATTER, P, M * Nn, N.RING_F32)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        rc.gemm_reduce_scatter(a, b, out, ws=ws)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        rc.gemm_reduce_scatter(a, b, out, ws=ws)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    code, info = rc.last_error(ws)
+    if code != 0:
+        raise SystemExit("gemm_reduce_scatter reported %s (info %#x)" % (N.strerror(code), info))
+    kern_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    avg = sum(kern_ms) / len(kern_ms)
+    flop = 2.0 * P * M * Nn * K
+    print("[bench] %d steps: %.4f ms/step (wall), kernel avg %.4f ms" % (args.steps, ms_step, avg),
+          file=sys.stderr, flush=True)
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        import oracle
+        rows = np.arange(0, M // P, (M // P) // 16)          # 16 sampled rows per rank
+        t = time.perf_counter()
+        worst = 0.0
+        for r in range(P):
+            ref, mag = oracle.gemm_reduce_scatter_rows_f64(A, B, r, rows)
+            got = out[r].cpu().numpy()[rows].astype(np.float64)
+            worst = max(worst, float((np.abs(got - ref) / mag).max()))
+        dt = time.perf_counter() - t
+        sflop = 2.0 * P * P * len(rows) * Nn * K
+        cpu = {"value": round(sflop / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle", "seconds": round(dt, 3),
+               "sample": "%d output rows per rank (fp64 rows of sum_q A_q B_q, NumPy BLAS)" % len(rows)}
+        parity = worst <= (K + P) * 2.0 ** -24
+        print("[bench] sampled rows max normalised error %.3e (bound %.3e)"
+              % (worst, (K + P) * 2.0 ** -24), file=sys.stderr, flush=True)
+    line = {
+        "metric": "GEMM + ring reduce-scatter TFLOP/s, P=%d virtual ranks, bf16 %dx%dx%d per rank"
+                  % (P, M, Nn, K),
+        "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 (f32 accumulate)", "data": "synthetic",
+        "config": {"workload": args.workload, "P": P, "M": M, "N": Nn, "K": K,
+                   "flop_per_step": flop, "parallelism": "P virtual ranks on 1 GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(flop / (avg * 1e-3) / 1e12, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flop / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "gemm_rs_kernel", "kernel_ms_avg": round(avg, 5)},
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +235,8 @@ def main():
     from ring_collectives_amd import collectives as rc
 
     w = WORKLOADS[args.workload]
+    if w["op"] == "gemm_rs":
+        return _gemm_main(args, w)
     P, n, kind = w["P"], w["n"], w["kind"]
     print("[bench] workload %s: generating inputs" % args.workload, file=sys.stderr, flush=True)
     x = _make_inputs(w)

@@ -28,8 +28,9 @@
 // w % 2) as 4 x 4 MFMA blocks of 32 x 32.  K advances 64 at a time through a
 // double-buffered LDS stage (A as 256 rows x 64 k, B transposed in registers
 // to 256 columns x 64 k so both MFMA operands read 16 contiguous bytes).
-// Partial tiles travel through the workspace in MFMA fragment order (each
-// lane's 16 accumulators contiguous), and a flag guards each wave's quarter,
+// Partial tiles travel through the workspace in MFMA fragment order (what one
+// instruction of a wave moves is 1 KiB of contiguous memory), and a flag
+// guards each wave's quarter,
 // so producer wave w and consumer wave w of the next rank pair up directly.
 //
 // Work assignment: workgroup g serves rank g % P and tile positions
@@ -53,6 +54,8 @@ constexpr int kBK = 64;                        // K per LDS stage
 constexpr int kLdsStride = kBK + 8;            // bf16 per LDS row (16 B pad vs bank conflicts)
 constexpr int kLdsOperand = kBM * kLdsStride;  // bf16 per operand per stage
 constexpr int kTileFloats = kBM * kBN;
+constexpr int kEpiStride = 128 + 4;            // floats per LDS row of the final transpose
+constexpr int kEpiWaveFloats = 32 * kEpiStride;  // one wave's 32-row band
 constexpr int kQuarterFloats = kTileFloats / 4;
 
 struct GemmParams {
@@ -80,10 +83,11 @@ __device__ __forceinline__ float* work_quarter(const GemmParams& p, int q, int t
            (size_t)wave * kQuarterFloats;
 }
 
-// acc[mi][ni] of lane `lane` lives at float offset ((mi * 4 + ni) * 64 + lane) * 16
-// of a quarter: byte offset lane * 64 + frag_soff(mi, ni, part) for its part-th 4 floats.
+// Fragment order of a quarter: the part-th 4 accumulators of block (mi, ni)
+// of lane l sit at byte lane * 16 + frag_soff(mi, ni, part), so one
+// instruction of a wave moves 1 KiB of contiguous memory.
 __device__ __forceinline__ unsigned frag_soff(int mi, int ni, int part) {
-    return (unsigned)((mi * 4 + ni) * 64 * 64 + part * 16);
+    return (unsigned)(((mi * 4 + ni) * 4 + part) * 1024);
 }
 
 // C tile (tr, tc) of A_q B_q into acc (wave's quarter).
@@ -103,8 +107,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const unsigned sh
     const rsrc_t Av = tile_view(A + (size_t)tr * kBM * K, (long long)kBM * K * 2);
     const rsrc_t Bv = tile_view(B + (size_t)tc * kBN, ((long long)(K - 1) * N + kBN) * 2);
     // global -> register staging: A as 2048 vectors of 8 k (row = v / 8),
-    // B as an 8 x 8 block of bf16 per thread (k block tid / 32, n block tid % 32)
-    const int kb = tid >> 5, nb = tid & 31;
+    // B as an 8 x 8 block of bf16 per thread (n block tid / 8, k block tid % 8:
+    // 16 consecutive lanes then write 16 different 16-byte bank groups of LDS)
+    const int nb = tid >> 3, kb = tid & 7;
     const unsigned a_voff = (unsigned)(((tid >> 3) * K + (tid & 7) * 8) * 2);
     const unsigned b_voff = (unsigned)((kb * 8 * N + nb * 8) * 2);
     u32x4 ra[8], rb[8];
@@ -136,6 +141,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const unsigned sh
     };
     const int KT = K / kBK;
     load(0);
+    __syncthreads();   // the previous tile's epilogue may still be reading LDS
     stage(0);
     __syncthreads();
     for (int kt = 0; kt < KT; ++kt) {
@@ -186,56 +192,88 @@ __global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmParams p) {
             f32x16 acc[4][4];
             gemm_tile(p, A, B, tr, tc, acc, lds, tid, lane, wr, wc);
 
+            // Epilogue.  Each 32 x 32 block is loaded, added and stored in one
+            // go so only a few accumulators are live outside the AGPRs.  The
+            // per-lane offsets are recomputed here (the empty asm hides them
+            // from loop-invariant hoisting, which would otherwise keep 256
+            // element addresses alive across the tile loop).
+            unsigned lane16 = (unsigned)lane * 16u;
+            asm volatile("" : "+v"(lane16));
+            rsrc_t rv = tile_view(nullptr, 0);
             if (phase > 0) {
-                // add the left neighbour's tile of the previous phase
+                // the left neighbour's tile of the previous phase (raw at s = 0)
                 int* f = gflag(p, phase - 1, left, pos, wave);
                 const int seen = peek_flag(f);
                 if (!wait_flag(f, p.status, p.spin_limit, q, phase, pos, lane, seen)) return;
-                const rsrc_t rv = tile_view(work_quarter(p, left, tr, tc, wave), kQuarterFloats * 4);
-#pragma unroll
-                for (int b = 0; b < 16; ++b) {
-                    const int mi = b >> 2, ni = b & 3;
-                    u32x4 x[4];
-#pragma unroll
-                    for (int part = 0; part < 4; ++part)
-                        x[part] = ld16s<POL_DEV>(rv, lane * 64u, frag_soff(mi, ni, part));
-#pragma unroll
-                    for (int part = 0; part < 4; ++part)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc[mi][ni][part * 4 + e] = __uint_as_float(x[part][e]) + acc[mi][ni][part * 4 + e];
-                }
+                rv = tile_view(work_quarter(p, left, tr, tc, wave), kQuarterFloats * 4);
             }
             if (!final_phase) {
                 const rsrc_t wv = tile_view(work_quarter(p, q, tr, tc, wave), kQuarterFloats * 4);
 #pragma unroll
-                for (int b = 0; b < 16; ++b) {
-                    const int mi = b >> 2, ni = b & 3;
+                for (int mi = 0; mi < 4; ++mi) {
+                    u32x4 x[4][4];
+                    if (phase > 0) {
 #pragma unroll
-                    for (int part = 0; part < 4; ++part) {
-                        u32x4 x;
+                        for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] = __float_as_uint(acc[mi][ni][part * 4 + e]);
-                        st16s<POL_DEV>(x, wv, lane * 64u, frag_soff(mi, ni, part));
+                            for (int part = 0; part < 4; ++part)
+                                x[ni][part] = ld16s<POL_DEV>(rv, lane16, frag_soff(mi, ni, part));
                     }
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                        for (int part = 0; part < 4; ++part) {
+                            u32x4 o;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float c = acc[mi][ni][part * 4 + e];
+                                o[e] = __float_as_uint(phase > 0 ? __uint_as_float(x[ni][part][e]) + c : c);
+                            }
+                            st16s<POL_DEV>(o, wv, lane16, frag_soff(mi, ni, part));
+                        }
                 }
                 signal_flag(gflag(p, phase, q, pos, wave), lane);
             } else {
-                // final sum of chunk q: row-major into out[q]
+                // Final sum of chunk q, row-major into out[q].  Each wave turns
+                // its quarter around in its own slice of LDS (free after the K
+                // loop), 32 rows at a time, and writes 512-byte rows.
+                int lds_lane = wave * kEpiWaveFloats + 4 * (lane >> 5) * kEpiStride + (lane & 31);
+                asm volatile("" : "+v"(lds_lane));
+                float* stage_lane = reinterpret_cast<float*>(lds) + lds_lane;   // scatter base
+                int lds_row = wave * kEpiWaveFloats + (lane >> 5) * kEpiStride + (lane & 31) * 4;
+                asm volatile("" : "+v"(lds_row));
+                const float* gather_lane = reinterpret_cast<const float*>(lds) + lds_row;
                 const int lrow0 = (tr - q * p.tm_chunk) * kBM + wr * 128;
                 float* ob = p.out[q] + (size_t)lrow0 * p.N + tc * kBN + wc * 128;
                 const rsrc_t ov = tile_view(ob, ((long long)127 * p.N + 128) * 4);
-                const unsigned voff = (unsigned)((4 * (lane >> 5) * p.N + (lane & 31)) * 4);
+                unsigned lane_out = (unsigned)(((lane >> 5) * p.N + (lane & 31) * 4) * 4);
+                asm volatile("" : "+v"(lane_out));
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
+                for (int mi = 0; mi < 4; ++mi) {
+                    u32x4 x[4][4];
+                    if (phase > 0) {
+#pragma unroll
+                        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                            for (int part = 0; part < 4; ++part)
+                                x[ni][part] = ld16s<POL_DEV>(rv, lane16, frag_soff(mi, ni, part));
+                    }
 #pragma unroll
                     for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
                         for (int v = 0; v < 16; ++v) {
-                            const int row = mi * 32 + 8 * (v >> 2) + (v & 3);   // + 4 (lane / 32)
-                            st4s<POL_PLAIN>(__float_as_uint(acc[mi][ni][v]), ov, voff,
-                                            (unsigned)((row * p.N + ni * 32) * 4));
+                            const float c = acc[mi][ni][v];
+                            const float o = phase > 0 ? __uint_as_float(x[ni][v >> 2][v & 3]) + c : c;
+                            stage_lane[(8 * (v >> 2) + (v & 3)) * kEpiStride + ni * 32] = o;
                         }
+                    // 32 rows x 128 columns: in step i lane l reads 16 bytes of row
+                    // 2 i + l / 32 at column 4 (l % 32)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const u32x4 o = *(const u32x4*)(gather_lane + 2 * i * kEpiStride);
+                        st16s<POL_PLAIN>(o, ov, lane_out, (unsigned)(((mi * 32 + 2 * i) * p.N) * 4));
+                    }
+                }
             }
         }
     }
