@@ -25,9 +25,9 @@
 //
 // Tiles.  One 256-thread workgroup computes one 256 x 256 fp32 output tile
 // with v_mfma_f32_32x32x16_bf16: wave w owns the 128 x 128 quarter (w / 2,
-// w % 2) as 4 x 4 MFMA blocks of 32 x 32.  K advances 64 at a time through a
-// double-buffered LDS stage (A as 256 rows x 64 k, B transposed in registers
-// to 256 columns x 64 k so both MFMA operands read 16 contiguous bytes).
+// w % 2) as 4 x 4 MFMA blocks of 32 x 32.  K advances 64 at a time through
+// two LDS stages filled by direct global->LDS loads while the other stage
+// feeds the matrix cores.
 // Partial tiles travel through the workspace in MFMA fragment order (what one
 // instruction of a wave moves is 1 KiB of contiguous memory), and a flag
 // guards each wave's quarter,
@@ -50,9 +50,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256;                       // output tile rows
 constexpr int kBN = 256;                       // output tile columns
-constexpr int kBK = 64;                        // K per LDS stage
-constexpr int kLdsStride = kBK + 8;            // bf16 per LDS row (16 B pad vs bank conflicts)
-constexpr int kLdsOperand = kBM * kLdsStride;  // bf16 per operand per stage
+constexpr int kBK = 32;                        // K per LDS stage
 constexpr int kTileFloats = kBM * kBN;
 constexpr int kEpiStride = 128 + 4;            // floats per LDS row of the final transpose
 constexpr int kEpiWaveFloats = 32 * kEpiStride;  // one wave's 32-row band
@@ -90,11 +88,59 @@ __device__ __forceinline__ unsigned frag_soff(int mi, int ni, int part) {
     return (unsigned)(((mi * 4 + ni) * 4 + part) * 1024);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// K-loop pipeline: kNS LDS stages of kBK values of k each, filled kNS - 1
+// stages ahead of the stage the matrix cores read.
+constexpr int kStageA = kBM * kBK * 2;            // bytes of A per stage
+constexpr int kStageBytes = kStageA + kBK * kBN * 2;
+constexpr int kNS = 4;
+#ifndef RING_GEMM_SCHED
+#define RING_GEMM_SCHED 0
+#endif
+constexpr int kLdsBytes = kNS * kStageBytes;
+constexpr int kAChunks = kBK / 8;                  // 16-byte chunks per A row
+constexpr int kARowsPerInst = 64 / kAChunks;       // A rows one 1-KiB load fills
+constexpr int kLoadsA = kBM / kARowsPerInst / 4;   // A load instructions per wave per stage
+constexpr int kLoadsB = kBK / 2 / 4;               // B load instructions per wave per stage
+constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
+static_assert(kBK == 32, "the swizzles below assume 4 chunks per A row");
+static_assert(kLdsBytes <= 160 * 1024, "LDS");
+
+// LDS stage layout (bytes): A at 0 (256 rows m x kBK k), B at kStageA (kBK
+// rows k x 256 n, 512 B per row); no padding.  Both are filled by direct
+// global->LDS loads (one instruction = 64 lanes x 16 B = 1 KiB of consecutive
+// LDS) and spread over the banks by XOR-ing the 16-byte chunk index:
+//   A: chunk c of row m is stored at chunk c ^ ((m >> 2) & 3)
+//   B: chunk c of row k is stored at chunk c ^ (2 (k & 3))
+// so the fragment reads below touch 16 different bank groups per 16 lanes.
+
+__device__ __forceinline__ lds_void* lds_at(unsigned short* lds, unsigned byte) {
+    return (lds_void*)((__attribute__((address_space(3))) char*)(lds_void*)lds + byte);
+}
+
+// Wait until at most `n` of this wave's vector memory operations are in flight.
+__device__ __forceinline__ void wait_vm(int n) {
+    if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // C tile (tr, tc) of A_q B_q into acc (wave's quarter).
+//
+// MFMA operands (v_mfma_f32_32x32x16_bf16): lane l holds A[m = l % 32][k =
+// 8 (l / 32) + t] and B[k = 8 (l / 32) + t][n = l % 32], t = 0..7.  A is read
+// with ds_read_b128 (8 consecutive k of one row).  B comes from its natural
+// k-major layout through the LDS transpose read ds_read_b64_tr_b16: within
+// each group of 16 lanes, when lane j points at row kb + j / 4, columns
+// cb + 4 (j % 4) .. +3, lane i receives rows kb .. kb+3 of column cb + i, so
+// two such reads give a lane its 8 consecutive k of one column.
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, const unsigned short* __restrict__ A,
                                           const unsigned short* __restrict__ B, int tr, int tc,
                                           f32x16 (&acc)[4][4], unsigned short* lds, int tid,
-                                          int lane, int wr, int wc) {
+                                          int lane, int wave, int wr, int wc) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -106,71 +152,119 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const unsigned sh
     // A panel: 256 rows x K; B panel: K rows x 256 columns (row stride N).
     const rsrc_t Av = tile_view(A + (size_t)tr * kBM * K, (long long)kBM * K * 2);
     const rsrc_t Bv = tile_view(B + (size_t)tc * kBN, ((long long)(K - 1) * N + kBN) * 2);
-    // global -> register staging: A as 2048 vectors of 8 k (row = v / 8),
-    // B as an 8 x 8 block of bf16 per thread (n block tid / 8, k block tid % 8:
-    // 16 consecutive lanes then write 16 different 16-byte bank groups of LDS)
-    const int nb = tid >> 3, kb = tid & 7;
-    const unsigned a_voff = (unsigned)(((tid >> 3) * K + (tid & 7) * 8) * 2);
-    const unsigned b_voff = (unsigned)((kb * 8 * N + nb * 8) * 2);
-    u32x4 ra[8], rb[8];
-    auto load = [&](int kt) {
+
+    // Direct loads.  A instruction i of wave w fills rows 16 (4 w + i) .. +15
+    // (lane: row + lane / 4, stored chunk lane % 4); B instruction i fills k
+    // rows 2 (4 w + i), +1 (lane: row + lane / 32, stored chunk lane % 32).
+    // Each lane fetches the logical chunk its stored position holds.
+    const unsigned a_voff = (unsigned)(((lane >> 2) * K + ((lane & 3) ^ ((lane >> 4) & 3)) * 8) * 2);
+    unsigned b_voff[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(Av, a_voff, (i * 32 * K + kt * kBK) * 2, POL_PLAIN);
+    for (int par = 0; par < 2; ++par) {
+        const int kr = par * 2 + (lane >> 5);              // row mod 4 of this lane
+        const int cb = (lane & 31) ^ (2 * (kr & 3));
+        b_voff[par] = (unsigned)(((lane >> 5) * N + cb * 8) * 2);
+    }
+    // Fill LDS stage `slot` with K block kt.
+    auto issue = [&](int kt, int slot) {
+        const unsigned base = (unsigned)(slot * kStageBytes);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            rb[i] = __builtin_amdgcn_raw_buffer_load_b128(Bv, b_voff, (kt * kBK + i) * N * 2, POL_PLAIN);
-    };
-    auto stage = [&](int buf) {
-        unsigned short* As = lds + buf * 2 * kLdsOperand;
-        unsigned short* Bs = As + kLdsOperand;
+        for (int i = 0; i < kLoadsA; ++i) {
+            const int r0 = (wave * kLoadsA + i) * kARowsPerInst;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(Av, lds_at(lds, base + r0 * kBK * 2), 16, a_voff,
+                                                     (unsigned)((r0 * K + kt * kBK) * 2), 0, POL_PLAIN);
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *(u32x4*)(As + ((tid >> 3) + 32 * i) * kLdsStride + (tid & 7) * 8) = ra[i];
-        // transpose the 8 (k) x 8 (n) block: column n becomes 8 contiguous k
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            u32x4 o;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const unsigned lo = rb[2 * d][n >> 1], hi = rb[2 * d + 1][n >> 1];
-                o[d] = __builtin_amdgcn_perm(hi, lo, (n & 1) ? 0x07060302u : 0x05040100u);
-            }
-            *(u32x4*)(Bs + (nb * 8 + n) * kLdsStride + kb * 8) = o;
+        for (int i = 0; i < kLoadsB; ++i) {
+            const int k0 = (wave * kLoadsB + i) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(Bv, lds_at(lds, base + kStageA + k0 * 512), 16,
+                                                     b_voff[i & 1],
+                                                     (unsigned)((kt * kBK + k0) * N * 2), 0, POL_PLAIN);
         }
     };
+
+    // Fragment read offsets (bytes within a stage).
+    //   A (mi, kk): row wr*128 + mi*32 + l%32, chunk (2 kk + l/32) ^ ((l >> 2) & 3)
+    //   B (ni, kk, half h): row kk*16 + 8 (g/2) + 4h + i/4, column
+    //     wc*128 + ni*32 + 16 (g%2) + 4 (i%4), g = l/16, i = l%16
+    unsigned a_off[kBK / 16], b_off[4];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk)
+        a_off[kk] = (unsigned)((wr * 128 + (lane & 31)) * kBK * 2 +
+                               (((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) * 16));
+    {
+        const int g = lane >> 4, i = lane & 15;
+        const int krow = 8 * (g >> 1) + (i >> 2);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int n = wc * 128 + ni * 32 + 16 * (g & 1) + 4 * (i & 3);
+            const int chunk = (n >> 3) ^ (2 * (krow & 3));
+            b_off[ni] = (unsigned)(kStageA + krow * 512 + chunk * 16 + (n & 7) * 2);
+        }
+    }
+    auto read_frags = [&](unsigned base, int kk, bf16x8 (&af)[4], bf16x8 (&bf)[4]) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            af[mi] = *(const bf16x8*)((const char*)lds + base + a_off[kk] + mi * 32 * kBK * 2);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const unsigned o = base + b_off[ni] + kk * 16 * 512;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_at(lds, o));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lds_at(lds, o + 4 * 512));
+            typedef short s16x8 __attribute__((ext_vector_type(8)));
+            const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            bf[ni] = __builtin_bit_cast(bf16x8, v);
+        }
+    };
+
     const int KT = K / kBK;
-    load(0);
     __syncthreads();   // the previous tile's epilogue may still be reading LDS
-    stage(0);
-    __syncthreads();
+    // Every iteration issues one stage, so exactly kNS - 2 later stages are in
+    // flight when stage kt must have landed.  Past the end of K the issue
+    // re-reads the last K block into the slot that is never read again (the
+    // loop body stays one basic block for the scheduler).
+    for (int s = 0; s < kNS - 1; ++s) issue(s < KT ? s : KT - 1, s);
     for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 1 < KT) load(kt + 1);
-        const unsigned short* As = lds + (kt & 1) * 2 * kLdsOperand;
-        const unsigned short* Bs = As + kLdsOperand;
+        wait_vm((kNS - 2) * kLoadsPerStage);     // stage kt has landed (this wave's part)
+        __syncthreads();                          // everyone's has; stage kt-1 is free
+        const int nxt = kt + kNS - 1;
+        issue(nxt < KT ? nxt : KT - 1, nxt % kNS);
+        const unsigned base = (unsigned)((kt % kNS) * kStageBytes);
+        bf16x8 af[2][4], bf[2][4];
+        read_frags(base, 0, af[0], bf[0]);
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
-            bf16x8 af[4], bfr[4];
-            const int koff = kk * 16 + (lane >> 5) * 8;
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                af[mi] = *(const bf16x8*)(As + (wr * 128 + mi * 32 + (lane & 31)) * kLdsStride + koff);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                bfr[ni] = *(const bf16x8*)(Bs + (wc * 128 + ni * 32 + (lane & 31)) * kLdsStride + koff);
+            if (kk + 1 < kBK / 16) read_frags(base, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][mi], bf[kk & 1][ni],
+                                                                          acc[mi][ni], 0, 0, 0);
         }
-        if (kt + 1 < KT) stage((kt + 1) & 1);
-        __syncthreads();
+#if RING_GEMM_SCHED
+        // Interleave: the first k-slice's LDS reads, then one MFMA per
+        // direct load and per LDS read of the second k-slice, then the rest.
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+        for (int i = 0; i < kLoadsPerStage; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 32 - 12 - kLoadsPerStage, 0);
+#endif
     }
+    wait_vm(0);        // the trailing loads have landed
+    __syncthreads();   // all waves are done with the stages before the epilogue uses LDS
 }
 
 __global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned short lds[2 * 2 * kLdsOperand];
+    __shared__ __attribute__((aligned(16))) unsigned short lds[kLdsBytes / 2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -190,7 +284,7 @@ __global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmParams p) {
             const int tr = c * p.tm_chunk + pos / p.tn;
             const int tc = pos % p.tn;
             f32x16 acc[4][4];
-            gemm_tile(p, A, B, tr, tc, acc, lds, tid, lane, wr, wc);
+            gemm_tile(p, A, B, tr, tc, acc, lds, tid, lane, wave, wr, wc);
 
             // Epilogue.  Each 32 x 32 block is loaded, added and stored in one
             // go so only a few accumulators are live outside the AGPRs.  The
@@ -313,7 +407,7 @@ extern "C" int gemm_reduce_scatter(const void* const* A, const void* const* B, v
     if (P < 1 || P > RING_MAX_RANKS || M < 0 || N < 0 || K < 0) return RING_EINVAL;
     if (!A || !B || !out) return RING_EINVAL;
     if (M == 0 || N == 0) return RING_OK;
-    if (M % (kBM * P) || N % kBN || K % kBK || K == 0) return RING_EUNSUPPORTED;
+    if (M % (kBM * P) || N % kBN || K % 64 || K == 0) return RING_EUNSUPPORTED;
     for (int r = 0; r < P; ++r) {
         if (!A[r] || !B[r] || !out[r]) return RING_EINVAL;
         if (((uintptr_t)A[r] | (uintptr_t)B[r] | (uintptr_t)out[r]) & 15) return RING_EINVAL;
