@@ -18,7 +18,10 @@ int elem_bytes(int dtype) {
     }
 }
 
-int elems_per_vec(int dtype) { return elem_bytes(dtype) ? 16 / elem_bytes(dtype) : 0; }
+// Elements one lane handles per tile vector: 16 bytes of fp32/int32; for
+// bf16, 4 elements (8 bytes of input, 16 bytes of fp32 carry), so every
+// carry store of a wave covers contiguous memory.
+int elems_per_vec(int dtype) { return dtype == RING_BF16 ? 4 : (elem_bytes(dtype) ? 16 / elem_bytes(dtype) : 0); }
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -51,7 +54,7 @@ static ring_tuning_t& tuning_ref() {
     static ring_tuning_t t = [] {
         ring_tuning_t d;
         d.tile_vecs = 8;
-        d.waves_per_cu = 8;
+        d.waves_per_cu = 12;
         d.map_mode = 0;
         d.timeout_s = 5.0;
         d.stepwise = 0;

@@ -38,6 +38,13 @@ template <int POL> __device__ __forceinline__ u32x4 ld16(rsrc_t v, unsigned off)
 template <int POL> __device__ __forceinline__ void st16(u32x4 x, rsrc_t v, unsigned off) {
     __builtin_amdgcn_raw_buffer_store_b128(x, v, off, 0, POL);
 }
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <int POL> __device__ __forceinline__ u32x2 ld8(rsrc_t v, unsigned off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(v, off, 0, POL);
+}
+template <int POL> __device__ __forceinline__ void st8(u32x2 x, rsrc_t v, unsigned off) {
+    __builtin_amdgcn_raw_buffer_store_b64(x, v, off, 0, POL);
+}
 template <int POL> __device__ __forceinline__ unsigned ld4(rsrc_t v, unsigned off) {
     return __builtin_amdgcn_raw_buffer_load_b32(v, off, 0, POL);
 }

@@ -91,7 +91,7 @@ __device__ __forceinline__ void signal_flag(const RingParams& p, int k, int r, i
 template <int DT> struct Elem;
 template <> struct Elem<DT_F32> { typedef float T; static constexpr int VPE = 4; };
 template <> struct Elem<DT_I32> { typedef int T; static constexpr int VPE = 4; };
-template <> struct Elem<DT_BF16> { typedef unsigned short T; static constexpr int VPE = 8; };
+template <> struct Elem<DT_BF16> { typedef unsigned short T; static constexpr int VPE = 4; };
 
 template <int DT> __device__ __forceinline__ unsigned add1(unsigned a, unsigned b);
 template <> __device__ __forceinline__ unsigned add1<DT_F32>(unsigned a, unsigned b) {
@@ -169,40 +169,37 @@ __device__ bool rs_tile_bf16(const RingParams& p, int r, int left, int k, int j,
     const rsrc_t out16 = tile_view((unsigned short*)p.dst[r] + t.e0, t.len * 2);
     const int seen = wait ? peek_flag(p, k, left, j) : 1;
     if (p.vec_ok) {
-        u32x4 a[U];
+        // lane vector v = 4 elements: 8 bytes of bf16, 16 bytes of fp32 carry
+        u32x2 a[U];
 #pragma unroll
-        for (int i = 0; i < U; ++i) a[i] = ld16<POL_PLAIN>(own, (unsigned)(lane + i * kWave) * 16u);
+        for (int i = 0; i < U; ++i) a[i] = ld8<POL_PLAIN>(own, (unsigned)(lane + i * kWave) * 8u);
         if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const unsigned v = (unsigned)(lane + i * kWave);   // a vector of 8 elements
-            float x[8];
+            const unsigned v = (unsigned)(lane + i * kWave);
+            float x[4];
             if (s == 0) {
-                const u32x4 b = ld16<POL_DEV>(rcv16, v * 16u);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) { x[2 * q] = bf16_lo(b[q]); x[2 * q + 1] = bf16_hi(b[q]); }
+                const u32x2 b = ld8<POL_DEV>(rcv16, v * 8u);
+                x[0] = bf16_lo(b[0]); x[1] = bf16_hi(b[0]); x[2] = bf16_lo(b[1]); x[3] = bf16_hi(b[1]);
             } else {
-                const u32x4 b0 = ld16<POL_DEV>(rcv32, v * 32u);
-                const u32x4 b1 = ld16<POL_DEV>(rcv32, v * 32u + 16u);
+                const u32x4 b = ld16<POL_DEV>(rcv32, v * 16u);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) { x[q] = __uint_as_float(b0[q]); x[4 + q] = __uint_as_float(b1[q]); }
+                for (int q = 0; q < 4; ++q) x[q] = __uint_as_float(b[q]);
             }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                x[2 * q] = bf16_lo(a[i][q]) + x[2 * q];
-                x[2 * q + 1] = bf16_hi(a[i][q]) + x[2 * q + 1];
-            }
+            x[0] = bf16_lo(a[i][0]) + x[0];
+            x[1] = bf16_hi(a[i][0]) + x[1];
+            x[2] = bf16_lo(a[i][1]) + x[2];
+            x[3] = bf16_hi(a[i][1]) + x[3];
             if (last) {
+                u32x2 o;
+                o[0] = pack_bf16(x[0], x[1]);
+                o[1] = pack_bf16(x[2], x[3]);
+                st8<POL_DEV>(o, out16, v * 8u);
+            } else {
                 u32x4 o;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) o[q] = pack_bf16(x[2 * q], x[2 * q + 1]);
-                st16<POL_DEV>(o, out16, v * 16u);
-            } else {
-                u32x4 o0, o1;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) { o0[q] = __float_as_uint(x[q]); o1[q] = __float_as_uint(x[4 + q]); }
-                st16<POL_DEV>(o0, out32, v * 32u);
-                st16<POL_DEV>(o1, out32, v * 32u + 16u);
+                for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(x[q]);
+                st16<POL_DEV>(o, out32, v * 16u);
             }
         }
     } else {
@@ -248,6 +245,7 @@ __device__ __forceinline__ void copy_tile(rsrc_t to, rsrc_t from, long long len,
 template <int DT, int U>
 __device__ bool ag_tile(const RingParams& p, int r, int left, int k, int j, int lane, bool wait) {
     constexpr int ESZ = sizeof(typename Elem<DT>::T);
+    constexpr int UC = U * Elem<DT>::VPE * ESZ / 16;   // 16-byte vectors per lane per tile
     const int t = k - (p.P - 1);
     const int c = ag_chunk(r, t, p.P);
     const TilePos q = tile_pos(p, c, j);
@@ -258,17 +256,17 @@ __device__ bool ag_tile(const RingParams& p, int r, int left, int k, int j, int 
     if (p.compact_src && t == 0) {
         // Place this rank's own piece (input, no wait, read by nobody else:
         // the right neighbour takes it from the input too) ...
-        copy_tile<U, ESZ, POL_PLAIN>(tile_view((char*)p.dst[r] + ((long long)r * p.C + q.off) * ESZ, nb),
+        copy_tile<UC, ESZ, POL_PLAIN>(tile_view((char*)p.dst[r] + ((long long)r * p.C + q.off) * ESZ, nb),
                                      tile_view((const char*)p.src[r] + q.off * ESZ, nb),
                                      q.len, p.vec_ok, false, lane);
         // ... and take the left neighbour's piece straight from its input.
-        copy_tile<U, ESZ, POL_PLAIN>(out, tile_view((const char*)p.src[left] + q.off * ESZ, nb),
+        copy_tile<UC, ESZ, POL_PLAIN>(out, tile_view((const char*)p.src[left] + q.off * ESZ, nb),
                                      q.len, p.vec_ok, pub, lane);
         return true;
     }
     const int seen = wait ? peek_flag(p, k, left, j) : 1;
     if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
-    copy_tile<U, ESZ, POL_DEV>(out, tile_view((const char*)p.dst[left] + q.e0 * ESZ, nb), q.len,
+    copy_tile<UC, ESZ, POL_DEV>(out, tile_view((const char*)p.dst[left] + q.e0 * ESZ, nb), q.len,
                                p.vec_ok, pub, lane);
     return true;
 }
