@@ -69,17 +69,21 @@ def moved_bytes(op: str, P: int, n: int, kind: str) -> int:
     return rs + ag
 
 
-def _sha_kernels() -> str:
+KERNEL_SOURCE = {"ring_step_kernel": "ring_kernels.hip", "copy_kernel_tab": "ring_kernels.hip",
+                 "gemm_rs_kernel": "gemm_rs.hip"}
+
+
+def _sha_source(kernel: str) -> str:
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "ring_collectives_amd", "csrc", "ring_kernels.hip"), "rb") as f:
+    with open(os.path.join(ROOT, "ring_collectives_amd", "csrc", KERNEL_SOURCE[kernel]), "rb") as f:
         h.update(f.read())
     return h.hexdigest()
 
 
-def _traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "ring_step_kernel_%s_counters.txt" % workload)
+def _traffic(workload: str, kernel: str):
+    """HBM-side bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_counters.txt" % (kernel, workload))
     if not os.path.exists(path):
         return None
     kv = {}
@@ -88,7 +92,7 @@ def _traffic(workload: str):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != _sha_kernels():
+    if kv.get("kernel_source_sha256") != _sha_source(kernel):
         return None
     try:
         return int(float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"]))
@@ -209,7 +213,8 @@ def _gemm_main(args, w):
         "roofline": {"bound": "mfma", "achieved": round(flop / (avg * 1e-3) / 1e12, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flop / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "gemm_rs_kernel", "kernel_ms_avg": round(avg, 5)},
+                     "traffic": _traffic(args.workload, "gemm_rs_kernel"), "kernel": "gemm_rs_kernel",
+                     "kernel_ms_avg": round(avg, 5)},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
     }
@@ -299,7 +304,7 @@ def main():
         parity = bool(np.array_equal(got, want))
         print("[bench] GPU output bit-exact vs oracle: %s" % parity, file=sys.stderr, flush=True)
 
-    traffic = _traffic(args.workload)
+    traffic = _traffic(args.workload, kernel)
     line = {
         "metric": "ring %s HBM GB/s & %% of peak, P=%d virtual ranks, %d MiB %s/rank"
                   % (w["op"].replace("_", "-"), P, n * (2 if kind == "bf16" else 4) >> 20,

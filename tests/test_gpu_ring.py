@@ -290,3 +290,38 @@ def test_watchdog_reports_timeout():
     rc.all_reduce(src, dst, ws=ws)
     assert rc.last_error(ws) == (0, 0)
     np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.all_reduce(x)))
+
+
+# ---------------------------------------------------------------- full sizes
+def test_full_size_fp32_p8_64Mi():
+    """The bandwidth workload (P = 8, 64 Mi fp32 per rank, normal(0, 1), seed
+    2) in the default launch configuration: every element bit for bit, plus
+    the componentwise bound against the fp64 rank-order sum on a sample."""
+    P, n = 8, 64 << 20
+    note("full size fp32 P=8 generate")
+    x = inputs.normal_f32(P, n, seed=inputs.SEED_F32_BW)
+    note("full size fp32 P=8 run")
+    got = _run_ar(x, "f32")
+    want = oracle.all_reduce(x)
+    np.testing.assert_array_equal(bits(got), bits(want))
+    idx = np.random.default_rng(0).integers(0, n, size=1 << 16)
+    ref, mag = oracle.rank_sum_f64(np.ascontiguousarray(x[:, idx]))
+    err = np.abs(got[0, idx].astype(np.float64) - ref) / mag
+    assert err.max() <= 1e-6 * P
+
+
+def test_full_size_bf16_p16_128Mi():
+    """The gradient-bucket workload (P = 16, 128 Mi bf16 per rank,
+    normal(0, 0.01), seed 3): every element bit for bit against the oracle's
+    fp32-carry ring, and within 1e-2 of the fp64 sum on a sample."""
+    P, n = 16, 128 << 20
+    note("full size bf16 P=16 generate")
+    x = inputs.normal_bf16(P, n, seed=inputs.SEED_BF16)
+    note("full size bf16 P=16 run")
+    got = _run_ar(x, "bf16")
+    want = oracle.all_reduce_bf16(x)
+    np.testing.assert_array_equal(got, want)
+    idx = np.random.default_rng(1).integers(0, n, size=1 << 16)
+    ref, mag = oracle.rank_sum_f64(np.ascontiguousarray(x[:, idx]), bf16=True)
+    err = np.abs(oracle.bf16_to_f32(got[0, idx]).astype(np.float64) - ref) / mag
+    assert err.max() <= 1e-2

@@ -1,0 +1,104 @@
+"""The oracle's pins must catch plausible mistakes.  Each case compiles a copy
+of oracle/ring_oracle.c with one mistake planted (a wrong index, a wrong
+neighbour, a dropped term, a wrong sign, a wrong rounding, a missing round),
+loads it in place of the real one, and runs the pin suite's checks: at least
+one must fail.  The unmodified source must pass them all."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ring_oracle.c")
+
+MUTANTS = {
+    "rs chunk off by one": ("return (r - s - 2 + 2 * P) % P;", "return (r - s - 1 + 2 * P) % P;"),
+    "right neighbour instead of left": ("return (r - 1 + P) % P;", "return (r + 1) % P;"),
+    "all-gather chunk off by one": ("return (r - t - 1 + P) % P;", "return (r - t + P) % P;"),
+    "fp32 add drops own term": ("tmp[(size_t)r * C + i] = own[i] + recv[i];",
+                                "tmp[(size_t)r * C + i] = recv[i];"),
+    "fp32 reads neighbour input instead of partial":
+        ("const float *recv = state + (size_t)left_of(r, P) * n + (size_t)c * C;",
+         "const float *recv = src + (size_t)left_of(r, P) * n + (size_t)c * C;"),
+    "int32 wrong sign": ("(uint32_t)own[i] + (uint32_t)recv[i]", "(uint32_t)own[i] - (uint32_t)recv[i]"),
+    "bf16 rounds half up": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0x8000u;"),
+    "bf16 carry rounded every hop": ("tmp[(size_t)r * C + i] = bf16_to_f32(own[i]) + recv[i];",
+                                     "tmp[(size_t)r * C + i] = bf16_to_f32(oracle_bf16_from_f32(bf16_to_f32(own[i]) + recv[i]));"),
+    "ppermute does not shift": ("s + (size_t)left_of(r, P) * bytes_per_rank, bytes_per_rank);",
+                                "s + (size_t)r * bytes_per_rank, bytes_per_rank);"),
+    "all-reduce misses a gather round": ("return oracle_all_gather(state, P, n, sizeof(float), P - 1);",
+                                         "return oracle_all_gather(state, P, n, sizeof(float), P - 2);"),
+    "all-gather places pieces at the wrong chunk":
+        ("memcpy((uint8_t *)state + (size_t)r * nb + (size_t)r * Cb,",
+         "memcpy((uint8_t *)state + (size_t)r * nb + (size_t)((r + 1) % P) * Cb,"),
+    "magnitude sum without abs": ("            m += fabs(x);\n        }\n        sum[i] = a;\n        if (abssum) abssum[i] = m;\n    }\n    return 0;\n}\n\nint oracle_rank_sum_f64_bf16",
+                                  "            m += x;\n        }\n        sum[i] = a;\n        if (abssum) abssum[i] = m;\n    }\n    return 0;\n}\n\nint oracle_rank_sum_f64_bf16"),
+}
+
+
+def _checks():
+    yield "ppermute table", pins.test_ppermute_matches_page_table
+    yield "all-gather table", pins.test_all_gather_matches_page_slot_table
+    for P in (2, 3, 4, 8):
+        yield "psum_scatter P=%d" % P, lambda P=P: pins.test_reduce_scatter_is_psum_scatter_int32(P)
+        yield "contributors P=%d" % P, lambda P=P: pins.test_reduce_scatter_contributor_sets(P)
+        yield "int32 all-reduce P=%d" % P, lambda P=P: pins.test_all_reduce_int32_brute_force(P)
+    yield "owner last", pins.test_fp32_association_order_owner_last
+    yield "chain direction", pins.test_fp32_association_order_chain_direction
+    yield "p2", pins.test_p2_single_round
+    for P in (2, 4):
+        yield "fp32 bound P=%d" % P, lambda P=P: pins.test_all_reduce_fp32_within_recursive_sum_bound(P)
+        yield "int fp32 exact P=%d" % P, lambda P=P: pins.test_all_reduce_int_valued_fp32_exact(P)
+    for bits, want in [(0x3F808000, 0x3F80), (0x3F818000, 0x3F82), (0x00008000, 0x0000)]:
+        yield "bf16 %#x" % bits, lambda b=bits, w=want: pins.test_bf16_rne_hand_cases(b, w)
+    yield "bf16 vs torch", pins.test_bf16_rne_matches_torch
+    yield "bf16 nan", pins.test_bf16_rne_nan_stays_nan
+    yield "all-gather concat", lambda: pins.test_all_gather_is_concatenation(4)
+    yield "rank sum", lambda: pins.test_rank_sum_f64_matches_numpy(3)
+    yield "bf16 carry", pins.test_bf16_carry_is_fp32_until_owner
+    yield "bf16 bound", lambda: pins.test_bf16_all_reduce_one_rounding_bound(4)
+
+
+def _load_variant(tmp_path, text, name):
+    c = tmp_path / ("%s.c" % name)
+    so = tmp_path / ("%s.so" % name)
+    c.write_text(text)
+    subprocess.check_call(["gcc", *oracle._CFLAGS, str(c), "-o", str(so), "-lm"])
+    lib = ctypes.CDLL(str(so))
+    return lib
+
+
+def _run_checks_with(lib, monkeypatch):
+    real = oracle._load()
+    for fname in ("oracle_ppermute", "oracle_reduce_scatter_f32", "oracle_reduce_scatter_i32",
+                  "oracle_all_gather", "oracle_all_gather_place", "oracle_all_reduce_f32",
+                  "oracle_all_reduce_i32", "oracle_reduce_scatter_bf16", "oracle_all_reduce_bf16",
+                  "oracle_bf16_from_f32_array", "oracle_rank_sum_f64_f32", "oracle_rank_sum_f64_bf16"):
+        f, g = getattr(lib, fname), getattr(real, fname)
+        f.argtypes, f.restype = g.argtypes, g.restype
+    monkeypatch.setattr(oracle, "_lib", lib)
+    failed = []
+    for label, check in _checks():
+        try:
+            check()
+        except (AssertionError, ValueError):
+            failed.append(label)
+    return failed
+
+
+def test_unmodified_source_passes(tmp_path, monkeypatch):
+    lib = _load_variant(tmp_path, open(SRC).read(), "clean")
+    assert _run_checks_with(lib, monkeypatch) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert old in text, "mutation site not found: %s" % name
+    lib = _load_variant(tmp_path, text.replace(old, new, 1), "mutant")
+    failed = _run_checks_with(lib, monkeypatch)
+    assert failed, "no pin caught the planted mistake '%s'" % name
