@@ -73,10 +73,15 @@ KERNEL_SOURCE = {"ring_step_kernel": "ring_kernels.hip", "copy_kernel_tab": "rin
                  "gemm_rs_kernel": "gemm_rs.hip"}
 
 
+KERNEL_HEADERS = ("ring_device.h", "ring_internal.h")
+
+
 def _sha_source(kernel: str) -> str:
+    """Hash of the kernel's source file and the device headers it includes."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "ring_collectives_amd", "csrc", KERNEL_SOURCE[kernel]), "rb") as f:
-        h.update(f.read())
+    for name in (KERNEL_SOURCE[kernel],) + KERNEL_HEADERS:
+        with open(os.path.join(ROOT, "ring_collectives_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 

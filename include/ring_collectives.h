@@ -149,7 +149,9 @@ int ring_all_reduce(const void *const *src, void *const *dst, int P, size_t n,
  * sum_q A[q] B[q].  The per-rank products are accumulated in fp32 on the
  * matrix cores; the sum over ranks follows the fp32 ring reduce-scatter over
  * row-block chunks (chunk c = rows [c M/P, (c+1) M/P)).
- * Shapes this version accepts: M % (256 P) == 0, N % 256 == 0, K % 64 == 0.
+ * Shapes this version accepts: M % (256 P) == 0, N % 128 == 0, K % 64 == 0.
+ * Output tiles are 256 x 256 or 256 x 128 (see gemm_tile_n below); results
+ * are the same bits either way.
  */
 int gemm_reduce_scatter(const void *const *A, const void *const *B, void *const *out,
                         int P, int M, int N, int K, void *ws, size_t ws_bytes,
@@ -182,6 +184,11 @@ const char *ring_strerror(int code);
  *                  of "Triton-distributed 语义", best practice 8).
  *   drop_round     test hook: if >= 1, rank 0 never signals round drop_round,
  *                  so its right neighbour's wait must end in RING_ETIMEOUT.
+ *   gemm_tile_n    output tile width of gemm_reduce_scatter: 128 (two
+ *                  4-wave workgroups per compute unit), 256 (one 8-wave
+ *                  workgroup; needs N % 256 == 0), or 0 to choose per call:
+ *                  256 when there are at least as many 256 x 256 tiles per
+ *                  chunk as compute units per rank, else 128.
  */
 typedef struct {
     int tile_vecs;
@@ -190,6 +197,7 @@ typedef struct {
     double timeout_s;
     int stepwise;
     int drop_round;
+    int gemm_tile_n;
 } ring_tuning_t;
 
 void ring_get_tuning(ring_tuning_t *t);

@@ -47,7 +47,8 @@ static int env_int(const char* name, int dflt) {
 static bool tuning_valid(const ring_tuning_t& x) {
     return (x.tile_vecs == 4 || x.tile_vecs == 8 || x.tile_vecs == 16) && x.waves_per_cu >= 4 &&
            x.waves_per_cu <= 16 && (x.map_mode == 0 || x.map_mode == 2) && x.timeout_s > 0 &&
-           x.timeout_s < 3600 && (x.stepwise == 0 || x.stepwise == 1) && x.drop_round >= 0;
+           x.timeout_s < 3600 && (x.stepwise == 0 || x.stepwise == 1) && x.drop_round >= 0 &&
+           (x.gemm_tile_n == 0 || x.gemm_tile_n == 128 || x.gemm_tile_n == 256);
 }
 
 static ring_tuning_t& tuning_ref() {
@@ -59,6 +60,7 @@ static ring_tuning_t& tuning_ref() {
         d.timeout_s = 5.0;
         d.stepwise = 0;
         d.drop_round = 0;
+        d.gemm_tile_n = 0;
         ring_tuning_t x = d;
         x.tile_vecs = env_int("RING_TILE_VECS", d.tile_vecs);
         x.waves_per_cu = env_int("RING_WAVES_PER_CU", d.waves_per_cu);
@@ -66,6 +68,7 @@ static ring_tuning_t& tuning_ref() {
         const char* to = getenv("RING_TIMEOUT_S");
         if (to && *to) x.timeout_s = atof(to);
         x.stepwise = env_int("RING_STEPWISE", 0);
+        x.gemm_tile_n = env_int("RING_GEMM_TILE_N", d.gemm_tile_n);
         return tuning_valid(x) ? x : d;
     }();
     return t;

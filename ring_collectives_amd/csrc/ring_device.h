@@ -51,15 +51,17 @@ template <int POL> __device__ __forceinline__ unsigned ld4(rsrc_t v, unsigned of
 template <int POL> __device__ __forceinline__ void st4(unsigned x, rsrc_t v, unsigned off) {
     __builtin_amdgcn_raw_buffer_store_b32(x, v, off, 0, POL);
 }
-// Variants with a wave-uniform byte offset `soff` (kept in a scalar register).
+// Load with a wave-uniform byte offset `soff` (kept in a scalar register).
+//
+// There is deliberately no store of that form.  The compiler inserts no wait
+// states between a buffer store of more than 8 bytes whose offset sits in a
+// scalar register and a following VALU write of the store's data registers,
+// and on gfx950 such a write, issued right after a 16-byte store, reached
+// memory in place of the stored value for part of the wave (seen with two
+// waves per SIMD).  Stores therefore carry their whole offset in the vector
+// register (soffset 0), the form the compiler does protect.
 template <int POL> __device__ __forceinline__ u32x4 ld16s(rsrc_t v, unsigned voff, unsigned soff) {
     return __builtin_amdgcn_raw_buffer_load_b128(v, voff, soff, POL);
-}
-template <int POL> __device__ __forceinline__ void st16s(u32x4 x, rsrc_t v, unsigned voff, unsigned soff) {
-    __builtin_amdgcn_raw_buffer_store_b128(x, v, voff, soff, POL);
-}
-template <int POL> __device__ __forceinline__ void st4s(unsigned x, rsrc_t v, unsigned voff, unsigned soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(x, v, voff, soff, POL);
 }
 template <int POL> __device__ __forceinline__ unsigned short ld2(rsrc_t v, unsigned off) {
     return __builtin_amdgcn_raw_buffer_load_b16(v, off, 0, POL);

@@ -156,10 +156,14 @@ def test_tuning_roundtrip_and_validation():
     try:
         prev = N.set_tuning(tile_vecs=16, map_mode=2)
         assert prev == old
+        assert old["gemm_tile_n"] == 0
         assert N.get_tuning()["tile_vecs"] == 16
+        N.set_tuning(gemm_tile_n=256)
+        assert N.get_tuning()["gemm_tile_n"] == 256
         for bad in ({"tile_vecs": 5}, {"waves_per_cu": 1}, {"waves_per_cu": 32}, {"map_mode": 1},
                     {"map_mode": 7},
-                    {"timeout_s": 0.0}, {"stepwise": 2}, {"drop_round": -1}):
+                    {"timeout_s": 0.0}, {"stepwise": 2}, {"drop_round": -1},
+                    {"gemm_tile_n": 64}, {"gemm_tile_n": 192}):
             with pytest.raises(N.RingError):
                 N.set_tuning(**bad)
     finally:

@@ -32,6 +32,15 @@ def _needs_gpu():
     yield
 
 
+@pytest.fixture(params=[128, 256])
+def tile_n(request):
+    """Both output tile widths: 256 x 128 (two workgroups per compute unit)
+    and 256 x 256 (one)."""
+    old = N.set_tuning(gemm_tile_n=request.param)
+    yield request.param
+    N.set_tuning(gemm_tile_n=old["gemm_tile_n"])
+
+
 def _dev_bf16(x):
     return [torch.from_numpy(np.ascontiguousarray(x[q]).view(np.int16)).cuda().view(torch.bfloat16)
             for q in range(x.shape[0])]
@@ -50,8 +59,8 @@ def _run(A, B, ws=None):
 
 @pytest.mark.parametrize("P,M,N,K", [(1, 256, 256, 64), (2, 512, 256, 128), (4, 1024, 512, 64),
                                      (4, 2048, 256, 192), (3, 768, 768, 64)])
-def test_integer_valued_exact(P, M, N, K):
-    note("gemm_rs integer P=%d M=%d N=%d K=%d" % (P, M, N, K))
+def test_integer_valued_exact(P, M, N, K, tile_n):
+    note("gemm_rs integer P=%d M=%d N=%d K=%d tile_n=%d" % (P, M, N, K, tile_n))
     rng = np.random.default_rng(200 + P)
     A = inputs.small_int_bf16(rng, (P, M, K))
     B = inputs.small_int_bf16(rng, (P, K, N))
@@ -66,10 +75,10 @@ def test_integer_valued_exact(P, M, N, K):
 
 
 @pytest.mark.parametrize("P", [2, 3, 4])
-def test_diagonal_a_ring_order_bit_exact(P):
+def test_diagonal_a_ring_order_bit_exact(P, tile_n):
     """A_q = diag(a_q): every product is exact in fp32, so only the ring's
     fp32 additions round, and they must match the oracle bit for bit."""
-    note("gemm_rs diagonal P=%d" % P)
+    note("gemm_rs diagonal P=%d tile_n=%d" % (P, tile_n))
     M = 256 * P * 2
     rng = np.random.default_rng(300 + P)
     a = inputs.bf16_bits(rng.standard_normal((P, M)).astype(np.float32))
@@ -100,6 +109,32 @@ def test_normal_within_bound(P, M, N, K):
     assert np.max(np.abs(got - want)) <= 1e-3 * np.max(np.abs(want))
 
 
+@pytest.mark.parametrize("P", [4, 8])
+def test_full_occupancy_integer_exact(P, tile_n):
+    """M = N = 4096: enough tiles that every compute unit holds as many
+    workgroups as it can, with rings of neighbouring ranks running in
+    different phases at once.  Integer-valued operands make every output
+    exact, so all elements are compared bit for bit, over repeated calls on
+    one workspace."""
+    M = Nn = 4096
+    K = 256
+    note("gemm_rs full occupancy P=%d tile_n=%d" % (P, tile_n))
+    rng = np.random.default_rng(600 + P)
+    A = inputs.small_int_bf16(rng, (P, M, K))
+    B = inputs.small_int_bf16(rng, (P, K, Nn))
+    want = oracle.gemm_reduce_scatter(A, B)
+    a, b = _dev_bf16(A), _dev_bf16(B)
+    ws = None
+    for call in range(3):
+        out = [torch.full((M // P, Nn), float("nan"), dtype=torch.float32, device="cuda") for _ in range(P)]
+        ws = rc.gemm_reduce_scatter(a, b, out, ws=ws)
+        torch.cuda.synchronize()
+        assert rc.last_error(ws)[0] == 0
+        got = np.stack([o.cpu().numpy() for o in out])
+        bad = int(np.count_nonzero(got.view(np.uint32) != want.view(np.uint32)))
+        assert bad == 0, "call %d: %d elements differ" % (call, bad)
+
+
 def test_full_size_sampled_rows():
     """P = 4, A_q and B_q bf16 4096 x 4096, normal(0, 1/64), seed 4: sampled
     output rows of every rank against the fp64 oracle."""
@@ -118,6 +153,30 @@ def test_full_size_sampled_rows():
         worst = max(worst, float(err.max()))
     assert worst <= (K + P) * 2.0 ** -24, worst
     print("max normalised error %.3e" % worst)
+
+
+def test_narrow_n_uses_128_wide_tiles():
+    """N = 384 is a multiple of 128 but not of 256: the automatic choice
+    takes 256 x 128 tiles and the result is exact; forcing 256-wide tiles is
+    rejected before any launch."""
+    P, M, Nn, K = 2, 512, 384, 128
+    note("gemm_rs N=384")
+    rng = np.random.default_rng(8)
+    A = inputs.small_int_bf16(rng, (P, M, K))
+    B = inputs.small_int_bf16(rng, (P, K, Nn))
+    assert N.get_tuning()["gemm_tile_n"] == 0
+    got, _ = _run(A, B)
+    want = oracle.gemm_reduce_scatter(A, B)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    old = N.set_tuning(gemm_tile_n=256)
+    try:
+        a, b = _dev_bf16(A), _dev_bf16(B)
+        out = [torch.empty((M // P, Nn), dtype=torch.float32, device="cuda") for _ in range(P)]
+        with pytest.raises(N.RingError) as e:
+            rc.gemm_reduce_scatter(a, b, out)
+        assert e.value.code == N.RING_EUNSUPPORTED
+    finally:
+        N.set_tuning(gemm_tile_n=old["gemm_tile_n"])
 
 
 def test_repeated_calls_and_errors():
