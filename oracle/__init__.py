@@ -67,6 +67,9 @@ def _load():
             "oracle_all_reduce_i32": [vp, vp, i32, sz],
             "oracle_reduce_scatter_bf16": [vp, vp, vp, i32, sz, i32],
             "oracle_all_reduce_bf16": [vp, vp, vp, i32, sz],
+            "oracle_reduce_scatter_bidir_f32": [vp, vp, i32, sz, i32],
+            "oracle_reduce_scatter_bidir_i32": [vp, vp, i32, sz, i32],
+            "oracle_reduce_scatter_bidir_bf16": [vp, vp, vp, i32, sz, i32],
             "oracle_bf16_from_f32_array": [vp, vp, sz],
             "oracle_rank_sum_f64_f32": [vp, i32, sz, vp, vp],
             "oracle_rank_sum_f64_bf16": [vp, i32, sz, vp, vp],
@@ -126,6 +129,36 @@ def reduce_scatter(x: np.ndarray, rounds: int | None = None) -> np.ndarray:
     else:
         raise TypeError("reduce_scatter: fp32 or int32 (bf16: reduce_scatter_bf16)")
     _check(rc, "reduce_scatter")
+    return out
+
+
+def bidir_top_len(C: int) -> int:
+    """Elements in the top half of a chunk of C elements (the half that
+    travels left in the bidirectional reduce-scatter)."""
+    return C - C // 2
+
+
+def reduce_scatter_bidir(x: np.ndarray, steps: int | None = None) -> np.ndarray:
+    """Bidirectional ring reduce-scatter ("Pallas TPU Distributed Collectives
+    复习文档" section 4): top halves of the chunks travel left, bottom halves
+    right, each summed owner first.  fp32 and int32.  Returns the (P, n)
+    state after `steps` steps (default P): the sum computed at step s sits at
+    the top half of chunk (d+s+1) mod P and the bottom half of chunk
+    (d-s-1) mod P of row d; after all P steps chunk d of row d is the sum
+    over ranks."""
+    x = np.ascontiguousarray(x)
+    P = x.shape[0]
+    n = x[0].size
+    steps = P if steps is None else steps
+    out = np.empty_like(x)
+    lib = _load()
+    if x.dtype == np.float32:
+        rc = lib.oracle_reduce_scatter_bidir_f32(_ptr(x), _ptr(out), P, n, steps)
+    elif x.dtype == np.int32:
+        rc = lib.oracle_reduce_scatter_bidir_i32(_ptr(x), _ptr(out), P, n, steps)
+    else:
+        raise TypeError("reduce_scatter_bidir: fp32 or int32 (bf16: reduce_scatter_bidir_bf16)")
+    _check(rc, "reduce_scatter_bidir")
     return out
 
 
@@ -191,6 +224,19 @@ def reduce_scatter_bf16(x: np.ndarray, rounds: int | None = None):
     carry = np.empty(x.shape, dtype=np.float32)
     _check(_load().oracle_reduce_scatter_bf16(_ptr(x), _ptr(dst), _ptr(carry), P,
                                               x[0].size, rounds), "reduce_scatter_bf16")
+    return dst, carry
+
+
+def reduce_scatter_bidir_bf16(x: np.ndarray, steps: int | None = None):
+    """bf16 bidirectional reduce-scatter with fp32 partial sums and one
+    rounding of the complete block; returns (dst, carry)."""
+    x = _ranks(x, np.uint16)
+    P = x.shape[0]
+    steps = P if steps is None else steps
+    dst = np.empty_like(x)
+    carry = np.empty(x.shape, dtype=np.float32)
+    _check(_load().oracle_reduce_scatter_bidir_bf16(_ptr(x), _ptr(dst), _ptr(carry), P,
+                                                    x[0].size, steps), "reduce_scatter_bidir_bf16")
     return dst, carry
 
 

@@ -287,6 +287,173 @@ int oracle_all_reduce_bf16(const uint16_t *src, uint16_t *dst, float *carry,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Bidirectional reduce-scatter ("Pallas TPU Distributed Collectives 复习文档" */
+/* section 4, lax.psum_scatter, and its P = 4 walk-through in 4.6).          */
+/*                                                                          */
+/* Every chunk (the page's "block") is split into a top half, which travels  */
+/* to the LEFT neighbour, and a bottom half, which travels to the RIGHT one. */
+/* Device d first hands the halves of its own block d to its neighbours.    */
+/* At step s = 0 .. P-2 it takes the top half it received from its right    */
+/* neighbour, adds its own contribution to block (d + s + 1) mod P, and     */
+/* passes the sum on to the left; likewise the bottom half received from    */
+/* the left neighbour gets its contribution to block (d - s - 1) mod P and  */
+/* goes on to the right.  At the last step (s = P - 1) the halves that      */
+/* arrive belong to block d and are complete: they are kept, nothing more   */
+/* is added.  So the top half of block b is summed owner first,             */
+/*     ((x_b + x_{b-1}) + x_{b-2}) + ... + x_{b+1},                         */
+/* and the bottom half ((x_b + x_{b+1}) + x_{b+2}) + ... + x_{b-1}.          */
+/*                                                                          */
+/* Reading for the split of a chunk of C elements (the page's blocks have   */
+/* an even number of rows): the top half is the first C - C/2 elements.     */
+/*                                                                          */
+/* `state` (P*n, rank-major) starts as a copy of src.  The sum a device     */
+/* computes at step s is stored at the half it belongs to: the top half of  */
+/* chunk (d + s + 1) mod P and the bottom half of chunk (d - s - 1) mod P   */
+/* of device d's buffer; the last step stores the complete block d in chunk */
+/* d.  `steps` (0 .. P) lets tests stop early and look at the state.        */
+/* ------------------------------------------------------------------------ */
+static size_t bidir_top_len(size_t C) { return C - C / 2; }
+static int mod_p(int x, int P) { return ((x % P) + P) % P; }
+
+int oracle_reduce_scatter_bidir_f32(const float *src, float *state, int P, size_t n,
+                                    int steps)
+{
+    if (check_args(P, n) || steps < 0 || steps > P) return -1;
+    const size_t C = n / (size_t)P, h = bidir_top_len(C), hb = C - h;
+    memmove(state, src, sizeof(float) * (size_t)P * n);
+    /* the half each device passes on next: top to the left, bottom to the right */
+    float *top = (float *)malloc(sizeof(float) * (h ? h : 1) * (size_t)P);
+    float *bot = (float *)malloc(sizeof(float) * (hb ? hb : 1) * (size_t)P);
+    float *ntop = (float *)malloc(sizeof(float) * (h ? h : 1) * (size_t)P);
+    float *nbot = (float *)malloc(sizeof(float) * (hb ? hb : 1) * (size_t)P);
+    if (!top || !bot || !ntop || !nbot) { free(top); free(bot); free(ntop); free(nbot); return -1; }
+    for (int d = 0; d < P; ++d) {
+        const float *own = src + (size_t)d * n + (size_t)d * C;
+        memcpy(top + (size_t)d * h, own, sizeof(float) * h);
+        memcpy(bot + (size_t)d * hb, own + h, sizeof(float) * hb);
+    }
+    for (int s = 0; s < steps; ++s) {
+        const int last = (s == P - 1);
+        for (int d = 0; d < P; ++d) {
+            const float *from_right = top + (size_t)mod_p(d + 1, P) * h;
+            const float *from_left = bot + (size_t)mod_p(d - 1, P) * hb;
+            const float *xt = src + (size_t)d * n + (size_t)mod_p(d + s + 1, P) * C;
+            const float *xb = src + (size_t)d * n + (size_t)mod_p(d - s - 1, P) * C + h;
+            for (size_t i = 0; i < h; ++i)
+                ntop[(size_t)d * h + i] = last ? from_right[i] : from_right[i] + xt[i];
+            for (size_t i = 0; i < hb; ++i)
+                nbot[(size_t)d * hb + i] = last ? from_left[i] : from_left[i] + xb[i];
+        }
+        for (int d = 0; d < P; ++d) {
+            const int ct = last ? d : mod_p(d + s + 1, P);
+            const int cb = last ? d : mod_p(d - s - 1, P);
+            memcpy(state + (size_t)d * n + (size_t)ct * C, ntop + (size_t)d * h, sizeof(float) * h);
+            memcpy(state + (size_t)d * n + (size_t)cb * C + h, nbot + (size_t)d * hb, sizeof(float) * hb);
+        }
+        float *t = top; top = ntop; ntop = t;
+        t = bot; bot = nbot; nbot = t;
+    }
+    free(top); free(bot); free(ntop); free(nbot);
+    return 0;
+}
+
+/* The same schedule on int32; additions wrap modulo 2^32. */
+int oracle_reduce_scatter_bidir_i32(const int32_t *src, int32_t *state, int P, size_t n,
+                                    int steps)
+{
+    if (check_args(P, n) || steps < 0 || steps > P) return -1;
+    const size_t C = n / (size_t)P, h = bidir_top_len(C), hb = C - h;
+    memmove(state, src, sizeof(int32_t) * (size_t)P * n);
+    uint32_t *top = (uint32_t *)malloc(sizeof(uint32_t) * (h ? h : 1) * (size_t)P);
+    uint32_t *bot = (uint32_t *)malloc(sizeof(uint32_t) * (hb ? hb : 1) * (size_t)P);
+    uint32_t *ntop = (uint32_t *)malloc(sizeof(uint32_t) * (h ? h : 1) * (size_t)P);
+    uint32_t *nbot = (uint32_t *)malloc(sizeof(uint32_t) * (hb ? hb : 1) * (size_t)P);
+    if (!top || !bot || !ntop || !nbot) { free(top); free(bot); free(ntop); free(nbot); return -1; }
+    for (int d = 0; d < P; ++d) {
+        const int32_t *own = src + (size_t)d * n + (size_t)d * C;
+        memcpy(top + (size_t)d * h, own, sizeof(int32_t) * h);
+        memcpy(bot + (size_t)d * hb, own + h, sizeof(int32_t) * hb);
+    }
+    for (int s = 0; s < steps; ++s) {
+        const int last = (s == P - 1);
+        for (int d = 0; d < P; ++d) {
+            const uint32_t *from_right = top + (size_t)mod_p(d + 1, P) * h;
+            const uint32_t *from_left = bot + (size_t)mod_p(d - 1, P) * hb;
+            const int32_t *xt = src + (size_t)d * n + (size_t)mod_p(d + s + 1, P) * C;
+            const int32_t *xb = src + (size_t)d * n + (size_t)mod_p(d - s - 1, P) * C + h;
+            for (size_t i = 0; i < h; ++i)
+                ntop[(size_t)d * h + i] = last ? from_right[i] : from_right[i] + (uint32_t)xt[i];
+            for (size_t i = 0; i < hb; ++i)
+                nbot[(size_t)d * hb + i] = last ? from_left[i] : from_left[i] + (uint32_t)xb[i];
+        }
+        for (int d = 0; d < P; ++d) {
+            const int ct = last ? d : mod_p(d + s + 1, P);
+            const int cb = last ? d : mod_p(d - s - 1, P);
+            memcpy(state + (size_t)d * n + (size_t)ct * C, ntop + (size_t)d * h, sizeof(int32_t) * h);
+            memcpy(state + (size_t)d * n + (size_t)cb * C + h, nbot + (size_t)d * hb, sizeof(int32_t) * hb);
+        }
+        uint32_t *t = top; top = ntop; ntop = t;
+        t = bot; bot = nbot; nbot = t;
+    }
+    free(top); free(bot); free(ntop); free(nbot);
+    return 0;
+}
+
+/*
+ * bf16 inputs with fp32 partial sums (the reading used for the one-way ring
+ * as well): the halves travel in fp32, `carry` (P*n) receives each step's
+ * sums at the same positions as `state` in the fp32 version, and only the
+ * complete block is rounded once to bf16, at the last step, into dst[d][d].
+ * dst starts as a copy of src.
+ */
+int oracle_reduce_scatter_bidir_bf16(const uint16_t *src, uint16_t *dst, float *carry,
+                                     int P, size_t n, int steps)
+{
+    if (check_args(P, n) || steps < 0 || steps > P) return -1;
+    const size_t C = n / (size_t)P, h = bidir_top_len(C), hb = C - h;
+    memmove(dst, src, sizeof(uint16_t) * (size_t)P * n);
+    for (size_t i = 0; i < (size_t)P * n; ++i) carry[i] = bf16_to_f32(src[i]);
+    float *top = (float *)malloc(sizeof(float) * (h ? h : 1) * (size_t)P);
+    float *bot = (float *)malloc(sizeof(float) * (hb ? hb : 1) * (size_t)P);
+    float *ntop = (float *)malloc(sizeof(float) * (h ? h : 1) * (size_t)P);
+    float *nbot = (float *)malloc(sizeof(float) * (hb ? hb : 1) * (size_t)P);
+    if (!top || !bot || !ntop || !nbot) { free(top); free(bot); free(ntop); free(nbot); return -1; }
+    for (int d = 0; d < P; ++d) {
+        const uint16_t *own = src + (size_t)d * n + (size_t)d * C;
+        for (size_t i = 0; i < h; ++i) top[(size_t)d * h + i] = bf16_to_f32(own[i]);
+        for (size_t i = 0; i < hb; ++i) bot[(size_t)d * hb + i] = bf16_to_f32(own[h + i]);
+    }
+    for (int s = 0; s < steps; ++s) {
+        const int last = (s == P - 1);
+        for (int d = 0; d < P; ++d) {
+            const float *from_right = top + (size_t)mod_p(d + 1, P) * h;
+            const float *from_left = bot + (size_t)mod_p(d - 1, P) * hb;
+            const uint16_t *xt = src + (size_t)d * n + (size_t)mod_p(d + s + 1, P) * C;
+            const uint16_t *xb = src + (size_t)d * n + (size_t)mod_p(d - s - 1, P) * C + h;
+            for (size_t i = 0; i < h; ++i)
+                ntop[(size_t)d * h + i] = last ? from_right[i] : from_right[i] + bf16_to_f32(xt[i]);
+            for (size_t i = 0; i < hb; ++i)
+                nbot[(size_t)d * hb + i] = last ? from_left[i] : from_left[i] + bf16_to_f32(xb[i]);
+        }
+        for (int d = 0; d < P; ++d) {
+            const int ct = last ? d : mod_p(d + s + 1, P);
+            const int cb = last ? d : mod_p(d - s - 1, P);
+            memcpy(carry + (size_t)d * n + (size_t)ct * C, ntop + (size_t)d * h, sizeof(float) * h);
+            memcpy(carry + (size_t)d * n + (size_t)cb * C + h, nbot + (size_t)d * hb, sizeof(float) * hb);
+            if (last) {
+                uint16_t *o = dst + (size_t)d * n + (size_t)d * C;
+                for (size_t i = 0; i < h; ++i) o[i] = oracle_bf16_from_f32(ntop[(size_t)d * h + i]);
+                for (size_t i = 0; i < hb; ++i) o[h + i] = oracle_bf16_from_f32(nbot[(size_t)d * hb + i]);
+            }
+        }
+        float *t = top; top = ntop; ntop = t;
+        t = bot; bot = nbot; nbot = t;
+    }
+    free(top); free(bot); free(ntop); free(nbot);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Plain definitions used as references for tolerance checks.               */
 /* Sum over ranks in rank order 0..P-1, in fp64, and the sum of magnitudes  */
 /* (the denominator of the componentwise error bound of recursive sums).    */

@@ -10,6 +10,7 @@ import subprocess
 import pytest
 
 import oracle
+import test_oracle_bidir_pins as bidir
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ring_oracle.c")
@@ -34,6 +35,20 @@ MUTANTS = {
     "all-gather places pieces at the wrong chunk":
         ("memcpy((uint8_t *)state + (size_t)r * nb + (size_t)r * Cb,",
          "memcpy((uint8_t *)state + (size_t)r * nb + (size_t)((r + 1) % P) * Cb,"),
+    "bidir top half pulled from the left":
+        ("const float *from_right = top + (size_t)mod_p(d + 1, P) * h;",
+         "const float *from_right = top + (size_t)mod_p(d - 1, P) * h;"),
+    "bidir block index off by one":
+        ("const float *xt = src + (size_t)d * n + (size_t)mod_p(d + s + 1, P) * C;",
+         "const float *xt = src + (size_t)d * n + (size_t)mod_p(d + s, P) * C;"),
+    "bidir last step adds again":
+        ("ntop[(size_t)d * h + i] = last ? from_right[i] : from_right[i] + xt[i];",
+         "ntop[(size_t)d * h + i] = from_right[i] + xt[i];"),
+    "bidir halves split at the wrong place": ("static size_t bidir_top_len(size_t C) { return C - C / 2; }",
+                                              "static size_t bidir_top_len(size_t C) { return C / 2 + 1; }"),
+    "bidir bf16 rounds every step":
+        ("ntop[(size_t)d * h + i] = last ? from_right[i] : from_right[i] + bf16_to_f32(xt[i]);",
+         "ntop[(size_t)d * h + i] = last ? from_right[i] : bf16_to_f32(oracle_bf16_from_f32(from_right[i] + bf16_to_f32(xt[i])));"),
     "magnitude sum without abs": ("            m += fabs(x);\n        }\n        sum[i] = a;\n        if (abssum) abssum[i] = m;\n    }\n    return 0;\n}\n\nint oracle_rank_sum_f64_bf16",
                                   "            m += x;\n        }\n        sum[i] = a;\n        if (abssum) abssum[i] = m;\n    }\n    return 0;\n}\n\nint oracle_rank_sum_f64_bf16"),
 }
@@ -60,6 +75,13 @@ def _checks():
     yield "rank sum", lambda: pins.test_rank_sum_f64_matches_numpy(3)
     yield "bf16 carry", pins.test_bf16_carry_is_fp32_until_owner
     yield "bf16 bound", lambda: pins.test_bf16_all_reduce_one_rounding_bound(4)
+    yield "bidir page trace", bidir.test_bidir_matches_page_trace_in_fp32_order
+    for P in (2, 3, 4):
+        yield "bidir psum_scatter P=%d" % P, lambda P=P: bidir.test_bidir_is_psum_scatter_int32(P)
+        yield "bidir contributors P=%d" % P, lambda P=P: bidir.test_bidir_contributor_sets(P)
+    yield "bidir odd chunks", lambda: bidir.test_bidir_odd_chunks(3, 5)
+    yield "bidir p1 p2", bidir.test_bidir_p1_identity_and_p2
+    yield "bidir bf16", lambda: bidir.test_bidir_bf16_one_rounding(4)
 
 
 def _load_variant(tmp_path, text, name):
@@ -76,7 +98,9 @@ def _run_checks_with(lib, monkeypatch):
     for fname in ("oracle_ppermute", "oracle_reduce_scatter_f32", "oracle_reduce_scatter_i32",
                   "oracle_all_gather", "oracle_all_gather_place", "oracle_all_reduce_f32",
                   "oracle_all_reduce_i32", "oracle_reduce_scatter_bf16", "oracle_all_reduce_bf16",
-                  "oracle_bf16_from_f32_array", "oracle_rank_sum_f64_f32", "oracle_rank_sum_f64_bf16"):
+                  "oracle_bf16_from_f32_array", "oracle_rank_sum_f64_f32", "oracle_rank_sum_f64_bf16",
+                  "oracle_reduce_scatter_bidir_f32", "oracle_reduce_scatter_bidir_i32",
+                  "oracle_reduce_scatter_bidir_bf16"):
         f, g = getattr(lib, fname), getattr(real, fname)
         f.argtypes, f.restype = g.argtypes, g.restype
     monkeypatch.setattr(oracle, "_lib", lib)
