@@ -5,7 +5,9 @@
 A step is one ring all-reduce (the reduce-scatter rounds and the all-gather
 rounds, 2(P-1) rounds in one launch) over P virtual ranks whose buffers all
 sit in this GPU's HBM; inputs are resident before the timed region starts.
-Prints one JSON line.
+Prints one JSON line.  Other workloads (--workload) time one call of another
+collective of the same path: the bf16 all-reduce, the one-way and the
+bidirectional reduce-scatter, ppermute, and the fused GEMM + reduce-scatter.
 
 Default workload (the headline): P = 8 ranks, 64 Mi fp32 per rank (256 MiB
 per rank, 2 GiB in all), normal(0, 1), seed 2, out of place.
@@ -38,6 +40,11 @@ WORKLOADS = {
                             std=1.0 / 64, n=4096 * 4096),
     # a plain copy of known size (2 x 256 MiB read + written): counter calibration
     "ppermute_f32_p2_64Mi": dict(op="ppermute", P=2, n=64 << 20, kind="f32", seed=2, std=1.0),
+    # reduce-scatter alone on the headline inputs: one-way ring, and the
+    # bidirectional form (top halves of the chunks travel left, bottom right)
+    "rs_f32_p8_64Mi": dict(op="reduce_scatter", P=8, n=64 << 20, kind="f32", seed=2, std=1.0),
+    "rs_bidir_f32_p8_64Mi": dict(op="reduce_scatter_bidir", P=8, n=64 << 20, kind="f32", seed=2,
+                                 std=1.0),
 }
 DEFAULT = "ar_f32_p8_64Mi"
 
@@ -49,6 +56,13 @@ def moved_bytes(op: str, P: int, n: int, kind: str) -> int:
         return 2 * P * n * (2 if kind == "bf16" else 4)
     if P == 1:
         return 0
+    if op == "reduce_scatter_bidir":
+        # P-1 steps that add (as the one-way reduce-scatter rounds), then one
+        # that moves the complete halves of every rank's own chunk
+        if kind == "bf16":
+            rs = C * P * sum(2 + (2 if s == 0 else 4) + 4 for s in range(P - 1))
+            return rs + C * P * (4 + 2)
+        return (P - 1) * 12 * C * P + 8 * C * P
     if kind == "bf16":
         # carry in fp32: round 0 reads two bf16 and writes fp32; middle rounds
         # read bf16 + fp32 and write fp32; the owner's last round writes bf16.
@@ -70,7 +84,7 @@ def moved_bytes(op: str, P: int, n: int, kind: str) -> int:
 
 
 KERNEL_SOURCE = {"ring_step_kernel": "ring_kernels.hip", "copy_kernel_tab": "ring_kernels.hip",
-                 "gemm_rs_kernel": "gemm_rs.hip"}
+                 "ring_bidir_kernel": "ring_kernels.hip", "gemm_rs_kernel": "gemm_rs.hip"}
 
 
 KERNEL_HEADERS = ("ring_device.h", "ring_internal.h")
@@ -137,10 +151,15 @@ def _cpu_baseline(w, x):
     import oracle
     P, n = x.shape
     t0 = time.perf_counter()
-    if w["kind"] == "bf16":
-        want = oracle.all_reduce_bf16(x)
-    elif w["op"] == "ppermute":
+    if w["op"] == "ppermute":
         want = oracle.ppermute(x)
+    elif w["op"] == "reduce_scatter":
+        want = oracle.reduce_scatter_bf16(x)[0] if w["kind"] == "bf16" else oracle.reduce_scatter(x)
+    elif w["op"] == "reduce_scatter_bidir":
+        want = (oracle.reduce_scatter_bidir_bf16(x)[0] if w["kind"] == "bf16"
+                else oracle.reduce_scatter_bidir(x))
+    elif w["kind"] == "bf16":
+        want = oracle.all_reduce_bf16(x)
     else:
         want = oracle.all_reduce(x)
     dt = time.perf_counter() - t0
@@ -253,16 +272,19 @@ def main():
     torch.cuda.set_device(0)
     src = _to_dev(x, kind)
     dst = [torch.empty_like(t) for t in src]
-    ws = rc.workspace(N.OP_ALL_REDUCE, P, n, src[0].dtype)
+    op = w["op"]
+    ws_op = {"reduce_scatter": N.OP_REDUCE_SCATTER, "reduce_scatter_bidir": N.OP_REDUCE_SCATTER_BIDIR}
+    ws = rc.workspace(ws_op.get(op, N.OP_ALL_REDUCE), P, n, src[0].dtype)
     stream = torch.cuda.current_stream()
-    if w["op"] == "ppermute":
-        def step():
-            rc.ppermute(src, dst)
-        kernel = "copy_kernel_tab"
-    else:
-        def step():
-            rc.all_reduce(src, dst, ws=ws)
-        kernel = "ring_step_kernel"
+    call = {"ppermute": lambda: rc.ppermute(src, dst),
+            "all_reduce": lambda: rc.all_reduce(src, dst, ws=ws),
+            "reduce_scatter": lambda: rc.reduce_scatter(src, dst, ws=ws),
+            "reduce_scatter_bidir": lambda: rc.reduce_scatter_bidir(src, dst, ws=ws)}[op]
+
+    def step():
+        call()
+    kernel = {"ppermute": "copy_kernel_tab", "reduce_scatter_bidir": "ring_bidir_kernel"}.get(
+        op, "ring_step_kernel")
 
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -270,7 +292,7 @@ def main():
     torch.cuda.synchronize()
     code, info = rc.last_error(ws)
     if code != 0:
-        raise SystemExit("ring_all_reduce reported %s (info %#x)" % (N.strerror(code), info))
+        raise SystemExit("ring %s reported %s (info %#x)" % (op, N.strerror(code), info))
 
     # timed region: K steps, one launch each; events on the launch stream
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -285,7 +307,7 @@ def main():
     t1 = time.perf_counter()
     code, info = rc.last_error(ws)
     if code != 0:
-        raise SystemExit("ring_all_reduce reported %s (info %#x)" % (N.strerror(code), info))
+        raise SystemExit("ring %s reported %s (info %#x)" % (op, N.strerror(code), info))
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_step = (t1 - t0) * 1e3 / args.steps
     avg_kern_ms = sum(kern_ms) / len(kern_ms)
@@ -306,6 +328,12 @@ def main():
         else:
             got = np.stack([t.cpu().numpy() for t in dst]).view(np.uint32)
             want = want.view(np.uint32)
+        if op == "reduce_scatter":
+            # the one-way reduce-scatter leaves chunk (r - 1) mod P of rank r unwritten
+            C = n // P
+            for r in range(P):
+                c = (r - 1) % P
+                got[r, c * C:(c + 1) * C] = want[r, c * C:(c + 1) * C]
         parity = bool(np.array_equal(got, want))
         print("[bench] GPU output bit-exact vs oracle: %s" % parity, file=sys.stderr, flush=True)
 

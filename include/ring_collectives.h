@@ -57,7 +57,8 @@ typedef enum {
     RING_OP_REDUCE_SCATTER = 1,
     RING_OP_ALL_GATHER = 2,
     RING_OP_ALL_REDUCE = 3,
-    RING_OP_GEMM_REDUCE_SCATTER = 4
+    RING_OP_GEMM_REDUCE_SCATTER = 4,
+    RING_OP_REDUCE_SCATTER_BIDIR = 5
 } ring_op_t;
 
 enum {
@@ -112,6 +113,29 @@ int ring_ppermute(const void *const *src, void *const *dst, int P, size_t n,
  */
 int ring_reduce_scatter(const void *const *src, void *const *dst, int P, size_t n,
                         int dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Bidirectional ring reduce-scatter, P steps ("Pallas TPU Distributed
+ * Collectives 复习文档", section 4, lax.psum_scatter, and its walk-through in
+ * 4.6).  Every chunk is split into a top half (its first C - C/2 elements),
+ * which travels to the left neighbour, and a bottom half, which travels to
+ * the right one, so both directions of every ring link carry half the data.
+ * At step s = 0..P-2 rank r takes the top half of chunk (r + s + 1) mod P
+ * from its right neighbour (that neighbour's input at s = 0, otherwise the
+ * partial sum it stored at step s-1) and adds its own input; likewise the
+ * bottom half of chunk (r - s - 1) mod P from its left neighbour.  At step
+ * P-1 the halves of chunk r arrive complete and are stored unchanged.
+ *
+ * On return chunk r of dst[r] holds the sum over all ranks of chunk r, as for
+ * ring_reduce_scatter; the other chunks of dst[r] hold partial sums
+ * (unspecified).  fp32 order, owner first: top half of chunk c is
+ * ((x_c + x_{c-1}) + ...) + x_{c+1}, bottom half ((x_c + x_{c+1}) + ...) +
+ * x_{c-1}, indices mod P.  bf16: partial sums travel in fp32 through the
+ * workspace and the complete half is rounded once to bf16.  In place is
+ * allowed as for ring_reduce_scatter.  Workspace: RING_OP_REDUCE_SCATTER_BIDIR.
+ */
+int ring_reduce_scatter_bidir(const void *const *src, void *const *dst, int P, size_t n,
+                              int dtype, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Ring all-gather, P-1 rounds ("全归约 3", Walkthrough, second phase; the

@@ -90,6 +90,13 @@ def reduce_scatter(src, dst, ws=None, stream=None):
                   src, dst, ws, stream)
 
 
+def reduce_scatter_bidir(src, dst, ws=None, stream=None):
+    """Bidirectional ring reduce-scatter (top halves of the chunks travel
+    left, bottom halves right): chunk r of dst[r] <- sum over ranks."""
+    return _rs_ar(N.lib().ring_reduce_scatter_bidir, "ring_reduce_scatter_bidir",
+                  N.OP_REDUCE_SCATTER_BIDIR, src, dst, ws, stream)
+
+
 def all_reduce(src, dst, ws=None, stream=None):
     """Ring all-reduce: every dst[r] <- sum over ranks of src."""
     return _rs_ar(N.lib().ring_all_reduce, "ring_all_reduce", N.OP_ALL_REDUCE,

@@ -29,7 +29,9 @@ RingWs ring_ws_layout(int P, size_t n, int dtype) {
     RingWs w;
     const size_t C = n / (size_t)P;
     const size_t tile_min = (size_t)kWave * kMinTileVecs * elems_per_vec(dtype);
-    const size_t T = (C + tile_min - 1) / tile_min;
+    // + 1: the bidirectional reduce-scatter tiles each half of a chunk
+    // separately, which can take one tile more than the whole chunk
+    const size_t T = (C + tile_min - 1) / tile_min + 1;
     const size_t rows = P > 1 ? 2 * (size_t)(P - 1) : 1;
     w.flags_off = kStatusBytes;
     w.flags_bytes = align_up(rows * (size_t)P * (T ? T : 1) * kFlagStride * sizeof(int), 256);
@@ -137,12 +139,14 @@ static int overlap_kind(const void* const* src, size_t src_bytes, void* const* d
 
 static hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
-// Launch the chunk-step kernel over global rounds [k_begin, k_end).
+// Launch the chunk-step kernel over global rounds [k_begin, k_end) (the
+// bidirectional kernel over its rounds 0 .. P-1 when bidir is set).
 static int run_ring(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream, int k_begin, int k_end,
-                    int compact_src) {
+                    int compact_src, int bidir = 0) {
     const RingWs lay = ring_ws_layout(P, n, dtype);
-    const bool need_carry = dtype == RING_BF16 && k_begin < P - 1;   // reduce-scatter rounds
+    // reduce-scatter rounds of bf16 data carry fp32 partial sums
+    const bool need_carry = dtype == RING_BF16 && (bidir || k_begin < P - 1);
     if (!ws || ((uintptr_t)ws & 255)) return RING_EWORKSPACE;
     if (ws_bytes < (need_carry ? lay.total : lay.total - lay.carry_bytes)) return RING_EWORKSPACE;
     const ring_tuning_t tu = tuning();
@@ -150,11 +154,13 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
     const int esz = elem_bytes(dtype);
     const long long C = (long long)(n / (size_t)P);
     const int tile = kWave * tu.tile_vecs * elems_per_vec(dtype);
-    const int T = (int)((C + tile - 1) / tile);
+    const long long h = C - C / 2;   // top half of a chunk (bidirectional)
+    const int T_top = bidir ? (int)((h + tile - 1) / tile) : 0;
+    const int T = bidir ? T_top + (int)((C - h + tile - 1) / tile) : (int)((C + tile - 1) / tile);
 
     RingParams prm;
     memset(&prm, 0, sizeof prm);
-    int vec_ok = ((C * esz) % 16) == 0;
+    int vec_ok = ((C * esz) % 16) == 0 && (!bidir || ((h * esz) % 16) == 0);
     for (int r = 0; r < P; ++r) {
         prm.src[r] = src ? src[r] : nullptr;
         prm.dst[r] = dst[r];
@@ -174,10 +180,13 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
     prm.k_end = k_end;
     prm.vec_ok = vec_ok;
     prm.compact_src = compact_src;
+    prm.bidir = bidir;
+    prm.T_top = T_top;
+    prm.h = h;
 
     // Grid: every wave must be resident at once (waves wait on each other).
     // Stay within half the occupancy limit: margin for anything else resident.
-    int occ = ring_blocks_per_cu(dtype, tu.tile_vecs);
+    int occ = ring_blocks_per_cu(dtype, tu.tile_vecs, bidir);
     if (occ < 1) return RING_EHIP;
     int bpc = (tu.waves_per_cu + kWavesPerBlock - 1) / kWavesPerBlock;
     if (bpc > occ / 2) bpc = occ / 2 > 0 ? occ / 2 : 1;
@@ -235,6 +244,9 @@ size_t ring_workspace_bytes(int op, int P, size_t n, int dtype) {
         case RING_OP_ALL_REDUCE:
             if (!elem_bytes(dtype) || n % (size_t)P) return 0;
             return ring_ws_layout(P, n, dtype).total;
+        case RING_OP_REDUCE_SCATTER_BIDIR:
+            if (!elem_bytes(dtype) || n % (size_t)P) return 0;
+            return ring_ws_layout(P, n, dtype).total;
         case RING_OP_ALL_GATHER: {
             if (!elem_bytes(dtype) || n % (size_t)P) return 0;
             RingWs w = ring_ws_layout(P, n, dtype);
@@ -264,8 +276,10 @@ int ring_ppermute(const void* const* src, void* const* dst, int P, size_t n, int
     return launch_copy(src, dst, P, bytes, 1, as_stream(stream)) == hipSuccess ? RING_OK : RING_EHIP;
 }
 
+enum { KIND_RS, KIND_AR, KIND_RS_BIDIR };
+
 static int rs_or_ar(const void* const* src, void* const* dst, int P, size_t n, int dtype,
-                    void* ws, size_t ws_bytes, void* stream, bool all_reduce) {
+                    void* ws, size_t ws_bytes, void* stream, int kind) {
     int rc = check_common(src, P, n, dtype, true);
     if (rc) return rc;
     if ((rc = check_common(dst, P, n, dtype, true))) return rc;
@@ -277,18 +291,25 @@ static int rs_or_ar(const void* const* src, void* const* dst, int P, size_t n, i
         if (ov == 1) return RING_OK;
         return launch_copy(src, dst, 1, bytes, 0, as_stream(stream)) == hipSuccess ? RING_OK : RING_EHIP;
     }
+    if (kind == KIND_RS_BIDIR)   // P steps: P-1 that add, one that takes the complete halves
+        return run_ring(src, dst, P, n, dtype, ws, ws_bytes, stream, 0, P, 0, 1);
     return run_ring(src, dst, P, n, dtype, ws, ws_bytes, stream, 0,
-                    all_reduce ? 2 * (P - 1) : P - 1, 0);
+                    kind == KIND_AR ? 2 * (P - 1) : P - 1, 0);
 }
 
 int ring_reduce_scatter(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                         void* ws, size_t ws_bytes, void* stream) {
-    return rs_or_ar(src, dst, P, n, dtype, ws, ws_bytes, stream, false);
+    return rs_or_ar(src, dst, P, n, dtype, ws, ws_bytes, stream, KIND_RS);
+}
+
+int ring_reduce_scatter_bidir(const void* const* src, void* const* dst, int P, size_t n, int dtype,
+                              void* ws, size_t ws_bytes, void* stream) {
+    return rs_or_ar(src, dst, P, n, dtype, ws, ws_bytes, stream, KIND_RS_BIDIR);
 }
 
 int ring_all_reduce(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream) {
-    return rs_or_ar(src, dst, P, n, dtype, ws, ws_bytes, stream, true);
+    return rs_or_ar(src, dst, P, n, dtype, ws, ws_bytes, stream, KIND_AR);
 }
 
 int ring_all_gather(const void* const* src_or_null, void* const* dst, int P, size_t n, int dtype,

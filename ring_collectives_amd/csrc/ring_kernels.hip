@@ -5,6 +5,8 @@
 //   * ring_step_kernel  : the persistent chunk-step kernel that runs the ring
 //                         reduce-scatter and all-gather rounds for every
 //                         virtual rank at once.
+//   * ring_bidir_kernel : the bidirectional reduce-scatter (halves of every
+//                         chunk travel both ways round the ring).
 //   * fill_zero_kernel  : workspace initialisation.
 //
 // Ring schedule ("全归约 3：Ring——每步大小恒定", Walkthrough).  P ranks, chunk
@@ -121,29 +123,28 @@ __device__ __forceinline__ TilePos tile_pos(const RingParams& p, int c, int j) {
     return t;
 }
 
-// One reduce-scatter round of one tile, fp32 / int32:
-//   dst[r][c] = src[r][c] + (s == 0 ? src[left][c] : dst[left][c])
+// One reduce-scatter round of tile t (position j) of one rank, fp32 / int32:
+//   dst[r][t] = src[r][t] + (first ? src[from][t] : dst[from][t])
+// after waiting for flag (k, from, j): rank `from` finished the tile.
 template <int DT, int U>
-__device__ bool rs_tile(const RingParams& p, int r, int left, int k, int j, int lane, bool wait) {
-    const int s = k;
-    const int c = rs_chunk(r, s, p.P);
-    const TilePos t = tile_pos(p, c, j);
+__device__ bool rs_tile_at(const RingParams& p, int r, int from, int k, int j, const TilePos& t,
+                           bool first, int lane, bool wait) {
     const long long nb = t.len * 4;
     const rsrc_t own = tile_view((const char*)p.src[r] + t.e0 * 4, nb);
-    const rsrc_t rcv = tile_view((const char*)(s == 0 ? p.src[left] : p.dst[left]) + t.e0 * 4, nb);
+    const rsrc_t rcv = tile_view((const char*)(first ? p.src[from] : p.dst[from]) + t.e0 * 4, nb);
     const rsrc_t out = tile_view((char*)p.dst[r] + t.e0 * 4, nb);
-    const int seen = wait ? peek_flag(p, k, left, j) : 1;
+    const int seen = wait ? peek_flag(p, k, from, j) : 1;
     if (p.vec_ok) {
         u32x4 a[U], b[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) a[i] = ld16<POL_PLAIN>(own, (unsigned)(lane + i * kWave) * 16u);
-        if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
+        if (wait && !wait_flag(p, k, from, r, j, lane, seen)) return false;
 #pragma unroll
         for (int i = 0; i < U; ++i) b[i] = ld16<POL_DEV>(rcv, (unsigned)(lane + i * kWave) * 16u);
 #pragma unroll
         for (int i = 0; i < U; ++i) st16<POL_DEV>(add4<DT>(a[i], b[i]), out, (unsigned)(lane + i * kWave) * 16u);
     } else {
-        if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
+        if (wait && !wait_flag(p, k, from, r, j, lane, seen)) return false;
         for (long long i = lane; i < t.len; i += kWave) {
             const unsigned o = (unsigned)i * 4u;
             st4<POL_DEV>(add1<DT>(ld4<POL_PLAIN>(own, o), ld4<POL_DEV>(rcv, o)), out, o);
@@ -152,33 +153,39 @@ __device__ bool rs_tile(const RingParams& p, int r, int left, int k, int j, int 
     return true;
 }
 
-// One reduce-scatter round of one tile, bf16 inputs with the fp32 carry:
-//   round 0      : carry[r][c] = f32(src[r][c]) + f32(src[left][c])
-//   middle rounds: carry[r][c] = f32(src[r][c]) + carry[left][c]
-//   last (owner) : dst[r][r]   = bf16(f32(src[r][r]) + carry[left][r])
+// One round of the one-way ring: chunk c = (r - s - 2) mod P from the left.
+template <int DT, int U>
+__device__ __forceinline__ bool rs_tile(const RingParams& p, int r, int left, int k, int j, int lane,
+                                        bool wait) {
+    const TilePos t = tile_pos(p, rs_chunk(r, k, p.P), j);
+    return rs_tile_at<DT, U>(p, r, left, k, j, t, k == 0, lane, wait);
+}
+
+// One reduce-scatter round of tile t (position j), bf16 inputs with the fp32
+// carry, from rank `from`:
+//   first  : carry[r][t] = f32(src[r][t]) + f32(src[from][t])
+//   middle : carry[r][t] = f32(src[r][t]) + carry[from][t]
+//   last   : dst[r][t]   = bf16(f32(src[r][t]) + carry[from][t])
 template <int U>
-__device__ bool rs_tile_bf16(const RingParams& p, int r, int left, int k, int j, int lane, bool wait) {
-    const int s = k;
-    const int c = rs_chunk(r, s, p.P);
-    const bool last = (s == p.P - 2);
-    const TilePos t = tile_pos(p, c, j);
+__device__ bool rs_tile_bf16_at(const RingParams& p, int r, int from, int k, int j, const TilePos& t,
+                                bool first, bool last, int lane, bool wait) {
     const rsrc_t own = tile_view((const unsigned short*)p.src[r] + t.e0, t.len * 2);
-    const rsrc_t rcv16 = tile_view((const unsigned short*)p.src[left] + t.e0, t.len * 2);
-    const rsrc_t rcv32 = tile_view(p.carry + (size_t)left * p.n + t.e0, t.len * 4);
+    const rsrc_t rcv16 = tile_view((const unsigned short*)p.src[from] + t.e0, t.len * 2);
+    const rsrc_t rcv32 = tile_view(p.carry + (size_t)from * p.n + t.e0, t.len * 4);
     const rsrc_t out32 = tile_view(p.carry + (size_t)r * p.n + t.e0, t.len * 4);
     const rsrc_t out16 = tile_view((unsigned short*)p.dst[r] + t.e0, t.len * 2);
-    const int seen = wait ? peek_flag(p, k, left, j) : 1;
+    const int seen = wait ? peek_flag(p, k, from, j) : 1;
     if (p.vec_ok) {
         // lane vector v = 4 elements: 8 bytes of bf16, 16 bytes of fp32 carry
         u32x2 a[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) a[i] = ld8<POL_PLAIN>(own, (unsigned)(lane + i * kWave) * 8u);
-        if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
+        if (wait && !wait_flag(p, k, from, r, j, lane, seen)) return false;
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const unsigned v = (unsigned)(lane + i * kWave);
             float x[4];
-            if (s == 0) {
+            if (first) {
                 const u32x2 b = ld8<POL_DEV>(rcv16, v * 8u);
                 x[0] = bf16_lo(b[0]); x[1] = bf16_hi(b[0]); x[2] = bf16_lo(b[1]); x[3] = bf16_hi(b[1]);
             } else {
@@ -203,10 +210,10 @@ __device__ bool rs_tile_bf16(const RingParams& p, int r, int left, int k, int j,
             }
         }
     } else {
-        if (wait && !wait_flag(p, k, left, r, j, lane, seen)) return false;
+        if (wait && !wait_flag(p, k, from, r, j, lane, seen)) return false;
         for (long long i = lane; i < t.len; i += kWave) {
             const unsigned o2 = (unsigned)i * 2u, o4 = (unsigned)i * 4u;
-            const float recv = (s == 0) ? __uint_as_float((unsigned)ld2<POL_DEV>(rcv16, o2) << 16)
+            const float recv = first ? __uint_as_float((unsigned)ld2<POL_DEV>(rcv16, o2) << 16)
                                         : __uint_as_float(ld4<POL_DEV>(rcv32, o4));
             const float x = __uint_as_float((unsigned)ld2<POL_PLAIN>(own, o2) << 16) + recv;
             if (last) st2<POL_DEV>((unsigned short)bf16_rne(x), out16, o2);
@@ -214,6 +221,13 @@ __device__ bool rs_tile_bf16(const RingParams& p, int r, int left, int k, int j,
         }
     }
     return true;
+}
+
+template <int U>
+__device__ __forceinline__ bool rs_tile_bf16(const RingParams& p, int r, int left, int k, int j, int lane,
+                                             bool wait) {
+    const TilePos t = tile_pos(p, rs_chunk(r, k, p.P), j);
+    return rs_tile_bf16_at<U>(p, r, left, k, j, t, k == 0, k == p.P - 2, lane, wait);
 }
 
 // Copy one tile (len elements of ESZ bytes) from `from` to `to`; the store
@@ -321,6 +335,103 @@ __global__ __launch_bounds__(kBlock) void ring_step_kernel(RingParams p) {
     }
 }
 
+// ---------------------------------------------------------------- bidirectional reduce-scatter
+// ("Pallas TPU Distributed Collectives 复习文档", section 4.)  The top half of
+// every chunk (its first h elements) travels left, the bottom half right.
+// Tile positions j < T_top cover the top half and are pulled from the right
+// neighbour; the others cover the bottom half and are pulled from the left.
+// Round k = 0 .. P-2 adds this rank's contribution to chunk (r + k + 1) mod P
+// (top) or (r - k - 1) mod P (bottom); round P-1 stores the complete half of
+// chunk r that arrives.  A wave waits only for the same position of round
+// k-1 on the rank it pulls from, which that rank's wave of the same index
+// handles earlier in its own order, so the ring groups progress exactly as
+// the one-way kernel's do.
+struct BidirPos {
+    int from;      // the rank this tile is pulled from
+    TilePos t;
+};
+__device__ __forceinline__ BidirPos bidir_pos(const RingParams& p, int r, int k, int j) {
+    BidirPos b;
+    long long lo, hi;
+    int jj, c;
+    if (j < p.T_top) {
+        b.from = (r + 1) % p.P;
+        c = (r + k + 1) % p.P;
+        lo = 0;
+        hi = p.h;
+        jj = j;
+    } else {
+        b.from = (r - 1 + p.P) % p.P;
+        c = ((r - k - 1) % p.P + p.P) % p.P;
+        lo = p.h;
+        hi = p.C;
+        jj = j - p.T_top;
+    }
+    b.t.off = lo + (long long)jj * p.tile;
+    b.t.e0 = (long long)c * p.C + b.t.off;
+    b.t.len = (hi - b.t.off) < p.tile ? (hi - b.t.off) : p.tile;
+    return b;
+}
+
+// Last round: the half of chunk r that rank `from` completed in round P-2
+// becomes this rank's result (bf16: rounded once from the fp32 carry).
+template <int DT, int U>
+__device__ bool bidir_final_tile(const RingParams& p, int r, int from, int k, int j, const TilePos& t,
+                                 int lane, bool wait) {
+    const int seen = wait ? peek_flag(p, k, from, j) : 1;
+    if (wait && !wait_flag(p, k, from, r, j, lane, seen)) return false;
+    if constexpr (DT == DT_BF16) {
+        const rsrc_t rcv32 = tile_view(p.carry + (size_t)from * p.n + t.e0, t.len * 4);
+        const rsrc_t out16 = tile_view((unsigned short*)p.dst[r] + t.e0, t.len * 2);
+        if (p.vec_ok) {
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const unsigned v = (unsigned)(lane + i * kWave);
+                const u32x4 b = ld16<POL_DEV>(rcv32, v * 16u);
+                u32x2 o;
+                o[0] = pack_bf16(__uint_as_float(b[0]), __uint_as_float(b[1]));
+                o[1] = pack_bf16(__uint_as_float(b[2]), __uint_as_float(b[3]));
+                st8<POL_PLAIN>(o, out16, v * 8u);
+            }
+        } else {
+            for (long long i = lane; i < t.len; i += kWave)
+                st2<POL_PLAIN>((unsigned short)bf16_rne(__uint_as_float(ld4<POL_DEV>(rcv32, (unsigned)i * 4u))),
+                               out16, (unsigned)i * 2u);
+        }
+    } else {
+        const long long nb = t.len * 4;
+        copy_tile<U, 4, POL_DEV>(tile_view((char*)p.dst[r] + t.e0 * 4, nb),
+                                 tile_view((const char*)p.dst[from] + t.e0 * 4, nb), t.len, p.vec_ok,
+                                 false, lane);
+    }
+    return true;
+}
+
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void ring_bidir_kernel(RingParams p) {
+    int r, w;
+    if (!map_wave(p, r, w)) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int j = w; j < p.T; j += p.waves_per_rank) {
+        for (int k = p.k_begin; k < p.k_end; ++k) {
+            const bool wait = (k > p.k_begin);
+            const BidirPos b = bidir_pos(p, r, k, j);
+            bool ok;
+            if (k < p.P - 1) {
+                if constexpr (DT == DT_BF16)
+                    ok = rs_tile_bf16_at<U>(p, r, b.from, k, j, b.t, k == 0, false, lane, wait);
+                else
+                    ok = rs_tile_at<DT, U>(p, r, b.from, k, j, b.t, k == 0, lane, wait);
+            } else {
+                ok = bidir_final_tile<DT, U>(p, r, b.from, k, j, b.t, lane, wait);
+            }
+            if (!ok) return;
+            if (k + 1 < p.k_end && !(r == 0 && k + 1 == p.drop_round))
+                signal_flag(p, k + 1, r, j, lane);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- copy / fill
 __global__ __launch_bounds__(kBlock) void fill_zero_kernel(unsigned* p, long long words, long long tail_bytes) {
     const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -394,7 +505,10 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 
 template <int DT, int U>
 static hipError_t launch_ring_t(RingParams& prm, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((ring_step_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
+    if (prm.bidir)
+        hipLaunchKernelGGL((ring_bidir_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
+    else
+        hipLaunchKernelGGL((ring_step_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
     return hipGetLastError();
 }
 
@@ -408,23 +522,30 @@ static hipError_t launch_ring_dt(RingParams& prm, int tile_vecs, int grid, hipSt
     }
 }
 
-template <int DT>
-static int blocks_per_cu_dt(int tile_vecs) {
+template <int DT, int U>
+static int blocks_per_cu_t(int bidir) {
     int nb = 0;
-    hipError_t e = hipErrorInvalidValue;
-    switch (tile_vecs) {
-        case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_step_kernel<DT, 4>, kBlock, 0); break;
-        case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_step_kernel<DT, 8>, kBlock, 0); break;
-        case 16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_step_kernel<DT, 16>, kBlock, 0); break;
-    }
+    const hipError_t e =
+        bidir ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_bidir_kernel<DT, U>, kBlock, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_step_kernel<DT, U>, kBlock, 0);
     return e == hipSuccess ? nb : 0;
 }
 
-int ring_blocks_per_cu(int dtype, int tile_vecs) {
+template <int DT>
+static int blocks_per_cu_dt(int tile_vecs, int bidir) {
+    switch (tile_vecs) {
+        case 4: return blocks_per_cu_t<DT, 4>(bidir);
+        case 8: return blocks_per_cu_t<DT, 8>(bidir);
+        case 16: return blocks_per_cu_t<DT, 16>(bidir);
+        default: return 0;
+    }
+}
+
+int ring_blocks_per_cu(int dtype, int tile_vecs, int bidir) {
     switch (dtype) {
-        case RING_F32: return blocks_per_cu_dt<DT_F32>(tile_vecs);
-        case RING_I32: return blocks_per_cu_dt<DT_I32>(tile_vecs);
-        case RING_BF16: return blocks_per_cu_dt<DT_BF16>(tile_vecs);
+        case RING_F32: return blocks_per_cu_dt<DT_F32>(tile_vecs, bidir);
+        case RING_I32: return blocks_per_cu_dt<DT_I32>(tile_vecs, bidir);
+        case RING_BF16: return blocks_per_cu_dt<DT_BF16>(tile_vecs, bidir);
         default: return 0;
     }
 }

@@ -35,7 +35,7 @@ def test_library_loads():
 def test_every_declared_symbol_is_exported():
     decl = _declared_functions()
     assert {"ring_ppermute", "ring_reduce_scatter", "ring_all_gather", "ring_all_reduce",
-            "gemm_reduce_scatter"} <= decl
+            "gemm_reduce_scatter", "ring_reduce_scatter_bidir"} <= decl
     out = subprocess.check_output(["nm", "-D", "--defined-only", N.LIB_PATH], text=True)
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     missing = sorted(decl - exported)
@@ -88,6 +88,23 @@ def _call_rs(P, n, dtype=N.RING_F32, src=None, dst=None, ws=0x100000, ws_bytes=1
 def test_bad_rank_count(P):
     a, ka = _fake([0x1000] * 70)
     assert N.lib().ring_reduce_scatter(a, a, P, 64, N.RING_F32, 0x100000, 1 << 30, None) == N.RING_EINVAL
+
+
+def test_bidir_argument_checks():
+    L = N.lib()
+    a, ka = _fake([0x10000000 + r * 0x1000000 for r in range(4)])
+    b, kb = _fake([0x50000000 + r * 0x1000000 for r in range(4)])
+    assert L.ring_reduce_scatter_bidir(a, b, 4, 4097, N.RING_F32, 0x100000, 1 << 30, None) == N.RING_EINVAL
+    assert L.ring_reduce_scatter_bidir(a, b, 4, 4096, 7, 0x100000, 1 << 30, None) == N.RING_EUNSUPPORTED
+    assert L.ring_reduce_scatter_bidir(a, b, 0, 4096, N.RING_F32, 0x100000, 1 << 30, None) == N.RING_EINVAL
+    assert L.ring_reduce_scatter_bidir(a, b, 4, 0, N.RING_F32, 0x100000, 1 << 30, None) == N.RING_OK
+    # too small a workspace is rejected before any launch
+    assert L.ring_reduce_scatter_bidir(a, b, 4, 4096, N.RING_F32, 0x100000, 256, None) == N.RING_EWORKSPACE
+    w = L.ring_workspace_bytes(N.OP_REDUCE_SCATTER_BIDIR, 4, 4096, N.RING_F32)
+    assert w >= L.ring_workspace_bytes(N.OP_REDUCE_SCATTER, 4, 4096, N.RING_F32) > 0
+    assert L.ring_workspace_bytes(N.OP_REDUCE_SCATTER_BIDIR, 4, 4097, N.RING_F32) == 0
+    wb = L.ring_workspace_bytes(N.OP_REDUCE_SCATTER_BIDIR, 4, 4096, N.RING_BF16)
+    assert wb >= 4 * 4096 * 4     # the fp32 partial sums
 
 
 def test_indivisible_size():
