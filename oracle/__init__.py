@@ -302,6 +302,33 @@ def gemm_reduce_scatter(A: np.ndarray, B: np.ndarray) -> np.ndarray:
     return np.stack([st[r].reshape(M, N)[r * rows:(r + 1) * rows] for r in range(P)])
 
 
+def all_gather_gemm(A_shards: np.ndarray, B: np.ndarray):
+    """All-gather then matmul ("TPU 与分布式通信原语", collective matmul: the
+    all-gather-matmul kernel gathers the row blocks of x around the ring,
+    then multiplies by the local weight).  A_shards: (P, M/P, K) bf16 bits,
+    rank q's row block of A; B: (P, K, N) bf16 bits.  Returns (A_full, C):
+    A_full (P, M, K) is every rank's gathered A -- the ring all-gather of the
+    row blocks (chunk c = rows [c M/P, (c+1) M/P)) -- and C (P, M, N) fp32 is
+    A_full[q] @ B[q] (fp64 product, one rounding)."""
+    A_shards = _ranks(A_shards, np.uint16)
+    B = _ranks(B, np.uint16)
+    P, Mc, K = A_shards.shape
+    full = all_gather_pieces(A_shards.reshape(P, Mc * K)).reshape(P, P * Mc, K)
+    return full, gemm_products_f32(full, B)
+
+
+def all_gather_gemm_rows_f64(A_shards: np.ndarray, B: np.ndarray, q: int, rows) -> tuple:
+    """Sampled reference for all_gather_gemm: rows `rows` of A_full @ B[q] in
+    fp64 and the magnitude denominator |A_full[rows]| @ |B[q]|, with A_full
+    the concatenation of the row blocks."""
+    A_shards = _ranks(A_shards, np.uint16)
+    P, Mc, K = A_shards.shape
+    rows = np.asarray(rows)
+    a = bf16_to_f32(A_shards.reshape(P * Mc, K)[rows]).astype(np.float64)
+    b = bf16_to_f32(_ranks(B, np.uint16)[q]).astype(np.float64)
+    return a @ b, np.abs(a) @ np.abs(b)
+
+
 def gemm_reduce_scatter_rows_f64(A: np.ndarray, B: np.ndarray, r: int, rows) -> tuple:
     """Sampled reference: for output rank r and local row indices `rows`,
     the fp64 value of sum_q A_q[i,:] @ B_q and the magnitude denominator

@@ -399,3 +399,53 @@ def test_chunk_major_roundtrip():
     np.testing.assert_array_equal(inputs.from_chunk_major(flat, 4, 8), x)
     # chunk c is column block c
     np.testing.assert_array_equal(flat[2, 128 * 8:2 * 128 * 8].reshape(8, 128), x[2, :, 128:256])
+
+
+# ---------------------------------------------------------------- all-gather + GEMM
+@pytest.mark.parametrize("P", [1, 2, 3, 4])
+def test_all_gather_gemm_gathers_the_row_blocks(P):
+    """Every rank's gathered A is the concatenation of the row blocks in rank
+    order (the all-gather's meaning, Pallas page section 2)."""
+    rng = np.random.default_rng(15 + P)
+    A = inputs.small_int_bf16(rng, (P, 8, 24))
+    B = inputs.small_int_bf16(rng, (P, 24, 16))
+    full, _ = oracle.all_gather_gemm(A, B)
+    want = A.reshape(P * 8, 24)
+    for q in range(P):
+        np.testing.assert_array_equal(full[q], want)
+
+
+@pytest.mark.parametrize("P", [1, 2, 4])
+def test_all_gather_gemm_integer_valued_exact(P):
+    """Integer-valued bf16 operands: C_q = concat(A) @ B_q exactly (int64)."""
+    rng = np.random.default_rng(16 + P)
+    A = inputs.small_int_bf16(rng, (P, 16, 64))
+    B = inputs.small_int_bf16(rng, (P, 64, 40))
+    _, C = oracle.all_gather_gemm(A, B)
+    a = oracle.bf16_to_f32(A.reshape(P * 16, 64)).astype(np.int64)
+    for q in range(P):
+        np.testing.assert_array_equal(C[q].astype(np.int64), a @ oracle.bf16_to_f32(B[q]).astype(np.int64))
+
+
+def test_all_gather_gemm_identity_b_returns_a():
+    """B_q = I: C_q is the gathered A, widened exactly to fp32."""
+    P, K = 4, 32
+    rng = np.random.default_rng(17)
+    A = inputs.bf16_bits(rng.standard_normal((P, 8, K)).astype(np.float32))
+    eye = inputs.bf16_bits(np.eye(K, dtype=np.float32))
+    _, C = oracle.all_gather_gemm(A, np.stack([eye] * P))
+    for q in range(P):
+        np.testing.assert_array_equal(C[q], oracle.bf16_to_f32(A.reshape(P * 8, K)))
+
+
+def test_all_gather_gemm_sampled_rows_reference():
+    P = 2
+    rng = np.random.default_rng(18)
+    A = inputs.bf16_bits(rng.standard_normal((P, 16, 48)).astype(np.float32))
+    B = inputs.bf16_bits(rng.standard_normal((P, 48, 24)).astype(np.float32))
+    _, C = oracle.all_gather_gemm(A, B)
+    rows = np.array([0, 5, 17, 31])
+    for q in range(P):
+        ref, mag = oracle.all_gather_gemm_rows_f64(A, B, q, rows)
+        assert np.all(np.abs(C[q][rows] - ref) <= 2.0 ** -24 * np.abs(ref) + 1e-30)
+        assert np.all(mag >= np.abs(ref))
