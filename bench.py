@@ -38,6 +38,10 @@ WORKLOADS = {
     # fused GEMM + reduce-scatter: P = 4, A_q, B_q bf16 4096 x 4096, normal(0, 1/64)
     "gemm_rs_p4_4096": dict(op="gemm_rs", P=4, M=4096, N=4096, K=4096, kind="bf16", seed=4,
                             std=1.0 / 64, n=4096 * 4096),
+    # fused all-gather + GEMM: P = 4, A 4096 x 4096 in row blocks of 1024,
+    # B_q bf16 4096 x 4096, normal(0, 1/64)
+    "ag_gemm_p4_4096": dict(op="ag_gemm", P=4, M=4096, N=4096, K=4096, kind="bf16", seed=5,
+                            std=1.0 / 64, n=4096 * 4096),
     # a plain copy of known size (2 x 256 MiB read + written): counter calibration
     "ppermute_f32_p2_64Mi": dict(op="ppermute", P=2, n=64 << 20, kind="f32", seed=2, std=1.0),
     # reduce-scatter alone on the headline inputs: one-way ring, and the
@@ -83,8 +87,10 @@ def moved_bytes(op: str, P: int, n: int, kind: str) -> int:
     return rs + ag
 
 
-KERNEL_SOURCE = {"ring_step_kernel": "ring_kernels.hip", "copy_kernel_tab": "ring_kernels.hip",
-                 "ring_bidir_kernel": "ring_kernels.hip", "gemm_rs_kernel": "gemm_rs.hip"}
+KERNEL_SOURCE = {"ring_step_kernel": ("ring_kernels.hip",), "copy_kernel_tab": ("ring_kernels.hip",),
+                 "ring_bidir_kernel": ("ring_kernels.hip",),
+                 "gemm_rs_kernel": ("gemm_rs.hip", "gemm_core.h"),
+                 "ag_gemm_kernel": ("ag_gemm.hip", "gemm_core.h")}
 
 
 KERNEL_HEADERS = ("ring_device.h", "ring_internal.h")
@@ -93,7 +99,7 @@ KERNEL_HEADERS = ("ring_device.h", "ring_internal.h")
 def _sha_source(kernel: str) -> str:
     """Hash of the kernel's source file and the device headers it includes."""
     h = hashlib.sha256()
-    for name in (KERNEL_SOURCE[kernel],) + KERNEL_HEADERS:
+    for name in KERNEL_SOURCE[kernel] + KERNEL_HEADERS:
         with open(os.path.join(ROOT, "ring_collectives_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -124,6 +130,9 @@ def _make_inputs(w):
     from ring_collectives_amd import inputs
     if w["op"] == "gemm_rs":
         return inputs.gemm_operands(w["P"], w["M"], w["N"], w["K"], std=w["std"], seed=w["seed"])
+    if w["op"] == "ag_gemm":   # rank q's row block of A (M / P rows), and its B_q
+        return inputs.gemm_operands(w["P"], w["M"] // w["P"], w["N"], w["K"], std=w["std"],
+                                    seed=w["seed"])
     if w["kind"] == "f32" and w["std"] is None:
         return inputs.to_chunk_major(inputs.small_f32(w["P"], (8, 512)), w["P"])
     if w["kind"] == "f32":
@@ -170,36 +179,50 @@ def _cpu_baseline(w, x):
 
 
 def _gemm_main(args, w):
-    """GEMM + reduce-scatter: TFLOP/s against the bf16 MFMA peak."""
+    """Fused GEMM workloads (GEMM + reduce-scatter, all-gather + GEMM):
+    TFLOP/s against the bf16 MFMA peak."""
     import numpy as np
     import torch
     from ring_collectives_amd import _native as N
     from ring_collectives_amd import collectives as rc
     P, M, Nn, K = w["P"], w["M"], w["N"], w["K"]
+    op = w["op"]
     print("[bench] workload %s: generating inputs" % args.workload, file=sys.stderr, flush=True)
     A, B = _make_inputs(w)
     torch.cuda.set_device(0)
     a = [torch.from_numpy(A[q].view(np.int16)).cuda().view(torch.bfloat16) for q in range(P)]
     b = [torch.from_numpy(B[q].view(np.int16)).cuda().view(torch.bfloat16) for q in range(P)]
-    out = [torch.empty((M // P, Nn), dtype=torch.float32, device="cuda") for _ in range(P)]
-    nb = N.lib().ring_workspace_bytes(N.OP_GEMM_REDUCE_SCATTER, P, M * Nn, N.RING_F32)
-    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    if op == "gemm_rs":
+        out = [torch.empty((M // P, Nn), dtype=torch.float32, device="cuda") for _ in range(P)]
+        ws = rc.workspace(N.OP_GEMM_REDUCE_SCATTER, P, M * Nn, torch.float32)
+
+        def step():
+            rc.gemm_reduce_scatter(a, b, out, ws=ws)
+        kernel, what = "gemm_rs_kernel", "GEMM + ring reduce-scatter"
+    else:
+        full = [torch.empty((M, K), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+        out = [torch.empty((M, Nn), dtype=torch.float32, device="cuda") for _ in range(P)]
+        ws = rc.workspace(N.OP_ALL_GATHER_GEMM, P, M * Nn, torch.float32)
+
+        def step():
+            rc.all_gather_gemm(a, b, full, out, ws=ws)
+        kernel, what = "ag_gemm_kernel", "ring all-gather + GEMM"
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        rc.gemm_reduce_scatter(a, b, out, ws=ws)
+        step()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        rc.gemm_reduce_scatter(a, b, out, ws=ws)
+        step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     code, info = rc.last_error(ws)
     if code != 0:
-        raise SystemExit("gemm_reduce_scatter reported %s (info %#x)" % (N.strerror(code), info))
+        raise SystemExit("%s reported %s (info %#x)" % (what, N.strerror(code), info))
     kern_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
     ms_step = (t1 - t0) * 1e3 / args.steps
     avg = sum(kern_ms) / len(kern_ms)
@@ -210,24 +233,40 @@ def _gemm_main(args, w):
     parity = None
     if not args.no_cpu:
         import oracle
-        rows = np.arange(0, M // P, (M // P) // 16)          # 16 sampled rows per rank
         t = time.perf_counter()
         worst = 0.0
-        for r in range(P):
-            ref, mag = oracle.gemm_reduce_scatter_rows_f64(A, B, r, rows)
-            got = out[r].cpu().numpy()[rows].astype(np.float64)
-            worst = max(worst, float((np.abs(got - ref) / mag).max()))
+        if op == "gemm_rs":
+            rows = np.arange(0, M // P, (M // P) // 16)          # 16 sampled rows per rank
+            for r in range(P):
+                ref, mag = oracle.gemm_reduce_scatter_rows_f64(A, B, r, rows)
+                got = out[r].cpu().numpy()[rows].astype(np.float64)
+                worst = max(worst, float((np.abs(got - ref) / mag).max()))
+            sflop = 2.0 * P * P * len(rows) * Nn * K
+            bound = (K + P) * 2.0 ** -24
+            sample = "%d output rows per rank (fp64 rows of sum_q A_q B_q, NumPy BLAS)" % len(rows)
+            same = True
+        else:
+            rows = np.arange(0, M, M // 16)                     # 16 sampled rows per rank
+            for r in range(P):
+                ref, mag = oracle.all_gather_gemm_rows_f64(A, B, r, rows)
+                got = out[r].cpu().numpy()[rows].astype(np.float64)
+                worst = max(worst, float((np.abs(got - ref) / mag).max()))
+            sflop = 2.0 * P * len(rows) * Nn * K
+            bound = K * 2.0 ** -24
+            sample = "%d output rows per rank (fp64 rows of A_full @ B_q, NumPy BLAS)" % len(rows)
+            gathered = A.reshape(M, K)
+            same = all(np.array_equal(t_.view(torch.int16).cpu().numpy().view(np.uint16), gathered)
+                       for t_ in full)
         dt = time.perf_counter() - t
-        sflop = 2.0 * P * P * len(rows) * Nn * K
         cpu = {"value": round(sflop / dt / 1e12, 6), "unit": "TFLOP/s",
                "cores": len(os.sched_getaffinity(0)), "kind": "oracle", "seconds": round(dt, 3),
-               "sample": "%d output rows per rank (fp64 rows of sum_q A_q B_q, NumPy BLAS)" % len(rows)}
-        parity = worst <= (K + P) * 2.0 ** -24
-        print("[bench] sampled rows max normalised error %.3e (bound %.3e)"
-              % (worst, (K + P) * 2.0 ** -24), file=sys.stderr, flush=True)
+               "sample": sample}
+        parity = bool(worst <= bound and same)
+        print("[bench] sampled rows max normalised error %.3e (bound %.3e)%s"
+              % (worst, bound, "" if op == "gemm_rs" else ", gathered A exact: %s" % same),
+              file=sys.stderr, flush=True)
     line = {
-        "metric": "GEMM + ring reduce-scatter TFLOP/s, P=%d virtual ranks, bf16 %dx%dx%d per rank"
-                  % (P, M, Nn, K),
+        "metric": "%s TFLOP/s, P=%d virtual ranks, bf16 %dx%dx%d per rank" % (what, P, M, Nn, K),
         "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -237,7 +276,7 @@ def _gemm_main(args, w):
         "roofline": {"bound": "mfma", "achieved": round(flop / (avg * 1e-3) / 1e12, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flop / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                     "traffic": _traffic(args.workload, "gemm_rs_kernel"), "kernel": "gemm_rs_kernel",
+                     "traffic": _traffic(args.workload, kernel), "kernel": kernel,
                      "kernel_ms_avg": round(avg, 5)},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
@@ -264,7 +303,7 @@ def main():
     from ring_collectives_amd import collectives as rc
 
     w = WORKLOADS[args.workload]
-    if w["op"] == "gemm_rs":
+    if w["op"] in ("gemm_rs", "ag_gemm"):
         return _gemm_main(args, w)
     P, n, kind = w["P"], w["n"], w["kind"]
     print("[bench] workload %s: generating inputs" % args.workload, file=sys.stderr, flush=True)

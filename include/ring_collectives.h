@@ -58,7 +58,8 @@ typedef enum {
     RING_OP_ALL_GATHER = 2,
     RING_OP_ALL_REDUCE = 3,
     RING_OP_GEMM_REDUCE_SCATTER = 4,
-    RING_OP_REDUCE_SCATTER_BIDIR = 5
+    RING_OP_REDUCE_SCATTER_BIDIR = 5,
+    RING_OP_ALL_GATHER_GEMM = 6
 } ring_op_t;
 
 enum {
@@ -72,8 +73,8 @@ enum {
 
 /*
  * Bytes of workspace a call needs.  op is a ring_op_t.  For
- * RING_OP_GEMM_REDUCE_SCATTER pass n = M * N (elements of one rank's product)
- * and dtype RING_F32.  Returns 0 for invalid arguments (and for ppermute,
+ * RING_OP_GEMM_REDUCE_SCATTER and RING_OP_ALL_GATHER_GEMM pass n = M * N
+ * (elements of one rank's product) and dtype RING_F32.  Returns 0 for invalid arguments (and for ppermute,
  * which needs none).
  */
 size_t ring_workspace_bytes(int op, int P, size_t n, int dtype);
@@ -182,6 +183,28 @@ int gemm_reduce_scatter(const void *const *A, const void *const *B, void *const 
                         void *stream);
 
 /*
+ * All-gather + GEMM with tile-level overlap ("Triton-distributed 语义",
+ * "AllGather + GEMM 重叠": GEMM tiles wait for the blocks they need and start
+ * as soon as they arrive, every rank starting on its local block; "TPU 与分布式
+ * 通信原语", collective matmul, all-gather-matmul, for the unfused meaning).
+ *
+ * A_shard[r]: bf16 (M / P) x K row-major, rank r's row block of A.
+ * B[r]: bf16 K x N row-major.  A_full[r]: bf16 M x K, written: on return it
+ * holds the ring all-gather of the row blocks (block c at rows
+ * [c M/P, (c+1) M/P)).  C[r]: fp32 M x N row-major, written: A_full @ B[r],
+ * accumulated in fp32 on the matrix cores.  The blocks travel the ring of
+ * ring_all_gather (rank r receives block (r - t - 1) mod P in round t); rank
+ * r's GEMM handles block r first, then the blocks in the order they arrive.
+ * A_full buffers must not overlap the shards or each other.  Every workgroup
+ * of the launch must be resident at once (the grid is sized for an otherwise
+ * idle GPU); a wait that outlives the watchdog ends in RING_ETIMEOUT.
+ * Shapes this version accepts: M % (256 P) == 0, N % 128 == 0, K % 64 == 0.
+ */
+int all_gather_gemm(const void *const *A_shard, const void *const *B, void *const *A_full,
+                    void *const *C, int P, int M, int N, int K, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/*
  * Synchronises `stream` and returns the error word a kernel left in `ws`
  * (RING_OK if none).  If info is not NULL it receives the stuck rank, round
  * and tile packed as rank | round << 8 | tile << 16 (tile saturates).
@@ -206,8 +229,9 @@ const char *ring_strerror(int code);
  *   stepwise       1: one launch per round, ordered by the stream instead of
  *                  flags (the "inject a barrier between steps" debugging aid
  *                  of "Triton-distributed 语义", best practice 8).
- *   drop_round     test hook: if >= 1, rank 0 never signals round drop_round,
- *                  so its right neighbour's wait must end in RING_ETIMEOUT.
+ *   drop_round     test hook: if >= 1, rank 0 never signals round drop_round
+ *                  (all_gather_gemm: never flags its slices of that phase),
+ *                  so the waits on it must end in RING_ETIMEOUT.
  *   gemm_tile_n    output tile width of gemm_reduce_scatter: 128 (two
  *                  4-wave workgroups per compute unit), 256 (one 8-wave
  *                  workgroup; needs N % 256 == 0), or 0 to choose per call:

@@ -146,6 +146,31 @@ def gemm_reduce_scatter(A, B, out, ws=None, stream=None):
     return ws
 
 
+def all_gather_gemm(A_shard, B, A_full, C, ws=None, stream=None):
+    """A_full[r] <- the row blocks A_shard[0..P-1] stacked (ring all-gather);
+    C[r] <- A_full[r] @ B[r] (bf16 in, fp32 out), overlapped tile by tile."""
+    P = len(A_shard)
+    Mc, K = A_shard[0].shape
+    K2, Nn = B[0].shape
+    M = Mc * P
+    if K2 != K or len(B) != P or len(A_full) != P or len(C) != P:
+        raise ValueError("all_gather_gemm: shape mismatch")
+    pa = _ranks(A_shard, "all_gather_gemm", Mc * K, torch.bfloat16)
+    pb = _ranks(B, "all_gather_gemm", K * Nn, torch.bfloat16)
+    pf = _ranks(A_full, "all_gather_gemm", M * K, torch.bfloat16)
+    pc = _ranks(C, "all_gather_gemm", M * Nn, torch.float32)
+    if ws is None:
+        nb = int(N.lib().ring_workspace_bytes(N.OP_ALL_GATHER_GEMM, P, M * Nn, N.RING_F32))
+        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=A_shard[0].device)
+    a, ka = N.ptr_array(pa)
+    b, kb = N.ptr_array(pb)
+    f, kf = N.ptr_array(pf)
+    c, kc = N.ptr_array(pc)
+    N.check(N.lib().all_gather_gemm(a, b, f, c, P, M, Nn, K, ws.data_ptr(), ws.numel(),
+                                    _stream(stream)), "all_gather_gemm")
+    return ws
+
+
 def last_error(ws: torch.Tensor, stream=None):
     """(code, info) left in a workspace by the last kernel (synchronises)."""
     import ctypes

@@ -1,0 +1,281 @@
+// ag_gemm.hip -- all-gather + GEMM with tile-level overlap.
+//
+// Rank q holds row block q of A (A_shard[q], M/P x K bf16) and its own B_q
+// (K x N bf16).  The ranks all-gather the row blocks around the ring into
+// A_full[q] (M x K; chunk c = rows [c M/P, (c+1) M/P)) and every rank computes
+// C_q = A_full @ B_q in fp32.  That is the all-gather-matmul of "TPU 与分布式
+// 通信原语" (collective matmul: gather the blocks of x, multiply by the local
+// weight), overlapped as the "AllGather + GEMM 重叠" pattern of
+// "Triton-distributed 语义": the GEMM tiles of a block start as soon as the
+// block has arrived, and every rank starts on its local block (the
+// threadblock swizzle of the same page, "线程块交织").
+//
+// Schedule.  Phase f = 0 .. P-1 handles chunk c = (q - f) mod P, the order in
+// which the ring delivers the blocks (round t of the ring all-gather brings
+// chunk (q - t - 1) mod P from the left neighbour), local block first:
+//   forwarding: at phase f >= 1 rank q copies chunk c from its left
+//     neighbour (from A_shard[left] at f = 1, the left rank's own block; from
+//     A_full[left] after) into A_full[q], slice by slice, each slice once the
+//     left neighbour has flagged it, and flags it in turn.  At f = 0 it
+//     places its own block.
+//   GEMM: the tiles of chunk c, each once every slice of its row panel is
+//     flagged (phase 0 reads the local block straight from A_shard[q]).
+// A slice is the part of a 256-row panel that one tile position forwards:
+// rows 256 t / tn .. 256 (t + 1) / tn of the panel for column tile t, all K
+// columns, so the tn workgroups of a panel forward it together.
+//
+// Progress.  Every workgroup forwards all its slices of a phase before it
+// waits for any slice of that phase, and forwarding waits only for the left
+// rank's previous phase; so by induction on the phase every slice gets
+// forwarded, provided all workgroups are resident (the grid is sized so).
+// The slice flags have several readers (the panel's GEMM tiles and the right
+// neighbour), so readers leave them set and the last workgroup to finish
+// clears the table for the next call.
+#include "gemm_core.h"
+
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+namespace ringc {
+
+struct AgGemmParams {
+    const unsigned short* As[RING_MAX_RANKS];   // rank q's block of A, (M / P) x K
+    const unsigned short* B[RING_MAX_RANKS];    // K x N
+    unsigned short* Af[RING_MAX_RANKS];         // gathered A, M x K
+    float* C[RING_MAX_RANKS];                   // M x N fp32
+    int* flags;                                 // [P phases][P ranks][tpc], kFlagStride apart
+    int* done;                                  // workgroups finished (clears the flags)
+    Status* status;
+    long long spin_limit;
+    int P, M, N, K;
+    int tm_chunk;                               // 256-row panels per chunk
+    int tn;                                     // column tiles (N / BN)
+    int tpc;                                    // tiles per chunk
+    int groups;                                 // workgroups per rank
+    int nflags;                                 // flags in the table
+    int drop_round;                             // test hook: rank 0 never flags this phase (0 = off)
+};
+
+constexpr size_t kDoneOffset = 64;   // the finish counter, inside the status block
+
+__device__ __forceinline__ int* ag_flag(const AgGemmParams& p, int f, int q, int pos) {
+    return p.flags + (((size_t)f * p.P + q) * p.tpc + pos) * kFlagStride;
+}
+
+// Rows [r0, r1) of chunk c's panel slice for tile position pos.
+__device__ __forceinline__ void slice_rows(const AgGemmParams& p, int pos, int& r0, int& r1) {
+    const int pr = pos / p.tn, t = pos % p.tn;
+    r0 = pr * kBM + (t * kBM) / p.tn;
+    r1 = pr * kBM + ((t + 1) * kBM) / p.tn;
+}
+
+// Copy rows [r0, r1) of a chunk (K bf16 each) with the whole workgroup.
+template <int LOAD_POL>
+__device__ __forceinline__ void copy_rows(const unsigned short* src, unsigned short* dst, int rows, int K,
+                                          int tid, int nthreads) {
+    const long long bytes = (long long)rows * K * 2;
+    const rsrc_t s = tile_view(src, bytes);
+    const rsrc_t d = tile_view(dst, bytes);
+    const long long nvec = bytes / 16;
+    for (long long i = tid; i < nvec; i += nthreads)
+        st16<POL_DEV>(ld16<LOAD_POL>(s, (unsigned)(i * 16)), d, (unsigned)(i * 16));
+}
+
+// One wave waits for flag f; the workgroup follows it.  Returns false (for
+// every wave) if the launch is being abandoned: a wave that gives up has
+// recorded the timeout in the error word before the barrier.
+__device__ __forceinline__ bool wg_wait(const AgGemmParams& p, int* f, int wave, int lane, int q, int phase,
+                                        int pos) {
+    if (wave == 0) {
+        const int seen = peek_flag(f);
+        wait_flag(f, p.status, p.spin_limit, q, phase, pos, lane, seen, false);
+    }
+    __syncthreads();
+    return __hip_atomic_load(&p.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
+}
+
+// All waves' stores are complete, then the flag is set once.
+__device__ __forceinline__ void wg_signal(int* f, int tid) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) __hip_atomic_fetch_add(f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class G>
+__device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
+    constexpr int BN = G::BN;
+    const int tid = threadIdx.x;
+    const int nthreads = 64 * G::NW;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave / G::WC, wc = wave % G::WC;
+    const int P = p.P;
+    const int q = blockIdx.x % P;
+    const int grp = blockIdx.x / P;
+    const int left = (q - 1 + P) % P;
+    const int Mc = p.M / P;
+
+    for (int f = 0; f < P; ++f) {
+        const int c = (q - f + P) % P;
+        // forward (or place) this workgroup's slices of chunk c
+        for (int pos = grp; pos < p.tpc; pos += p.groups) {
+            int r0, r1;
+            slice_rows(p, pos, r0, r1);
+            unsigned short* dst = p.Af[q] + ((size_t)c * Mc + r0) * p.K;
+            if (f == 0) {
+                copy_rows<POL_PLAIN>(p.As[q] + (size_t)r0 * p.K, dst, r1 - r0, p.K, tid, nthreads);
+                continue;   // nobody waits for the local block in A_full
+            }
+            if (f >= 2 && !wg_wait(p, ag_flag(p, f - 1, left, pos), wave, lane, q, f, pos))
+                return;
+            if (f == 1)   // the left rank's own block, straight from its input
+                copy_rows<POL_PLAIN>(p.As[left] + (size_t)r0 * p.K, dst, r1 - r0, p.K, tid, nthreads);
+            else
+                copy_rows<POL_DEV>(p.Af[left] + ((size_t)c * Mc + r0) * p.K, dst, r1 - r0, p.K, tid,
+                                   nthreads);
+            if (!(q == 0 && f == p.drop_round)) wg_signal(ag_flag(p, f, q, pos), tid);
+        }
+        // GEMM tiles of chunk c
+        for (int pos = grp; pos < p.tpc; pos += p.groups) {
+            const int pr = pos / p.tn, tc = pos % p.tn;
+            f32x16 acc[kMI][G::NI];
+            if (f == 0) {
+                gemm_tile<G, POL_PLAIN>(p.K, p.N, p.As[q], p.B[q], pr, tc, acc, lds, lane, wave, wr, wc);
+            } else {
+                for (int t = 0; t < p.tn; ++t)
+                    if (!wg_wait(p, ag_flag(p, f, q, pr * p.tn + t), wave, lane, q, f, pos)) return;
+                gemm_tile<G, POL_DEV>(p.K, p.N, p.Af[q], p.B[q], c * p.tm_chunk + pr, tc, acc, lds, lane,
+                                      wave, wr, wc);
+            }
+            float* ob = p.C[q] + ((size_t)c * Mc + pr * kBM + wr * kWM) * p.N + tc * BN + wc * G::WN;
+            store_part_rowmajor<G, false>(acc, tile_view(nullptr, 0), ob, p.N, lds, lane, wave);
+        }
+    }
+}
+
+template <class G>
+__global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void ag_gemm_kernel(AgGemmParams p) {
+    __shared__ __attribute__((aligned(16))) unsigned short lds[G::kLds / 2];
+    ag_gemm_body<G>(p, lds);
+    // The last workgroup to finish clears the slice flags for the next call
+    // (every reader is done by then; an abandoned launch gets here too).
+    // Wave 0 counts the workgroup out and, if it was the last, clears.
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        int prev = 0;
+        if (threadIdx.x == 0)
+            prev = __hip_atomic_fetch_add(p.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __builtin_amdgcn_readfirstlane(prev);
+        if (prev == (int)gridDim.x - 1) {
+            for (int i = threadIdx.x; i < p.nflags; i += 64)
+                __hip_atomic_store(p.flags + (size_t)i * kFlagStride, 0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            if (threadIdx.x == 0) __hip_atomic_store(p.done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- host side
+static size_t align256_ag(size_t x) { return (x + 255) / 256 * 256; }
+
+// Sized for 256 x 128 tiles, the narrowest used.
+struct AgWs {
+    size_t flags_off, flags_bytes, total;
+    int nflags;
+};
+
+static AgWs ag_ws_layout(int P, size_t MN) {
+    AgWs w;
+    const size_t tpc = MN / (size_t)P / ((size_t)kBM * 128);
+    w.nflags = (int)((size_t)P * P * (tpc ? tpc : 1));
+    w.flags_off = kStatusBytes;
+    w.flags_bytes = align256_ag((size_t)w.nflags * kFlagStride * sizeof(int));
+    w.total = w.flags_off + w.flags_bytes;
+    return w;
+}
+
+size_t ag_gemm_workspace_bytes(int P, size_t n) {
+    if (P < 1 || P > RING_MAX_RANKS || n == 0 || n % ((size_t)P * kBM * 128)) return 0;
+    return ag_ws_layout(P, n).total;
+}
+
+template <class G>
+static int launch_ag_gemm(AgGemmParams& prm, const DevInfo& di, hipStream_t stream) {
+    prm.tn = prm.N / G::BN;
+    prm.tpc = prm.tm_chunk * prm.tn;
+    // every workgroup must be resident (the panel's workgroups wait for each
+    // other's slices)
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ag_gemm_kernel<G>, 64 * G::NW, 0) != hipSuccess ||
+        occ < G::kWGsPerCU)
+        return RING_EHIP;
+    long long groups = (long long)di.cus * G::kWGsPerCU / prm.P;
+    if (groups > prm.tpc) groups = prm.tpc;
+    if (groups < 1) return RING_EUNSUPPORTED;
+    prm.groups = (int)groups;
+    hipLaunchKernelGGL(ag_gemm_kernel<G>, dim3((unsigned)(groups * prm.P)), dim3(64 * G::NW), 0, stream, prm);
+    return hipGetLastError() == hipSuccess ? RING_OK : RING_EHIP;
+}
+
+}  // namespace ringc
+
+using namespace ringc;
+
+static bool ag_overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+extern "C" int all_gather_gemm(const void* const* A_shard, const void* const* B, void* const* A_full,
+                               void* const* C, int P, int M, int N, int K, void* ws, size_t ws_bytes,
+                               void* stream) {
+    if (P < 1 || P > RING_MAX_RANKS || M < 0 || N < 0 || K < 0) return RING_EINVAL;
+    if (!A_shard || !B || !A_full || !C) return RING_EINVAL;
+    if (M == 0 || N == 0) return RING_OK;
+    if (M % (kBM * P) || N % 128 || K % 64 || K == 0) return RING_EUNSUPPORTED;
+    const size_t shard_bytes = (size_t)(M / P) * K * 2, full_bytes = (size_t)M * K * 2;
+    for (int r = 0; r < P; ++r) {
+        if (!A_shard[r] || !B[r] || !A_full[r] || !C[r]) return RING_EINVAL;
+        if (((uintptr_t)A_shard[r] | (uintptr_t)B[r] | (uintptr_t)A_full[r] | (uintptr_t)C[r]) & 15)
+            return RING_EINVAL;
+    }
+    // the gathered buffers are written while every shard and gathered buffer
+    // is being read: they must not overlap the inputs or each other
+    for (int a = 0; a < P; ++a)
+        for (int b = 0; b < P; ++b) {
+            if (ag_overlap(A_full[a], full_bytes, A_shard[b], shard_bytes)) return RING_EINVAL;
+            if (a != b && ag_overlap(A_full[a], full_bytes, A_full[b], full_bytes)) return RING_EINVAL;
+        }
+    const AgWs lay = ag_ws_layout(P, (size_t)M * N);
+    if (!ws || ((uintptr_t)ws & 255) || ws_bytes < lay.total) return RING_EWORKSPACE;
+
+    AgGemmParams prm;
+    memset(&prm, 0, sizeof prm);
+    for (int r = 0; r < P; ++r) {
+        prm.As[r] = (const unsigned short*)A_shard[r];
+        prm.B[r] = (const unsigned short*)B[r];
+        prm.Af[r] = (unsigned short*)A_full[r];
+        prm.C[r] = (float*)C[r];
+    }
+    prm.status = (Status*)ws;
+    prm.done = (int*)((char*)ws + kDoneOffset);
+    prm.flags = (int*)((char*)ws + lay.flags_off);
+    prm.nflags = lay.nflags;
+    const DevInfo di = dev_info();
+    const ring_tuning_t tu = tuning();
+    prm.spin_limit = (long long)(tu.timeout_s * (double)di.wall_khz * 1000.0);
+    prm.drop_round = tu.drop_round;
+    prm.P = P;
+    prm.M = M;
+    prm.N = N;
+    prm.K = K;
+    prm.tm_chunk = M / P / kBM;
+    int bn = tu.gemm_tile_n;
+    if (bn == 0) {
+        const long long wide_tiles = (long long)prm.tm_chunk * (N / 256);
+        bn = (N % 256 == 0 && wide_tiles >= (long long)(di.cus / P)) ? 256 : 128;
+    }
+    if (bn == 256 && N % 256) return RING_EUNSUPPORTED;
+    return bn == 256 ? launch_ag_gemm<Geo<256, 8>>(prm, di, (hipStream_t)stream)
+                     : launch_ag_gemm<Geo<128, 4>>(prm, di, (hipStream_t)stream);
+}

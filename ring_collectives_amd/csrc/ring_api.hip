@@ -254,6 +254,8 @@ size_t ring_workspace_bytes(int op, int P, size_t n, int dtype) {
         }
         case RING_OP_GEMM_REDUCE_SCATTER:
             return gemm_rs_workspace_bytes(P, n);
+        case RING_OP_ALL_GATHER_GEMM:
+            return ag_gemm_workspace_bytes(P, n);
         default: return 0;
     }
 }

@@ -91,14 +91,16 @@ __device__ __forceinline__ int peek_flag(const int* f) {
     return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Spin until flag f is set (unless `seen` already is), then clear it.
+// Spin until flag f is set (unless `seen` already is), then clear it (unless
+// `clear` is false: a flag with several readers is cleared by the kernel
+// that owns it once every reader is done).
 // Returns false if the launch is being abandoned (this wave timed out, or
 // another one did).  The loads of the neighbour's data that follow are
 // device-scope and are issued only after the flag was seen (control
 // dependency; the empty asm keeps the compiler from hoisting them).
 // (r, k, j) only label a timeout report.
 __device__ inline bool wait_flag(int* f, Status* st, long long spin_limit, int r, int k, int j,
-                                 int lane, int seen) {
+                                 int lane, int seen, bool clear = true) {
     if (seen < 1) {
         const long long t0 = wall_clock64();
         unsigned spins = 0;
@@ -116,7 +118,7 @@ __device__ inline bool wait_flag(int* f, Status* st, long long spin_limit, int r
     }
     asm volatile("" ::: "memory");
     // This wave is the flag's only reader in this launch: clear it for the next.
-    if (lane == 0) __hip_atomic_store(f, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (clear && lane == 0) __hip_atomic_store(f, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
 }
 

@@ -74,6 +74,7 @@ int ring_blocks_per_cu(int dtype, int tile_vecs, int bidir);   // occupancy of t
 
 // GEMM + reduce-scatter workspace size (n = M * N per rank).
 size_t gemm_rs_workspace_bytes(int P, size_t n);
+size_t ag_gemm_workspace_bytes(int P, size_t n);
 
 // Device properties cached per device.
 struct DevInfo {
