@@ -70,6 +70,9 @@ def _load():
             "oracle_reduce_scatter_bidir_f32": [vp, vp, i32, sz, i32],
             "oracle_reduce_scatter_bidir_i32": [vp, vp, i32, sz, i32],
             "oracle_reduce_scatter_bidir_bf16": [vp, vp, vp, i32, sz, i32],
+            "oracle_psum_circ_f32": [vp, vp, vp, i32, sz, i32],
+            "oracle_psum_circ_i32": [vp, vp, vp, i32, sz, i32],
+            "oracle_psum_circ_bf16": [vp, vp, i32, sz],
             "oracle_bf16_from_f32_array": [vp, vp, sz],
             "oracle_rank_sum_f64_f32": [vp, i32, sz, vp, vp],
             "oracle_rank_sum_f64_bf16": [vp, i32, sz, vp, vp],
@@ -160,6 +163,39 @@ def reduce_scatter_bidir(x: np.ndarray, steps: int | None = None) -> np.ndarray:
         raise TypeError("reduce_scatter_bidir: fp32 or int32 (bf16: reduce_scatter_bidir_bf16)")
     _check(rc, "reduce_scatter_bidir")
     return out
+
+
+def psum_circulating(x: np.ndarray, steps: int | None = None):
+    """Circulating-input psum ("Pallas TPU Distributed Collectives 复习文档"
+    section 3): every input travels once around the ring and each device adds
+    what arrives, x_{d-1} first and its own x_d last, into an accumulator
+    that starts at zero.  fp32 and int32.  Returns (acc, slots) after `steps`
+    steps (default P): acc (P, n), slots (P, 2, n) -- the two receive slots
+    of every device (the page's hbm_buf[0], hbm_buf[1]; 0 where never
+    written)."""
+    x = np.ascontiguousarray(x)
+    P, n = x.shape
+    steps = P if steps is None else steps
+    acc = np.empty_like(x)
+    slots = np.empty((P, 2, n), dtype=x.dtype)
+    lib = _load()
+    if x.dtype == np.float32:
+        rc = lib.oracle_psum_circ_f32(_ptr(x), _ptr(acc), _ptr(slots), P, n, steps)
+    elif x.dtype == np.int32:
+        rc = lib.oracle_psum_circ_i32(_ptr(x), _ptr(acc), _ptr(slots), P, n, steps)
+    else:
+        raise TypeError("psum_circulating: fp32 or int32 (bf16: psum_circulating_bf16)")
+    _check(rc, "psum_circulating")
+    return acc, slots
+
+
+def psum_circulating_bf16(x: np.ndarray) -> np.ndarray:
+    """bf16 circulating psum: fp32 accumulator, one rounding per device."""
+    x = _ranks(x, np.uint16)
+    P, n = x.shape
+    dst = np.empty_like(x)
+    _check(_load().oracle_psum_circ_bf16(_ptr(x), _ptr(dst), P, n), "psum_circulating_bf16")
+    return dst
 
 
 def all_gather(state: np.ndarray, rounds: int | None = None) -> np.ndarray:

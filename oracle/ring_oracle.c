@@ -454,6 +454,91 @@ int oracle_reduce_scatter_bidir_bf16(const uint16_t *src, uint16_t *dst, float *
 }
 
 /* ------------------------------------------------------------------------ */
+/* Circulating-input psum ("Pallas TPU Distributed Collectives 复习文档",     */
+/* section 3, lax.psum, and its walk-through table in 3.5).                 */
+/*                                                                          */
+/* Every device's whole input travels once around the ring to the right.   */
+/* Each device has two receive slots (the page's hbm_buf[0] / hbm_buf[1])   */
+/* and an accumulator that starts at zero.  First every device sends its    */
+/* input into slot 0 of its right neighbour.  At step s = 0 .. P-1 a device */
+/* adds what is in its slot s % 2 to its accumulator and forwards it to     */
+/* slot (s + 1) % 2 of its right neighbour.  So device d adds x_{d-1},      */
+/* x_{d-2}, ..., and last its own x_d, which comes back after P hops:       */
+/*     out[d] = ((((0 + x_{d-1}) + x_{d-2}) + ...) + x_d.                   */
+/* The page forwards at the last step too (the item has then been          */
+/* everywhere; it changes only the slots, as its table shows).              */
+/*                                                                          */
+/* `slots` (2*P*n, device-major, slot-major) and `acc` (P*n) hold the state */
+/* after `steps` steps (0 .. P); a slot never written holds 0.              */
+/* ------------------------------------------------------------------------ */
+int oracle_psum_circ_f32(const float *src, float *acc, float *slots, int P, size_t n, int steps)
+{
+    if (P < 1 || P > 64 || steps < 0 || steps > P) return -1;
+    float *item = (float *)malloc(sizeof(float) * (n ? n : 1) * (size_t)P);
+    if (!item) return -1;
+    memset(acc, 0, sizeof(float) * (size_t)P * n);
+    memset(slots, 0, sizeof(float) * 2 * (size_t)P * n);
+    for (int d = 0; d < P; ++d)          /* the first send: input -> right neighbour's slot 0 */
+        memcpy(slots + ((size_t)((d + 1) % P) * 2 + 0) * n, src + (size_t)d * n, sizeof(float) * n);
+    for (int s = 0; s < steps; ++s) {
+        const int w = s % 2;
+        for (int d = 0; d < P; ++d) {    /* read every working slot first */
+            const float *in = slots + ((size_t)d * 2 + w) * n;
+            memcpy(item + (size_t)d * n, in, sizeof(float) * n);
+            for (size_t i = 0; i < n; ++i) acc[(size_t)d * n + i] += in[i];
+        }
+        for (int d = 0; d < P; ++d)      /* then forward to the right neighbour's other slot */
+            memcpy(slots + ((size_t)((d + 1) % P) * 2 + (1 - w)) * n, item + (size_t)d * n,
+                   sizeof(float) * n);
+    }
+    free(item);
+    return 0;
+}
+
+/* The same on int32 (wrapping adds). */
+int oracle_psum_circ_i32(const int32_t *src, int32_t *acc, int32_t *slots, int P, size_t n, int steps)
+{
+    if (P < 1 || P > 64 || steps < 0 || steps > P) return -1;
+    int32_t *item = (int32_t *)malloc(sizeof(int32_t) * (n ? n : 1) * (size_t)P);
+    if (!item) return -1;
+    memset(acc, 0, sizeof(int32_t) * (size_t)P * n);
+    memset(slots, 0, sizeof(int32_t) * 2 * (size_t)P * n);
+    for (int d = 0; d < P; ++d)
+        memcpy(slots + ((size_t)((d + 1) % P) * 2 + 0) * n, src + (size_t)d * n, sizeof(int32_t) * n);
+    for (int s = 0; s < steps; ++s) {
+        const int w = s % 2;
+        for (int d = 0; d < P; ++d) {
+            const int32_t *in = slots + ((size_t)d * 2 + w) * n;
+            memcpy(item + (size_t)d * n, in, sizeof(int32_t) * n);
+            for (size_t i = 0; i < n; ++i)
+                acc[(size_t)d * n + i] = (int32_t)((uint32_t)acc[(size_t)d * n + i] + (uint32_t)in[i]);
+        }
+        for (int d = 0; d < P; ++d)
+            memcpy(slots + ((size_t)((d + 1) % P) * 2 + (1 - w)) * n, item + (size_t)d * n,
+                   sizeof(int32_t) * n);
+    }
+    free(item);
+    return 0;
+}
+
+/* bf16 inputs circulate unchanged; the accumulator is fp32 and the result
+ * is rounded once to bf16 (the reading used for every bf16 sum here). */
+int oracle_psum_circ_bf16(const uint16_t *src, uint16_t *dst, int P, size_t n)
+{
+    if (P < 1 || P > 64) return -1;
+    float *acc = (float *)calloc((n ? n : 1) * (size_t)P, sizeof(float));
+    if (!acc) return -1;
+    for (int d = 0; d < P; ++d)
+        for (int s = 0; s < P; ++s) {          /* item of step s: x_{(d - s - 1) mod P} */
+            const uint16_t *in = src + (size_t)(((d - s - 1) % P + P) % P) * n;
+            for (size_t i = 0; i < n; ++i) acc[(size_t)d * n + i] += bf16_to_f32(in[i]);
+        }
+    for (size_t i = 0; i < (size_t)P * n; ++i) dst[i] = oracle_bf16_from_f32(acc[i]);
+    free(acc);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Plain definitions used as references for tolerance checks.               */
 /* Sum over ranks in rank order 0..P-1, in fp64, and the sum of magnitudes  */
 /* (the denominator of the componentwise error bound of recursive sums).    */

@@ -12,6 +12,7 @@ import pytest
 import oracle
 import test_oracle_bidir_pins as bidir
 import test_oracle_pins as pins
+import test_oracle_psum_circ_pins as psum
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ring_oracle.c")
 
@@ -49,6 +50,16 @@ MUTANTS = {
     "bidir bf16 rounds every step":
         ("ntop[(size_t)d * h + i] = last ? from_right[i] : from_right[i] + bf16_to_f32(xt[i]);",
          "ntop[(size_t)d * h + i] = last ? from_right[i] : bf16_to_f32(oracle_bf16_from_f32(from_right[i] + bf16_to_f32(xt[i])));"),
+    "psum forwards to the left":
+        ("memcpy(slots + ((size_t)((d + 1) % P) * 2 + (1 - w)) * n, item + (size_t)d * n,\n                   sizeof(float) * n);",
+         "memcpy(slots + ((size_t)((d + P - 1) % P) * 2 + (1 - w)) * n, item + (size_t)d * n,\n                   sizeof(float) * n);"),
+    "psum adds the receiving slot": ("const float *in = slots + ((size_t)d * 2 + w) * n;",
+                                     "const float *in = slots + ((size_t)d * 2 + (1 - w)) * n;"),
+    "psum first send into slot 1":
+        ("memcpy(slots + ((size_t)((d + 1) % P) * 2 + 0) * n, src + (size_t)d * n, sizeof(float) * n);",
+         "memcpy(slots + ((size_t)((d + 1) % P) * 2 + 1) * n, src + (size_t)d * n, sizeof(float) * n);"),
+    "psum bf16 items in the wrong order": ("const uint16_t *in = src + (size_t)(((d - s - 1) % P + P) % P) * n;",
+                                           "const uint16_t *in = src + (size_t)(((d + s + 1) % P + P) % P) * n;"),
     "magnitude sum without abs": ("            m += fabs(x);\n        }\n        sum[i] = a;\n        if (abssum) abssum[i] = m;\n    }\n    return 0;\n}\n\nint oracle_rank_sum_f64_bf16",
                                   "            m += x;\n        }\n        sum[i] = a;\n        if (abssum) abssum[i] = m;\n    }\n    return 0;\n}\n\nint oracle_rank_sum_f64_bf16"),
 }
@@ -82,6 +93,12 @@ def _checks():
     yield "bidir odd chunks", lambda: bidir.test_bidir_odd_chunks(3, 5)
     yield "bidir p1 p2", bidir.test_bidir_p1_identity_and_p2
     yield "bidir bf16", lambda: bidir.test_bidir_bf16_one_rounding(4)
+    yield "psum page trace", psum.test_psum_matches_page_trace
+    for P in (2, 3, 4):
+        yield "psum sum P=%d" % P, lambda P=P: psum.test_psum_is_sum_over_devices_int32(P)
+        yield "psum visits P=%d" % P, lambda P=P: psum.test_psum_every_item_visits_every_device(P)
+    yield "psum bf16", lambda: psum.test_psum_fp32_bound_and_bf16_one_rounding(4)
+    yield "psum bf16 order", psum.test_psum_bf16_follows_page_order
 
 
 def _load_variant(tmp_path, text, name):
@@ -100,7 +117,8 @@ def _run_checks_with(lib, monkeypatch):
                   "oracle_all_reduce_i32", "oracle_reduce_scatter_bf16", "oracle_all_reduce_bf16",
                   "oracle_bf16_from_f32_array", "oracle_rank_sum_f64_f32", "oracle_rank_sum_f64_bf16",
                   "oracle_reduce_scatter_bidir_f32", "oracle_reduce_scatter_bidir_i32",
-                  "oracle_reduce_scatter_bidir_bf16"):
+                  "oracle_reduce_scatter_bidir_bf16", "oracle_psum_circ_f32", "oracle_psum_circ_i32",
+                  "oracle_psum_circ_bf16"):
         f, g = getattr(lib, fname), getattr(real, fname)
         f.argtypes, f.restype = g.argtypes, g.restype
     monkeypatch.setattr(oracle, "_lib", lib)
