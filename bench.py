@@ -38,6 +38,9 @@ WORKLOADS = {
     # fused GEMM + reduce-scatter: P = 4, A_q, B_q bf16 4096 x 4096, normal(0, 1/64)
     "gemm_rs_p4_4096": dict(op="gemm_rs", P=4, M=4096, N=4096, K=4096, kind="bf16", seed=4,
                             std=1.0 / 64, n=4096 * 4096),
+    # circulating-input psum on the headline inputs (moves P times each buffer)
+    "psum_circ_f32_p8_64Mi": dict(op="psum_circulating", P=8, n=64 << 20, kind="f32", seed=2,
+                                  std=1.0),
     # fused all-gather + GEMM: P = 4, A 4096 x 4096 in row blocks of 1024,
     # B_q bf16 4096 x 4096, normal(0, 1/64)
     "ag_gemm_p4_4096": dict(op="ag_gemm", P=4, M=4096, N=4096, K=4096, kind="bf16", seed=5,
@@ -58,6 +61,9 @@ def moved_bytes(op: str, P: int, n: int, kind: str) -> int:
     C = n // P
     if op == "ppermute":
         return 2 * P * n * (2 if kind == "bf16" else 4)
+    if op == "psum_circulating":
+        # first send (read + write), P slot reads, P-1 forwards, the result
+        return 2 * (P + 1) * n * (2 if kind == "bf16" else 4) * P
     if P == 1:
         return 0
     if op == "reduce_scatter_bidir":
@@ -88,7 +94,7 @@ def moved_bytes(op: str, P: int, n: int, kind: str) -> int:
 
 
 KERNEL_SOURCE = {"ring_step_kernel": ("ring_kernels.hip",), "copy_kernel_tab": ("ring_kernels.hip",),
-                 "ring_bidir_kernel": ("ring_kernels.hip",),
+                 "ring_bidir_kernel": ("ring_kernels.hip",), "ring_psum_kernel": ("ring_kernels.hip",),
                  "gemm_rs_kernel": ("gemm_rs.hip", "gemm_core.h"),
                  "ag_gemm_kernel": ("ag_gemm.hip", "gemm_core.h")}
 
@@ -164,6 +170,9 @@ def _cpu_baseline(w, x):
         want = oracle.ppermute(x)
     elif w["op"] == "reduce_scatter":
         want = oracle.reduce_scatter_bf16(x)[0] if w["kind"] == "bf16" else oracle.reduce_scatter(x)
+    elif w["op"] == "psum_circulating":
+        want = (oracle.psum_circulating_bf16(x) if w["kind"] == "bf16"
+                else oracle.psum_circulating(x)[0])
     elif w["op"] == "reduce_scatter_bidir":
         want = (oracle.reduce_scatter_bidir_bf16(x)[0] if w["kind"] == "bf16"
                 else oracle.reduce_scatter_bidir(x))
@@ -312,18 +321,20 @@ def main():
     src = _to_dev(x, kind)
     dst = [torch.empty_like(t) for t in src]
     op = w["op"]
-    ws_op = {"reduce_scatter": N.OP_REDUCE_SCATTER, "reduce_scatter_bidir": N.OP_REDUCE_SCATTER_BIDIR}
+    ws_op = {"reduce_scatter": N.OP_REDUCE_SCATTER, "reduce_scatter_bidir": N.OP_REDUCE_SCATTER_BIDIR,
+             "psum_circulating": N.OP_PSUM_CIRCULATING}
     ws = rc.workspace(ws_op.get(op, N.OP_ALL_REDUCE), P, n, src[0].dtype)
     stream = torch.cuda.current_stream()
     call = {"ppermute": lambda: rc.ppermute(src, dst),
             "all_reduce": lambda: rc.all_reduce(src, dst, ws=ws),
             "reduce_scatter": lambda: rc.reduce_scatter(src, dst, ws=ws),
-            "reduce_scatter_bidir": lambda: rc.reduce_scatter_bidir(src, dst, ws=ws)}[op]
+            "reduce_scatter_bidir": lambda: rc.reduce_scatter_bidir(src, dst, ws=ws),
+            "psum_circulating": lambda: rc.psum_circulating(src, dst, ws=ws)}[op]
 
     def step():
         call()
-    kernel = {"ppermute": "copy_kernel_tab", "reduce_scatter_bidir": "ring_bidir_kernel"}.get(
-        op, "ring_step_kernel")
+    kernel = {"ppermute": "copy_kernel_tab", "reduce_scatter_bidir": "ring_bidir_kernel",
+              "psum_circulating": "ring_psum_kernel"}.get(op, "ring_step_kernel")
 
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):

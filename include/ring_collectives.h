@@ -59,7 +59,8 @@ typedef enum {
     RING_OP_ALL_REDUCE = 3,
     RING_OP_GEMM_REDUCE_SCATTER = 4,
     RING_OP_REDUCE_SCATTER_BIDIR = 5,
-    RING_OP_ALL_GATHER_GEMM = 6
+    RING_OP_ALL_GATHER_GEMM = 6,
+    RING_OP_PSUM_CIRCULATING = 7
 } ring_op_t;
 
 enum {
@@ -137,6 +138,24 @@ int ring_reduce_scatter(const void *const *src, void *const *dst, int P, size_t 
  */
 int ring_reduce_scatter_bidir(const void *const *src, void *const *dst, int P, size_t n,
                               int dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Circulating-input psum ("Pallas TPU Distributed Collectives 复习文档",
+ * section 3, lax.psum, and its walk-through in 3.5): every rank's whole
+ * input travels once around the ring to the right, and each rank adds what
+ * arrives into an accumulator that starts at zero, so
+ *     dst[r] = (((0 + src[r-1]) + src[r-2]) + ...) + src[r]   (indices mod P)
+ * -- every rank ends with the sum over ranks, each in its own order.  Items
+ * move through two receive slots per rank in the workspace, and a rank
+ * writes its neighbour's slot only after the neighbour has flagged it free
+ * (the page's capacity semaphore).  It moves P times a rank's buffer per
+ * rank, against 2(P-1)/P for ring_all_reduce: the page's teaching contrast.
+ * bf16: the inputs circulate unchanged, the accumulator is fp32, the result
+ * is rounded once.  P need not divide n.  In place (dst[r] == src[r]) is
+ * allowed.  Workspace: RING_OP_PSUM_CIRCULATING.
+ */
+int ring_psum_circulating(const void *const *src, void *const *dst, int P, size_t n,
+                          int dtype, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Ring all-gather, P-1 rounds ("全归约 3", Walkthrough, second phase; the

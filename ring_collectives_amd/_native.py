@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libring_collectives.so")
 # ring_dtype_t / ring_op_t / error codes, as declared in include/ring_collectives.h
 RING_F32, RING_BF16, RING_I32 = 0, 1, 2
 (OP_PPERMUTE, OP_REDUCE_SCATTER, OP_ALL_GATHER, OP_ALL_REDUCE, OP_GEMM_REDUCE_SCATTER,
- OP_REDUCE_SCATTER_BIDIR, OP_ALL_GATHER_GEMM) = range(7)
+ OP_REDUCE_SCATTER_BIDIR, OP_ALL_GATHER_GEMM, OP_PSUM_CIRCULATING) = range(8)
 RING_OK, RING_EINVAL, RING_EUNSUPPORTED, RING_EWORKSPACE, RING_EHIP, RING_ETIMEOUT = (
     0, -1, -2, -3, -4, -5)
 MAX_RANKS = 64
@@ -31,6 +31,7 @@ SIGNATURES = {
     "ring_ppermute": (_i, [_pp, _pp, _i, _sz, _i, _vp]),
     "ring_reduce_scatter": (_i, [_pp, _pp, _i, _sz, _i, _vp, _sz, _vp]),
     "ring_reduce_scatter_bidir": (_i, [_pp, _pp, _i, _sz, _i, _vp, _sz, _vp]),
+    "ring_psum_circulating": (_i, [_pp, _pp, _i, _sz, _i, _vp, _sz, _vp]),
     "ring_all_gather": (_i, [_pp, _pp, _i, _sz, _i, _vp, _sz, _vp]),
     "ring_all_reduce": (_i, [_pp, _pp, _i, _sz, _i, _vp, _sz, _vp]),
     "gemm_reduce_scatter": (_i, [_pp, _pp, _pp, _i, _i, _i, _i, _vp, _sz, _vp]),

@@ -97,6 +97,13 @@ def reduce_scatter_bidir(src, dst, ws=None, stream=None):
                   N.OP_REDUCE_SCATTER_BIDIR, src, dst, ws, stream)
 
 
+def psum_circulating(src, dst, ws=None, stream=None):
+    """Circulating-input psum: every input once around the ring; dst[r] <-
+    the sum over ranks, added in the order src[r-1], src[r-2], ..., src[r]."""
+    return _rs_ar(N.lib().ring_psum_circulating, "ring_psum_circulating", N.OP_PSUM_CIRCULATING,
+                  src, dst, ws, stream)
+
+
 def all_reduce(src, dst, ws=None, stream=None):
     """Ring all-reduce: every dst[r] <- sum over ranks of src."""
     return _rs_ar(N.lib().ring_all_reduce, "ring_all_reduce", N.OP_ALL_REDUCE,

@@ -133,7 +133,7 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
             else
                 copy_rows<POL_DEV>(p.Af[left] + ((size_t)c * Mc + r0) * p.K, dst, r1 - r0, p.K, tid,
                                    nthreads);
-            if (!(q == 0 && f == p.drop_round)) wg_signal(ag_flag(p, f, q, pos), tid);
+            if (!(q == 0 && p.drop_round > 0 && f == p.drop_round)) wg_signal(ag_flag(p, f, q, pos), tid);
         }
         // GEMM tiles of chunk c
         for (int pos = grp; pos < p.tpc; pos += p.groups) {

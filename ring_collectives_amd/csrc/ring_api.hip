@@ -41,6 +41,21 @@ RingWs ring_ws_layout(int P, size_t n, int dtype) {
     return w;
 }
 
+// Circulating psum: the whole buffer is tiled (no chunks); flag rows 0..P-1
+// say a receive slot holds an item, rows P..2P-1 that a slot is free again.
+struct PsumWs {
+    size_t flags_off, slots_off, total;
+};
+static PsumWs psum_ws_layout(int P, size_t n, int dtype) {
+    PsumWs w;
+    const size_t tile_min = (size_t)kWave * kMinTileVecs * elems_per_vec(dtype);
+    const size_t T = (n + tile_min - 1) / tile_min;
+    w.flags_off = kStatusBytes;
+    w.slots_off = w.flags_off + align_up(2 * (size_t)P * (size_t)P * (T ? T : 1) * kFlagStride * sizeof(int), 256);
+    w.total = w.slots_off + align_up(2 * (size_t)P * n * (size_t)elem_bytes(dtype), 256);
+    return w;
+}
+
 static int env_int(const char* name, int dflt) {
     const char* v = getenv(name);
     return v && *v ? atoi(v) : dflt;
@@ -233,6 +248,52 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
     return RING_OK;
 }
 
+// Launch the circulating psum kernel.
+static int run_psum(const void* const* src, void* const* dst, int P, size_t n, int dtype, void* ws,
+                    size_t ws_bytes, void* stream) {
+    const PsumWs lay = psum_ws_layout(P, n, dtype);
+    if (!ws || ((uintptr_t)ws & 255) || ws_bytes < lay.total) return RING_EWORKSPACE;
+    const ring_tuning_t tu = tuning();
+    const DevInfo di = dev_info();
+    const int esz = elem_bytes(dtype);
+    const int tile = kWave * tu.tile_vecs * elems_per_vec(dtype);
+    const int T = (int)(((long long)n + tile - 1) / tile);
+    RingParams prm;
+    memset(&prm, 0, sizeof prm);
+    int vec_ok = (((long long)n * esz) % 16) == 0;
+    for (int r = 0; r < P; ++r) {
+        prm.src[r] = src[r];
+        prm.dst[r] = dst[r];
+        if (((uintptr_t)src[r] | (uintptr_t)dst[r]) & 15) vec_ok = 0;
+    }
+    prm.flags = (int*)((char*)ws + lay.flags_off);
+    prm.slots = (char*)ws + lay.slots_off;
+    prm.status = (Status*)ws;
+    prm.n = (long long)n;
+    prm.C = (long long)n;
+    prm.spin_limit = (long long)(tu.timeout_s * (double)di.wall_khz * 1000.0);
+    prm.P = P;
+    prm.T = T;
+    prm.tile = tile;
+    prm.vec_ok = vec_ok;
+    prm.psum = 1;
+    prm.drop_round = tu.drop_round;
+    // every wave of a tile position's ring must be resident: as run_ring
+    int occ = ring_blocks_per_cu(dtype, tu.tile_vecs, 2);
+    if (occ < 1) return RING_EHIP;
+    int bpc = (tu.waves_per_cu + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (bpc > occ / 2) bpc = occ / 2 > 0 ? occ / 2 : 1;
+    const long long max_waves = (long long)di.cus * bpc * kWavesPerBlock;
+    long long W = max_waves / P;
+    if (W > T) W = T;
+    if (W < 1) return RING_EUNSUPPORTED;
+    prm.waves_per_rank = (int)W;
+    prm.map_mode = 0;
+    const long long blocks = ((long long)P * W + kWavesPerBlock - 1) / kWavesPerBlock;
+    return launch_ring(prm, dtype, tu.tile_vecs, (int)blocks, as_stream(stream)) == hipSuccess ? RING_OK
+                                                                                               : RING_EHIP;
+}
+
 // ------------------------------------------------------------------ C ABI
 extern "C" {
 
@@ -256,6 +317,9 @@ size_t ring_workspace_bytes(int op, int P, size_t n, int dtype) {
             return gemm_rs_workspace_bytes(P, n);
         case RING_OP_ALL_GATHER_GEMM:
             return ag_gemm_workspace_bytes(P, n);
+        case RING_OP_PSUM_CIRCULATING:
+            if (!elem_bytes(dtype)) return 0;
+            return psum_ws_layout(P, n, dtype).total;
         default: return 0;
     }
 }
@@ -312,6 +376,17 @@ int ring_reduce_scatter_bidir(const void* const* src, void* const* dst, int P, s
 int ring_all_reduce(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream) {
     return rs_or_ar(src, dst, P, n, dtype, ws, ws_bytes, stream, KIND_AR);
+}
+
+int ring_psum_circulating(const void* const* src, void* const* dst, int P, size_t n, int dtype,
+                          void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_common(src, P, n, dtype, false);
+    if (rc) return rc;
+    if ((rc = check_common(dst, P, n, dtype, false))) return rc;
+    const size_t bytes = n * (size_t)elem_bytes(dtype);
+    if (overlap_kind(src, bytes, dst, bytes, P, true) < 0) return RING_EINVAL;
+    if (n == 0) return RING_OK;
+    return run_psum(src, dst, P, n, dtype, ws, ws_bytes, stream);
 }
 
 int ring_all_gather(const void* const* src_or_null, void* const* dst, int P, size_t n, int dtype,

@@ -43,6 +43,9 @@ struct RingParams {
     int compact_src;                  // all-gather from compact pieces
     int map_mode;                     // wave -> (rank, lane) mapping
     int drop_round;                   // test hook: rank 0 skips this signal (0 = off)
+    // circulating psum only
+    void* slots;                      // P x 2 receive slots of n elements
+    int psum;                         // 1: the circulating-input psum kernel
     // bidirectional reduce-scatter only
     int bidir;                        // 1: top halves travel left, bottom halves right
     int T_top;                        // positions 0 .. T_top-1 are top-half tiles
@@ -70,7 +73,7 @@ hipError_t launch_copy(const void* const* src, void* const* dst, int P, size_t b
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_ring(RingParams& prm, int dtype, int tile_vecs, int grid_blocks,
                        hipStream_t s);   // prm.bidir selects the bidirectional kernel
-int ring_blocks_per_cu(int dtype, int tile_vecs, int bidir);   // occupancy of the ring kernels
+int ring_blocks_per_cu(int dtype, int tile_vecs, int kind);   // occupancy: 0 ring, 1 bidir, 2 psum
 
 // GEMM + reduce-scatter workspace size (n = M * N per rank).
 size_t gemm_rs_workspace_bytes(int P, size_t n);

@@ -7,6 +7,8 @@
 //                         virtual rank at once.
 //   * ring_bidir_kernel : the bidirectional reduce-scatter (halves of every
 //                         chunk travel both ways round the ring).
+//   * ring_psum_kernel  : the circulating-input psum (every input once round
+//                         the ring, double receive slots, capacity flags).
 //   * fill_zero_kernel  : workspace initialisation.
 //
 // Ring schedule ("全归约 3：Ring——每步大小恒定", Walkthrough).  P ranks, chunk
@@ -432,6 +434,178 @@ __global__ __launch_bounds__(kBlock) void ring_bidir_kernel(RingParams p) {
     }
 }
 
+// ---------------------------------------------------------------- circulating-input psum
+// ("Pallas TPU Distributed Collectives 复习文档", section 3.)  Every rank's
+// whole input travels once around the ring; each rank adds what arrives,
+// x_{d-1} first and its own input last, into an accumulator that starts at
+// zero.  Rank d has two receive slots.  Tile j of rank d, in one wave:
+//   first send : src[d] -> slot 0 of the right neighbour; flag recv(0, right)
+//   step s     : (s < P-1) flag cap(s, d): my slot (s+1) % 2 is free again
+//                wait recv(s, d); load slot s % 2; add it to the accumulator
+//                (s < P-1) wait cap(s, right); store the item into the right
+//                neighbour's slot (s+1) % 2; flag recv(s+1, right)
+//   end        : dst[d] = the accumulator
+// recv(s, d) says slot s % 2 of rank d holds the item of step s; cap(s, d)
+// that rank d has finished step s-1, so its slot (s+1) % 2 may be written
+// (the page's capacity semaphore).  The last step's forward, which the page
+// also makes, would only carry an item back to where it has been: it is left
+// out.  Every flag has one reader and is cleared by it.  A wave waits on the
+// rank it receives from (an earlier step) or on its right neighbour having
+// started step s (which needs that neighbour's step s-1 and so on round the
+// ring, ending at an earlier step of this wave), so the P waves of a tile
+// position always progress.
+__device__ __forceinline__ int* recv_flag(const RingParams& p, int s, int d, int j) {
+    return flag_at(p, s, d, j);
+}
+__device__ __forceinline__ int* cap_flag(const RingParams& p, int s, int d, int j) {
+    return flag_at(p, p.P + s, d, j);
+}
+
+template <int DT, int U>
+__device__ bool psum_tile(const RingParams& p, int d, int j, int lane) {
+    constexpr int ESZ = sizeof(typename Elem<DT>::T);
+    const int P = p.P;
+    const int right = (d + 1) % P;
+    const long long e0 = (long long)j * p.tile;
+    const long long len = (p.n - e0) < p.tile ? (p.n - e0) : p.tile;
+    const long long nb = len * ESZ;
+    auto slot = [&](int r, int b) {
+        return tile_view((const char*)p.slots + (((size_t)r * 2 + b) * p.n + e0) * ESZ, nb);
+    };
+    const rsrc_t own = tile_view((const char*)p.src[d] + e0 * ESZ, nb);
+    const rsrc_t out = tile_view((char*)p.dst[d] + e0 * ESZ, nb);
+    const bool drop = (d == 0 && p.drop_round > 0);   // test hook (0 = off)
+    auto sig = [&](int* f, int row) {
+        if (!(drop && row == p.drop_round)) signal_flag(f, lane);
+    };
+    auto wait = [&](int* f, int s) {
+        return wait_flag(f, p.status, p.spin_limit, d, s, j, lane, peek_flag(f));
+    };
+    if (p.vec_ok) {
+        // a lane vector is 4 elements: 16 bytes (fp32, int32) or 8 (bf16)
+        float accf[U][4];
+        unsigned acci[U][4];
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                accf[i][e] = 0.0f;
+                acci[i][e] = 0u;
+            }
+        // first send
+        if constexpr (DT == DT_BF16)
+            copy_tile_p<U / 2, 2, POL_PLAIN, POL_DEV>(slot(right, 0), own, len, true, lane);
+        else
+            copy_tile_p<U, 4, POL_PLAIN, POL_DEV>(slot(right, 0), own, len, true, lane);
+        sig(recv_flag(p, 0, right, j), 0);
+        for (int s = 0; s < P; ++s) {
+            const bool fwd = (s < P - 1);
+            if (fwd) sig(cap_flag(p, s, d, j), P + s);
+            if (!wait(recv_flag(p, s, d, j), s)) return false;
+            const rsrc_t in = slot(d, s & 1);
+            if constexpr (DT == DT_BF16) {
+                u32x2 it[U];
+#pragma unroll
+                for (int i = 0; i < U; ++i) {
+                    it[i] = ld8<POL_DEV>(in, (unsigned)(lane + i * kWave) * 8u);
+                    accf[i][0] += bf16_lo(it[i][0]);
+                    accf[i][1] += bf16_hi(it[i][0]);
+                    accf[i][2] += bf16_lo(it[i][1]);
+                    accf[i][3] += bf16_hi(it[i][1]);
+                }
+                if (fwd) {
+                    if (!wait(cap_flag(p, s, right, j), s)) return false;
+                    const rsrc_t o = slot(right, (s + 1) & 1);
+#pragma unroll
+                    for (int i = 0; i < U; ++i) st8<POL_DEV>(it[i], o, (unsigned)(lane + i * kWave) * 8u);
+                    sig(recv_flag(p, s + 1, right, j), s + 1);
+                }
+            } else {
+                u32x4 it[U];
+#pragma unroll
+                for (int i = 0; i < U; ++i) {
+                    it[i] = ld16<POL_DEV>(in, (unsigned)(lane + i * kWave) * 16u);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (DT == DT_F32) accf[i][e] += __uint_as_float(it[i][e]);
+                        else acci[i][e] += it[i][e];
+                    }
+                }
+                if (fwd) {
+                    if (!wait(cap_flag(p, s, right, j), s)) return false;
+                    const rsrc_t o = slot(right, (s + 1) & 1);
+#pragma unroll
+                    for (int i = 0; i < U; ++i) st16<POL_DEV>(it[i], o, (unsigned)(lane + i * kWave) * 16u);
+                    sig(recv_flag(p, s + 1, right, j), s + 1);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const unsigned v = (unsigned)(lane + i * kWave);
+            if constexpr (DT == DT_BF16) {
+                u32x2 o;
+                o[0] = pack_bf16(accf[i][0], accf[i][1]);
+                o[1] = pack_bf16(accf[i][2], accf[i][3]);
+                st8<POL_PLAIN>(o, out, v * 8u);
+            } else {
+                u32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = DT == DT_F32 ? __float_as_uint(accf[i][e]) : acci[i][e];
+                st16<POL_PLAIN>(o, out, v * 16u);
+            }
+        }
+        return true;
+    }
+    // scalar path (buffers whose element count breaks 16-byte alignment):
+    // one element per lane per pass; the forward re-reads the item from this
+    // rank's own slot, which nobody writes before this wave flags cap(s+1, d)
+    constexpr int EPL = U * 4;   // elements per lane
+    unsigned acc[EPL];           // fp32 bits, or the int32 sum
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[i] = 0u;
+    copy_tile_p<U, ESZ, POL_PLAIN, POL_DEV>(slot(right, 0), own, len, false, lane);
+    sig(recv_flag(p, 0, right, j), 0);
+    for (int s = 0; s < P; ++s) {
+        const bool fwd = (s < P - 1);
+        if (fwd) sig(cap_flag(p, s, d, j), P + s);
+        if (!wait(recv_flag(p, s, d, j), s)) return false;
+        const rsrc_t in = slot(d, s & 1);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const unsigned idx = (unsigned)(lane + i * kWave);
+            if constexpr (DT == DT_BF16)
+                acc[i] = __float_as_uint(__uint_as_float(acc[i]) +
+                                         __uint_as_float((unsigned)ld2<POL_DEV>(in, idx * 2u) << 16));
+            else if constexpr (DT == DT_F32)
+                acc[i] = __float_as_uint(__uint_as_float(acc[i]) + __uint_as_float(ld4<POL_DEV>(in, idx * 4u)));
+            else
+                acc[i] += ld4<POL_DEV>(in, idx * 4u);
+        }
+        if (fwd) {
+            if (!wait(cap_flag(p, s, right, j), s)) return false;
+            copy_tile_p<U, ESZ, POL_DEV, POL_DEV>(slot(right, (s + 1) & 1), in, len, false, lane);
+            sig(recv_flag(p, s + 1, right, j), s + 1);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const unsigned idx = (unsigned)(lane + i * kWave);
+        if constexpr (DT == DT_BF16) st2<POL_PLAIN>((unsigned short)bf16_rne(__uint_as_float(acc[i])), out, idx * 2u);
+        else st4<POL_PLAIN>(acc[i], out, idx * 4u);
+    }
+    return true;
+}
+
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void ring_psum_kernel(RingParams p) {
+    int r, w;
+    if (!map_wave(p, r, w)) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    for (int j = w; j < p.T; j += p.waves_per_rank)
+        if (!psum_tile<DT, U>(p, r, j, lane)) return;
+}
+
 // ---------------------------------------------------------------- copy / fill
 __global__ __launch_bounds__(kBlock) void fill_zero_kernel(unsigned* p, long long words, long long tail_bytes) {
     const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -505,7 +679,9 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 
 template <int DT, int U>
 static hipError_t launch_ring_t(RingParams& prm, int grid, hipStream_t s) {
-    if (prm.bidir)
+    if (prm.psum)
+        hipLaunchKernelGGL((ring_psum_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
+    else if (prm.bidir)
         hipLaunchKernelGGL((ring_bidir_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
     else
         hipLaunchKernelGGL((ring_step_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
@@ -523,29 +699,30 @@ static hipError_t launch_ring_dt(RingParams& prm, int tile_vecs, int grid, hipSt
 }
 
 template <int DT, int U>
-static int blocks_per_cu_t(int bidir) {
+static int blocks_per_cu_t(int kind) {
     int nb = 0;
     const hipError_t e =
-        bidir ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_bidir_kernel<DT, U>, kBlock, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_step_kernel<DT, U>, kBlock, 0);
+        kind == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_psum_kernel<DT, U>, kBlock, 0)
+        : kind == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_bidir_kernel<DT, U>, kBlock, 0)
+                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_step_kernel<DT, U>, kBlock, 0);
     return e == hipSuccess ? nb : 0;
 }
 
 template <int DT>
-static int blocks_per_cu_dt(int tile_vecs, int bidir) {
+static int blocks_per_cu_dt(int tile_vecs, int kind) {
     switch (tile_vecs) {
-        case 4: return blocks_per_cu_t<DT, 4>(bidir);
-        case 8: return blocks_per_cu_t<DT, 8>(bidir);
-        case 16: return blocks_per_cu_t<DT, 16>(bidir);
+        case 4: return blocks_per_cu_t<DT, 4>(kind);
+        case 8: return blocks_per_cu_t<DT, 8>(kind);
+        case 16: return blocks_per_cu_t<DT, 16>(kind);
         default: return 0;
     }
 }
 
-int ring_blocks_per_cu(int dtype, int tile_vecs, int bidir) {
+int ring_blocks_per_cu(int dtype, int tile_vecs, int kind) {
     switch (dtype) {
-        case RING_F32: return blocks_per_cu_dt<DT_F32>(tile_vecs, bidir);
-        case RING_I32: return blocks_per_cu_dt<DT_I32>(tile_vecs, bidir);
-        case RING_BF16: return blocks_per_cu_dt<DT_BF16>(tile_vecs, bidir);
+        case RING_F32: return blocks_per_cu_dt<DT_F32>(tile_vecs, kind);
+        case RING_I32: return blocks_per_cu_dt<DT_I32>(tile_vecs, kind);
+        case RING_BF16: return blocks_per_cu_dt<DT_BF16>(tile_vecs, kind);
         default: return 0;
     }
 }
