@@ -381,3 +381,166 @@ def gemm_reduce_scatter_rows_f64(A: np.ndarray, B: np.ndarray, r: int, rows) -> 
         s = s + a @ b
         m = m + np.abs(a) @ np.abs(b)
     return s, m
+
+
+# --------------------------------------------------------------------------
+# tensor-parallel MLP layer
+# --------------------------------------------------------------------------
+_GELU_C = np.sqrt(2.0 / np.pi)
+
+
+def gelu_tanh(x: np.ndarray) -> np.ndarray:
+    """GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+    -- jax.nn.gelu's default, the activation of the tensor-parallel MLP in
+    "TPU 与分布式通信原语" (collective matmul) -- in fp64.  It is evaluated
+    through the identity 0.5 (1 + tanh(z)) = 1 / (1 + exp(-2z)), which keeps
+    full relative accuracy where 1 + tanh(z) would cancel (large negative x)."""
+    x = np.asarray(x, dtype=np.float64)
+    t = 2.0 * _GELU_C * (x + 0.044715 * x * x * x)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-t))
+
+
+def _bf16_grid(v: np.ndarray, how) -> np.ndarray:
+    """Round fp64 values to bf16 (8 significant bits, fp32's exponent range,
+    subnormals spaced 2^-133) with `how` (np.rint: nearest, ties to even;
+    np.floor / np.ceil: directed).  Returns fp64 values; |v| beyond bf16's
+    largest finite value is not expected here."""
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)                       # v = m 2^e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                  # below 2^-126: the subnormal spacing
+    step = np.ldexp(1.0, e - 8)
+    return how(v / step) * step
+
+
+def bf16_from_f64(v: np.ndarray) -> np.ndarray:
+    """One rounding of fp64 values to bf16 (nearest, ties to even) -> uint16."""
+    r = _bf16_grid(v, np.rint).astype(np.float32)       # exact: 8 significant bits
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_nearest(v: np.ndarray) -> np.ndarray:
+    """bf16_from_f64 as fp64 values.  Non-decreasing in v, so the roundings
+    of every value in [lo, hi] are the bf16 values in
+    [bf16_nearest(lo), bf16_nearest(hi)]."""
+    return _bf16_grid(v, np.rint)
+
+
+def _f64(h: np.ndarray) -> np.ndarray:
+    return bf16_to_f32(h).astype(np.float64)
+
+
+def tp_mlp_layer(x_shards: np.ndarray, W1: np.ndarray, W2: np.ndarray):
+    """One layer of the tensor-parallel MLP of "TPU 与分布式通信原语"
+    (collective matmul): X = gelu(X @ W1) @ W2 with W1 split by columns and W2
+    by rows, one device's view being
+        out_shard = ReduceScatter(gelu(AllGather(x_shard) @ W1_i) @ W2_i),
+    the activation shards being row blocks (tokens) of X.  Steps, in the
+    page's order (all bf16 arrays as uint16 bit patterns):
+      1. ring all-gather of the row blocks x_shards (P, M/P, D) -> x_full;
+      2. local0 = x_full @ W1[q] (fp64 product), rounded to bf16 (the page's
+         bf16 matmul output);
+      3. local1 = gelu(local0), rounded to bf16 -> h[q] (P, M, F/P);
+      4. local2 = h[q] @ W2[q] (fp64 product) rounded to fp32, then the fp32
+         ring reduce-scatter of its row blocks, and the owner's sum rounded
+         once to bf16 -> out (P, M/P, D).
+    Returns (x_full, h, out)."""
+    x_shards = _ranks(x_shards, np.uint16)
+    W1 = _ranks(W1, np.uint16)
+    W2 = _ranks(W2, np.uint16)
+    P, Mq, D = x_shards.shape
+    full = all_gather_pieces(x_shards.reshape(P, Mq * D)).reshape(P, P * Mq, D)
+    h = np.empty((P, P * Mq, W1.shape[2]), dtype=np.uint16)
+    for q in range(P):
+        local0 = bf16_from_f64(_f64(full[q]) @ _f64(W1[q]))
+        h[q] = bf16_from_f64(gelu_tanh(_f64(local0)))
+    partial = gemm_products_f32(h, W2)                      # (P, M, D) fp32
+    st = reduce_scatter(partial.reshape(P, -1))
+    out = np.stack([bf16_from_f32(st[r].reshape(P * Mq, D)[r * Mq:(r + 1) * Mq]) for r in range(P)])
+    return full, h, out
+
+
+def _exact_in_fp32(a: np.ndarray, b: np.ndarray) -> bool:
+    """True if every partial sum of every dot product of a @ b is exact in
+    fp32 whatever the order: all products are multiples of a common power of
+    two g (the coarsest grid both operands sit on) and sum |a b| < 2^24 g."""
+    def grid_bits(v):
+        v = v[v != 0]
+        for k in range(-160, 161):
+            s = np.ldexp(v, k)
+            if np.all(s == np.rint(s)):
+                return k
+        return None
+    ka, kb = grid_bits(a), grid_bits(b)
+    if ka is None or kb is None:
+        return False
+    g = np.ldexp(1.0, -(ka + kb))
+    return float((np.abs(a) @ np.abs(b)).max(initial=0.0)) < 2.0 ** 24 * g
+
+
+_GELU_ARGMIN = -0.7517916     # gelu's only minimum lies in [-0.7518, -0.7517]
+
+
+def gelu_fp32_rel_error(x: np.ndarray) -> np.ndarray:
+    """Relative error allowed for gelu(x) evaluated in fp32 as x sigmoid(t),
+    t = 2 sqrt(2/pi) (x + 0.044715 x^3), with the exponential exp(-|t|)
+    accurate to 2 units in the last place: the constants and the cube and
+    sums before t carry at most 7 roundings, an absolute error of 7 u |t| in
+    t and so a relative 7 u |t| in the exponential; sigmoid, 1 + e, the
+    division and the last product add a few units more (u = 2^-24).  The
+    bound used is twice (8 + 7 |t|) u."""
+    x = np.asarray(x, dtype=np.float64)
+    t = 2.0 * _GELU_C * (x + 0.044715 * x * x * x)
+    return 2.0 * (8.0 + 7.0 * np.abs(t)) * 2.0 ** -24
+
+
+def tp_mlp_bounds(x_shards: np.ndarray, W1: np.ndarray, W2: np.ndarray, r: int, rows):
+    """Reference intervals for tp_mlp_layer at the token rows `rows` of rank
+    r's output block, for an implementation that accumulates both products in
+    fp32 in any order and evaluates gelu in fp32.
+
+    Returns (h_ref, h_lo, h_hi, s, t):
+      h_ref (P, R, F/P) bf16 bits: this oracle's h at those rows;
+      h_lo, h_hi (P, R, F/P) fp64: the range of every h an fp32
+        implementation may produce (the first product within the
+        recursive-summation bound D 2^-24 sum|x w|, or exact when the
+        operands' grid makes it so, rounded to bf16; gelu of that within
+        gelu_fp32_rel_error, rounded to bf16);
+      s (R, D) fp64: sum_q h_ref[q] @ W2[q] at those rows;
+      t (R, D) fp64: how far an implementation's fp32 out may lie from s:
+        sum_q |h - h_ref| @ |W2[q]| over the h intervals plus
+        (F/P + P) 2^-24 sum_q max|h| @ |W2[q]|.
+    The bf16 output must lie in [bf16_nearest(s - t), bf16_nearest(s + t)]."""
+    x_shards = _ranks(x_shards, np.uint16)
+    W1 = _ranks(W1, np.uint16)
+    W2 = _ranks(W2, np.uint16)
+    P, Mq, D = x_shards.shape
+    Fr = W1.shape[2]
+    g = np.asarray(rows) + r * Mq
+    xr = _f64(x_shards.reshape(P * Mq, D)[g])
+    h_ref = np.empty((P, len(g), Fr), dtype=np.uint16)
+    h_lo = np.empty((P, len(g), Fr))
+    h_hi = np.empty((P, len(g), Fr))
+    s = 0.0
+    t_h = 0.0
+    mag = 0.0
+    for q in range(P):
+        w1 = _f64(W1[q])
+        a = xr @ w1
+        err = 0.0 if _exact_in_fp32(xr, w1) else D * 2.0 ** -24 * (np.abs(xr) @ np.abs(w1))
+        b = _f64(bf16_from_f64(a))
+        h_ref[q] = bf16_from_f64(gelu_tanh(b))
+        b_lo, b_hi = bf16_nearest(a - err), bf16_nearest(a + err)
+        g_lo = np.minimum(gelu_tanh(b_lo), gelu_tanh(b_hi))
+        g_lo = np.where((b_lo < _GELU_ARGMIN) & (b_hi > _GELU_ARGMIN), gelu_tanh(_GELU_ARGMIN), g_lo)
+        g_hi = np.maximum(gelu_tanh(b_lo), gelu_tanh(b_hi))
+        rel = np.maximum(gelu_fp32_rel_error(b_lo), gelu_fp32_rel_error(b_hi))
+        h_lo[q] = bf16_nearest(g_lo - rel * np.abs(g_lo))
+        h_hi[q] = bf16_nearest(g_hi + rel * np.abs(g_hi))
+        hr = _f64(h_ref[q])
+        w2 = np.abs(_f64(W2[q]))
+        s = s + hr @ _f64(W2[q])
+        t_h = t_h + np.maximum(hr - h_lo[q], h_hi[q] - hr) @ w2
+        mag = mag + np.maximum(np.abs(h_lo[q]), np.abs(h_hi[q])) @ w2
+    t = t_h + (Fr + P) * 2.0 ** -24 * mag
+    return h_ref, h_lo, h_hi, s, t

@@ -23,7 +23,9 @@ here, so only shape, type and distribution follow them):
   * bf16 gradient-bucket workload: P = 16, 128 Mi bf16 per rank,
     normal(0, 0.01), seed 3;
   * GEMM + reduce-scatter: P = 4, A_q and B_q bf16 4096 x 4096,
-    normal(0, 1/64), seed 4.
+    normal(0, 1/64), seed 4 (all-gather + GEMM: the same shapes, seed 5);
+  * tensor-parallel MLP layer: P = 4, x [M, 1024], W1 [1024, 16384],
+    W2 [16384, 1024], seed 6 (see mlp_operands).
 
 Two-dimensional per-rank arrays of shape (R, w * P) are stored chunk-major:
 chunk c (a flat, contiguous run of R * w elements) is column block c of the
@@ -152,3 +154,40 @@ def small_int_bf16(rng: np.random.Generator, shape, lo: int = -4, hi: int = 4) -
     """Integer-valued bf16 bit patterns (uniform integers in [lo, hi]); every
     such value is exact in bf16."""
     return bf16_bits(rng.integers(lo, hi, size=shape, endpoint=True).astype(np.float32))
+
+
+SEED_MLP = 6
+
+
+def mlp_operands(P: int = 4, M: int = 8192, D: int = 1024, F: int = 16384, seed: int = SEED_MLP):
+    """Tensor-parallel MLP layer operands as bf16 bit patterns: the layer
+    input's row blocks x (P, M/P, D), the column blocks of W1 (P, D, F/P) and
+    the row blocks of W2 (P, F/P, D) -- the x [tokens, 1024], W1 [1024, 16384],
+    W2 [16384, 1024] shapes of "TPU 与分布式通信原语" (collective matmul) at
+    P = 4, with more tokens.
+
+    x is normal(0, 1) on the grid 2^-4 (clipped to [-4, 4]) and W1 normal(0,
+    1/D) on the grid 2^-10 (clipped to 127 steps), so every product x w is a
+    multiple of 2^-14 and, for D up to 2048, every partial sum of x @ W1 is
+    exact in fp32 whatever the order; W2 is normal(0, 1/F) rounded to bf16.
+    Rank q draws x_q, W1_q and W2_q, in that order, from its own child stream.
+    """
+    Mq, Fr = M // P, F // P
+    x = np.empty((P, Mq, D), dtype=np.uint16)
+    w1 = np.empty((P, D, Fr), dtype=np.uint16)
+    w2 = np.empty((P, Fr, D), dtype=np.uint16)
+    gens = rank_streams(seed, P)
+
+    def draw(q):
+        g = gens[q]
+        a = np.clip(np.rint(g.standard_normal((Mq, D), dtype=np.float32) * 16.0), -64, 64)
+        x[q] = bf16_bits((a / 16.0).astype(np.float32))
+        b = np.clip(np.rint(g.standard_normal((D, Fr), dtype=np.float32) * (1024.0 / np.sqrt(D))),
+                    -127, 127)
+        w1[q] = bf16_bits((b / 1024.0).astype(np.float32))
+        c = g.standard_normal((Fr, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(F))
+        w2[q] = bf16_bits(c)
+
+    with ThreadPoolExecutor(_threads(P)) as ex:
+        list(ex.map(draw, range(P)))
+    return x, w1, w2

@@ -144,3 +144,78 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
     lib = _load_variant(tmp_path, text.replace(old, new, 1), "mutant")
     failed = _run_checks_with(lib, monkeypatch)
     assert failed, "no pin caught the planted mistake '%s'" % name
+
+
+# ---------------------------------------------------------------- the MLP layer
+# The MLP part of the oracle is Python; a mutant is a copy of the package
+# source with one mistake planted, executed as a module of its own and put in
+# place of `oracle` for the MLP pins.
+import importlib.util
+import types
+
+import test_oracle_mlp_pins as mlp
+
+PY_SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+
+PY_MUTANTS = {
+    "gelu cubic coefficient": ("t = 2.0 * _GELU_C * (x + 0.044715 * x * x * x)\n    with",
+                               "t = 2.0 * _GELU_C * (x + 0.04471 * x * x * x)\n    with"),
+    "gelu argument not doubled": ("t = 2.0 * _GELU_C * (x + 0.044715 * x * x * x)\n    with",
+                                  "t = _GELU_C * (x + 0.044715 * x * x * x)\n    with"),
+    "gelu cancels in the tail": ("return x / (1.0 + np.exp(-t))",
+                                 "return 0.5 * x * (1.0 + np.tanh(t / 2.0))"),
+    "product not rounded before gelu": ("h[q] = bf16_from_f64(gelu_tanh(_f64(local0)))",
+                                        "h[q] = bf16_from_f64(gelu_tanh(_f64(full[q]) @ _f64(W1[q])))"),
+    "wrong column block of W1": ("local0 = bf16_from_f64(_f64(full[q]) @ _f64(W1[q]))",
+                                 "local0 = bf16_from_f64(_f64(full[q]) @ _f64(W1[(q + 1) % P]))"),
+    "rank keeps the wrong row block": ("[r * Mq:(r + 1) * Mq]) for r in range(P)])",
+                                       "[((r + 1) % P) * Mq:((r + 1) % P + 1) * Mq]) for r in range(P)])"),
+    "bf16 rounding truncates": ("r = _bf16_grid(v, np.rint).astype(np.float32)",
+                                "r = _bf16_grid(v, np.trunc).astype(np.float32)"),
+    "bf16 subnormal spacing": ("e = np.maximum(e, -125)", "e = np.maximum(e, -126)"),
+}
+
+
+def _mlp_checks():
+    yield "gelu torch", mlp.test_gelu_matches_torch_tanh_form
+    for x in (-12.0, -10.0, -6.0, -0.75, 1.0, 3.0):
+        yield "gelu decimal %g" % x, lambda x=x: mlp.test_gelu_against_decimal_literal_formula(x)
+    yield "gelu identities", mlp.test_gelu_identities
+    yield "bf16 vs torch", mlp.test_bf16_from_f64_matches_torch_on_fp32_values
+    yield "bf16 one rounding", mlp.test_bf16_from_f64_is_one_rounding
+    yield "bf16 nearest", mlp.test_nearest_is_monotone_and_within_half_a_step
+    for P in (1, 2, 3, 4):
+        yield "unsharded P=%d" % P, lambda P=P: mlp.test_layer_equals_unsharded_computation(P)
+    yield "brute force", mlp.test_layer_brute_force_tiny
+
+
+def _py_variant(text):
+    spec = importlib.util.spec_from_loader("oracle_mutant", loader=None)
+    mod = types.ModuleType(spec.name)
+    mod.__file__ = PY_SRC   # the C library is found next to it, as for the real package
+    exec(compile(text, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _run_mlp_checks_with(mod, monkeypatch):
+    monkeypatch.setattr(mlp, "oracle", mod)
+    failed = []
+    for label, check in _mlp_checks():
+        try:
+            check()
+        except (AssertionError, ValueError):
+            failed.append(label)
+    return failed
+
+
+def test_unmodified_python_source_passes(monkeypatch):
+    assert _run_mlp_checks_with(_py_variant(open(PY_SRC).read()), monkeypatch) == []
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_python_mutant_is_caught(name, monkeypatch):
+    old, new = PY_MUTANTS[name]
+    text = open(PY_SRC).read()
+    assert old in text, "mutation site not found: %s" % name
+    failed = _run_mlp_checks_with(_py_variant(text.replace(old, new, 1)), monkeypatch)
+    assert failed, "no pin caught the planted mistake '%s'" % name
