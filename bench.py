@@ -45,6 +45,9 @@ WORKLOADS = {
     # B_q bf16 4096 x 4096, normal(0, 1/64)
     "ag_gemm_p4_4096": dict(op="ag_gemm", P=4, M=4096, N=4096, K=4096, kind="bf16", seed=5,
                             std=1.0 / 64, n=4096 * 4096),
+    # one tensor-parallel MLP layer: P = 4, x [8192, 1024] in row blocks of
+    # 2048 tokens, W1 [1024, 16384] by columns, W2 [16384, 1024] by rows
+    "tp_mlp_p4_8192": dict(op="tp_mlp", P=4, M=8192, D=1024, F=16384, kind="bf16", seed=6),
     # a plain copy of known size (2 x 256 MiB read + written): counter calibration
     "ppermute_f32_p2_64Mi": dict(op="ppermute", P=2, n=64 << 20, kind="f32", seed=2, std=1.0),
     # reduce-scatter alone on the headline inputs: one-way ring, and the
@@ -93,10 +96,21 @@ def moved_bytes(op: str, P: int, n: int, kind: str) -> int:
     return rs + ag
 
 
+def mlp_layer_cost(P: int, M: int, D: int, F: int) -> dict:
+    """Cost model of one tensor-parallel MLP layer ("TPU 与分布式通信原语",
+    collective matmul: the all-gather-matmul and the matmul-reduce-scatter of
+    one device take the same flops; a device sends P - 1 shards one way)."""
+    per = 2 * M * D * (F // P)
+    shard = (M // P) * D * 2
+    return {"flop_per_matmul_per_rank": per, "flop": 2 * P * per, "shard_bytes": shard,
+            "ring_bytes_per_direction": (P - 1) * shard}
+
+
 KERNEL_SOURCE = {"ring_step_kernel": ("ring_kernels.hip",), "copy_kernel_tab": ("ring_kernels.hip",),
                  "ring_bidir_kernel": ("ring_kernels.hip",), "ring_psum_kernel": ("ring_kernels.hip",),
                  "gemm_rs_kernel": ("gemm_rs.hip", "gemm_core.h"),
-                 "ag_gemm_kernel": ("ag_gemm.hip", "gemm_core.h")}
+                 "ag_gemm_kernel": ("ag_gemm.hip", "gemm_core.h"),
+                 "tp_mlp_layer": ("tp_mlp.hip", "ag_gemm.hip", "gemm_rs.hip", "gemm_core.h")}
 
 
 KERNEL_HEADERS = ("ring_device.h", "ring_internal.h")
@@ -293,6 +307,101 @@ def _gemm_main(args, w):
     print(json.dumps(line), flush=True)
 
 
+def _mlp_main(args, w):
+    """One tensor-parallel MLP layer (two launches: all-gather + GEMM with the
+    gelu epilogue, GEMM + reduce-scatter with the bf16 epilogue): TFLOP/s of
+    both products against the bf16 MFMA peak."""
+    import numpy as np
+    import torch
+    from ring_collectives_amd import collectives as rc
+    from ring_collectives_amd import inputs
+    from ring_collectives_amd import _native as N
+    P, M, D, F = w["P"], w["M"], w["D"], w["F"]
+    Mq, Fr = M // P, F // P
+    print("[bench] workload %s: generating inputs" % args.workload, file=sys.stderr, flush=True)
+    x, w1, w2 = inputs.mlp_operands(P, M, D, F, seed=w["seed"])
+    torch.cuda.set_device(0)
+    dev = lambda a: [torch.from_numpy(a[q].view(np.int16)).cuda().view(torch.bfloat16) for q in range(P)]
+    xs, W1, W2 = dev(x), dev(w1), dev(w2)
+    bf = torch.bfloat16
+    full = [torch.empty((M, D), dtype=bf, device="cuda") for _ in range(P)]
+    h = [torch.empty((M, Fr), dtype=bf, device="cuda") for _ in range(P)]
+    out = [torch.empty((Mq, D), dtype=bf, device="cuda") for _ in range(P)]
+    ws = rc.tp_mlp_workspace(P, M, D, F)
+
+    def step():
+        rc.tp_mlp_layer(xs, W1, W2, full, h, out, ws=ws)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    code, info = rc.last_error(ws)
+    if code != 0:
+        raise SystemExit("tp_mlp_layer reported %s (info %#x)" % (N.strerror(code), info))
+    kern_ms = [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    avg = sum(kern_ms) / len(kern_ms)
+    cost = mlp_layer_cost(P, M, D, F)
+    flop = cost["flop"]
+    print("[bench] %d steps: %.4f ms/step (wall), layer avg %.4f ms" % (args.steps, ms_step, avg),
+          file=sys.stderr, flush=True)
+    cpu = None
+    parity = None
+    if not args.no_cpu:
+        import oracle
+        rows = np.arange(0, Mq, Mq // 8)                      # 8 sampled tokens per rank
+        gf = [t_.view(torch.int16).cpu().numpy().view(np.uint16) for t_ in full]
+        gh = [t_.view(torch.int16).cpu().numpy().view(np.uint16) for t_ in h]
+        go = [t_.view(torch.int16).cpu().numpy().view(np.uint16) for t_ in out]
+        same = all(np.array_equal(g_, x.reshape(M, D)) for g_ in gf)
+        ok_h = ok_o = True
+        t = time.perf_counter()
+        for r in range(P):
+            _, lo, hi, s_, t_ = oracle.tp_mlp_bounds(x, w1, w2, r, rows)
+            for q in range(P):
+                hv = oracle.bf16_to_f32(gh[q][r * Mq + rows]).astype(np.float64)
+                ok_h &= bool(np.all((lo[q] <= hv) & (hv <= hi[q])))
+            ov = oracle.bf16_to_f32(go[r][rows]).astype(np.float64)
+            ok_o &= bool(np.all((oracle.bf16_nearest(s_ - t_) <= ov) & (ov <= oracle.bf16_nearest(s_ + t_))))
+        dt = time.perf_counter() - t
+        sflop = P * (2.0 * P * len(rows) * D * Fr * 2)
+        cpu = {"value": round(sflop / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle", "seconds": round(dt, 3),
+               "sample": "%d tokens per rank: both products of every rank at those rows, fp64 "
+                         "(NumPy BLAS), with the bf16 roundings and gelu" % len(rows)}
+        parity = bool(same and ok_h and ok_o)
+        print("[bench] gathered x exact: %s, sampled h in bounds: %s, sampled out in bounds: %s"
+              % (same, ok_h, ok_o), file=sys.stderr, flush=True)
+    line = {
+        "metric": "tensor-parallel MLP layer TFLOP/s, P=%d virtual ranks, bf16 x[%d,%d] W1[%d,%d] W2[%d,%d]"
+                  % (P, M, D, D, F, F, D),
+        "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 (f32 accumulate)", "data": "synthetic",
+        "config": {"workload": args.workload, "P": P, "tokens": M, "d_model": D, "d_hidden": F,
+                   "flop_per_step": flop, "parallelism": "P virtual ranks on 1 GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(flop / (avg * 1e-3) / 1e12, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flop / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": _traffic(args.workload, "tp_mlp_layer"),
+                     "kernel": "tp_mlp_layer (ag_gemm_kernel + gemm_rs_kernel)",
+                     "kernel_ms_avg": round(avg, 5)},
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +423,8 @@ def main():
     w = WORKLOADS[args.workload]
     if w["op"] in ("gemm_rs", "ag_gemm"):
         return _gemm_main(args, w)
+    if w["op"] == "tp_mlp":
+        return _mlp_main(args, w)
     P, n, kind = w["P"], w["n"], w["kind"]
     print("[bench] workload %s: generating inputs" % args.workload, file=sys.stderr, flush=True)
     x = _make_inputs(w)

@@ -224,6 +224,39 @@ int all_gather_gemm(const void *const *A_shard, const void *const *B, void *cons
                     void *stream);
 
 /*
+ * One tensor-parallel MLP layer, out = ReduceScatter(gelu(AllGather(x) @ W1_r)
+ * @ W2_r) ("TPU 与分布式通信原语", collective matmul: the tensor-parallel
+ * X = gelu(X @ W1) @ W2 with W1 split by columns and W2 by rows, and the
+ * multi-layer form in which each layer starts from the previous layer's
+ * shard).  gelu is the tanh form, 0.5 x (1 + tanh(sqrt(2/pi)(x + 0.044715
+ * x^3))); as on that page the first product is rounded to bf16 before gelu
+ * and gelu's result to bf16 before the second product.
+ *
+ * Shapes: M tokens, model width D, hidden width F (all ranks together).
+ * x_shard[r]: bf16 (M / P) x D, rows [r M/P, (r+1) M/P) of the layer input.
+ * W1[r]: bf16 D x (F / P), column block r of W1.  W2[r]: bf16 (F / P) x D,
+ * row block r of W2.  Written: x_full[r] (bf16 M x D, the gathered input),
+ * h[r] (bf16 M x (F / P), bf16(gelu(bf16(x_full[r] @ W1[r])))), and
+ * out_shard[r] (bf16 (M / P) x D): rows [r M/P, (r+1) M/P) of
+ * sum_q h[q] @ W2[q], accumulated in fp32 (products on the matrix cores, the
+ * sum over ranks in the ring reduce-scatter's order) and rounded once.
+ * Runs as two launches on `stream`: all_gather_gemm with the gelu epilogue,
+ * then gemm_reduce_scatter with a bf16 epilogue.  out_shard may be the same
+ * memory as x_shard (a layer in place); h must not overlap any input, x_full
+ * or another h; out_shard must not overlap h or W2; none may overlap ws.
+ * ws: at least tp_mlp_workspace_bytes(P, M, D, F) bytes, 256-byte aligned,
+ * zeroed once; ring_last_error reports a watchdog timeout of either launch.
+ * Shapes this version accepts: M % (256 P) == 0, D % 128 == 0,
+ * F % (128 P) == 0.
+ */
+int tp_mlp_layer(const void *const *x_shard, const void *const *W1, const void *const *W2,
+                 void *const *x_full, void *const *h, void *const *out_shard, int P, int M, int D,
+                 int F, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes of tp_mlp_layer; 0 for invalid or unsupported shapes. */
+size_t tp_mlp_workspace_bytes(int P, int M, int D, int F);
+
+/*
  * Synchronises `stream` and returns the error word a kernel left in `ws`
  * (RING_OK if none).  If info is not NULL it receives the stuck rank, round
  * and tile packed as rank | round << 8 | tile << 16 (tile saturates).

@@ -36,6 +36,8 @@ SIGNATURES = {
     "ring_all_reduce": (_i, [_pp, _pp, _i, _sz, _i, _vp, _sz, _vp]),
     "gemm_reduce_scatter": (_i, [_pp, _pp, _pp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "all_gather_gemm": (_i, [_pp, _pp, _pp, _pp, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "tp_mlp_layer": (_i, [_pp, _pp, _pp, _pp, _pp, _pp, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "tp_mlp_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "ring_last_error": (_i, [_vp, _sz, _vp, ctypes.POINTER(ctypes.c_int)]),
     "ring_strerror": (ctypes.c_char_p, [_i]),
 }

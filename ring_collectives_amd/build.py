@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["ring_api.hip", "ring_kernels.hip", "gemm_rs.hip", "ag_gemm.hip"]
+SOURCES = ["ring_api.hip", "ring_kernels.hip", "gemm_rs.hip", "ag_gemm.hip", "tp_mlp.hip"]
 LIB = os.path.join(HERE, "libring_collectives.so")
 ARCH = os.environ.get("RING_OFFLOAD_ARCH", "gfx950")
 

@@ -178,6 +178,38 @@ def all_gather_gemm(A_shard, B, A_full, C, ws=None, stream=None):
     return ws
 
 
+def tp_mlp_workspace(P: int, M: int, D: int, F: int, device=None) -> torch.Tensor:
+    """A zero-filled workspace for tp_mlp_layer at these shapes."""
+    nb = int(N.lib().tp_mlp_workspace_bytes(P, M, D, F))
+    return torch.zeros(max(nb, 256), dtype=torch.uint8, device=device if device is not None else "cuda")
+
+
+def tp_mlp_layer(x_shard, W1, W2, x_full, h, out, ws=None, stream=None):
+    """One tensor-parallel MLP layer over P virtual ranks (bf16 everywhere):
+    x_full[r] <- the row blocks x_shard[0..P-1] stacked (ring all-gather);
+    h[r] <- bf16(gelu(bf16(x_full[r] @ W1[r]))) (tanh gelu);
+    out[r] <- bf16(rows [r M/P, (r+1) M/P) of sum_q h[q] @ W2[q]), fp32 sums.
+    W1[r] is column block r of W1 (D x F/P), W2[r] row block r of W2
+    (F/P x D).  out may be x_shard itself (a layer in place)."""
+    P = len(x_shard)
+    Mq, D = x_shard[0].shape
+    D2, Fr = W1[0].shape
+    M, F = Mq * P, Fr * P
+    if D2 != D or tuple(W2[0].shape) != (Fr, D) or not (len(W1) == len(W2) == len(x_full) == len(h) ==
+                                                          len(out) == P):
+        raise ValueError("tp_mlp_layer: shape mismatch")
+    bf = torch.bfloat16
+    ptrs = [_ranks(x_shard, "tp_mlp_layer", Mq * D, bf), _ranks(W1, "tp_mlp_layer", D * Fr, bf),
+            _ranks(W2, "tp_mlp_layer", Fr * D, bf), _ranks(x_full, "tp_mlp_layer", M * D, bf),
+            _ranks(h, "tp_mlp_layer", M * Fr, bf), _ranks(out, "tp_mlp_layer", Mq * D, bf)]
+    if ws is None:
+        ws = tp_mlp_workspace(P, M, D, F, device=x_shard[0].device)
+    arrs = [N.ptr_array(p_) for p_ in ptrs]
+    N.check(N.lib().tp_mlp_layer(*[a_ for a_, _ in arrs], P, M, D, F, ws.data_ptr(), ws.numel(),
+                                 _stream(stream)), "tp_mlp_layer")
+    return ws
+
+
 def last_error(ws: torch.Tensor, stream=None):
     """(code, info) left in a workspace by the last kernel (synchronises)."""
     import ctypes

@@ -42,7 +42,7 @@ struct AgGemmParams {
     const unsigned short* As[RING_MAX_RANKS];   // rank q's block of A, (M / P) x K
     const unsigned short* B[RING_MAX_RANKS];    // K x N
     unsigned short* Af[RING_MAX_RANKS];         // gathered A, M x K
-    float* C[RING_MAX_RANKS];                   // M x N fp32
+    void* C[RING_MAX_RANKS];                    // M x N: fp32, or bf16 (the MLP's activation)
     int* flags;                                 // [P phases][P ranks][tpc], kFlagStride apart
     int* done;                                  // workgroups finished (clears the flags)
     Status* status;
@@ -54,6 +54,7 @@ struct AgGemmParams {
     int groups;                                 // workgroups per rank
     int nflags;                                 // flags in the table
     int drop_round;                             // test hook: rank 0 never flags this phase (0 = off)
+    int gelu_bf16;                              // C is bf16(gelu(bf16(product))), else fp32
 };
 
 constexpr size_t kDoneOffset = 64;   // the finish counter, inside the status block
@@ -147,8 +148,13 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
                 gemm_tile<G, POL_DEV>(p.K, p.N, p.Af[q], p.B[q], c * p.tm_chunk + pr, tc, acc, lds, lane,
                                       wave, wr, wc);
             }
-            float* ob = p.C[q] + ((size_t)c * Mc + pr * kBM + wr * kWM) * p.N + tc * BN + wc * G::WN;
-            store_part_rowmajor<G, false>(acc, tile_view(nullptr, 0), ob, p.N, lds, lane, wave);
+            const size_t at = ((size_t)c * Mc + pr * kBM + wr * kWM) * p.N + tc * BN + wc * G::WN;
+            if (p.gelu_bf16)
+                store_part_rowmajor<G, false, EPI_GELU_BF16>(acc, tile_view(nullptr, 0), (char*)p.C[q] + at * 2,
+                                                             p.N, lds, lane, wave);
+            else
+                store_part_rowmajor<G, false, EPI_F32>(acc, tile_view(nullptr, 0), (char*)p.C[q] + at * 4, p.N,
+                                                       lds, lane, wave);
         }
     }
 }
@@ -217,18 +223,13 @@ static int launch_ag_gemm(AgGemmParams& prm, const DevInfo& di, hipStream_t stre
     return hipGetLastError() == hipSuccess ? RING_OK : RING_EHIP;
 }
 
-}  // namespace ringc
-
-using namespace ringc;
-
 static bool ag_overlap(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
 }
 
-extern "C" int all_gather_gemm(const void* const* A_shard, const void* const* B, void* const* A_full,
-                               void* const* C, int P, int M, int N, int K, void* ws, size_t ws_bytes,
-                               void* stream) {
+int ag_gemm_run(const void* const* A_shard, const void* const* B, void* const* A_full, void* const* C,
+                int P, int M, int N, int K, void* ws, size_t ws_bytes, void* stream, int gelu_bf16) {
     if (P < 1 || P > RING_MAX_RANKS || M < 0 || N < 0 || K < 0) return RING_EINVAL;
     if (!A_shard || !B || !A_full || !C) return RING_EINVAL;
     if (M == 0 || N == 0) return RING_OK;
@@ -255,7 +256,7 @@ extern "C" int all_gather_gemm(const void* const* A_shard, const void* const* B,
         prm.As[r] = (const unsigned short*)A_shard[r];
         prm.B[r] = (const unsigned short*)B[r];
         prm.Af[r] = (unsigned short*)A_full[r];
-        prm.C[r] = (float*)C[r];
+        prm.C[r] = C[r];
     }
     prm.status = (Status*)ws;
     prm.done = (int*)((char*)ws + kDoneOffset);
@@ -276,6 +277,15 @@ extern "C" int all_gather_gemm(const void* const* A_shard, const void* const* B,
         bn = (N % 256 == 0 && wide_tiles >= (long long)(di.cus / P)) ? 256 : 128;
     }
     if (bn == 256 && N % 256) return RING_EUNSUPPORTED;
-    return bn == 256 ? launch_ag_gemm<Geo<256, 8>>(prm, di, (hipStream_t)stream)
-                     : launch_ag_gemm<Geo<128, 4>>(prm, di, (hipStream_t)stream);
+    prm.gelu_bf16 = gelu_bf16 ? 1 : 0;
+    const hipStream_t st = (hipStream_t)stream;
+    return bn == 256 ? launch_ag_gemm<Geo<256, 8>>(prm, di, st) : launch_ag_gemm<Geo<128, 4>>(prm, di, st);
+}
+
+}  // namespace ringc
+
+extern "C" int all_gather_gemm(const void* const* A_shard, const void* const* B, void* const* A_full,
+                               void* const* C, int P, int M, int N, int K, void* ws, size_t ws_bytes,
+                               void* stream) {
+    return ringc::ag_gemm_run(A_shard, B, A_full, C, P, M, N, K, ws, ws_bytes, stream, 0);
 }

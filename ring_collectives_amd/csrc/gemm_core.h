@@ -265,14 +265,49 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
 }
 
 
+// GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))),
+// the default of jax.nn.gelu, which the tensor-parallel MLP of "TPU 与分布式
+// 通信原语" (collective matmul) applies.  Since 1 + tanh(z) = 2 sigmoid(2z) it
+// is evaluated as x sigmoid(2z) in fp32, which stays accurate in the negative
+// tail where 1 + tanh(z) would cancel; the exponential only ever sees a
+// non-positive argument, so it cannot overflow.
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float t = 1.5957691216057308f * (x + 0.044715f * x * x * x);   // 2 sqrt(2/pi) (...)
+    const float e = expf(-fabsf(t));
+    const float sig = (t >= 0.0f ? 1.0f : e) / (1.0f + e);
+    return x * sig;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ unsigned bf16_rne_bits(float f) {
+    unsigned u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Output element of the row-major store: the fp32 sum itself, its bf16
+// rounding, or bf16(gelu(bf16(x))) -- the MLP's first layer rounds the
+// product to bf16 before the activation and the activation to bf16 after.
+enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_GELU_BF16 = 2 };
+
+template <int EPI>
+__device__ __forceinline__ unsigned epi_bf16(unsigned v) {
+    unsigned b = bf16_rne_bits(__uint_as_float(v));
+    if constexpr (EPI == EPI_GELU_BF16) b = bf16_rne_bits(gelu_tanh(__uint_as_float(b << 16)));
+    return b;
+}
+
 // Store a wave's part of a finished tile row-major: element (i, j) of the
-// part goes to ob[i * ld + j].  With ADD, the same part of another tile,
-// kept in fragment order at rv, is added first (device-scope loads).  Each
-// wave turns its part around in its own slice of LDS (free after the K
-// loop), 32 rows at a time, and writes whole row segments.
-template <class G, bool ADD>
-__device__ __forceinline__ void store_part_rowmajor(const f32x16 (&acc)[kMI][G::NI], rsrc_t rv, float* ob,
+// part goes to ob[i * ld + j], fp32 for EPI_F32 and bf16 otherwise.  With
+// ADD, the same part of another tile, kept in fragment order at rv, is added
+// first (device-scope loads), in fp32, before any rounding.  Each wave turns
+// its part around in its own slice of LDS (free after the K loop), 32 rows
+// at a time, and writes whole row segments.
+template <class G, bool ADD, int EPI = EPI_F32>
+__device__ __forceinline__ void store_part_rowmajor(const f32x16 (&acc)[kMI][G::NI], rsrc_t rv, void* ob,
                                                     int ld, unsigned short* lds, int lane, int wave) {
+    constexpr int OSZ = EPI == EPI_F32 ? 4 : 2;   // bytes per output element
     // per-lane offsets laundered through empty asm so they are recomputed
     // here rather than kept alive across the K loop
     unsigned lane16 = (unsigned)lane * 16u;
@@ -285,8 +320,8 @@ __device__ __forceinline__ void store_part_rowmajor(const f32x16 (&acc)[kMI][G::
     int lds_row = wave * G::kEpiWave + (lane / VPR) * G::kEpiStride + (lane % VPR) * 4;
     asm volatile("" : "+v"(lds_row));
     const float* gather_lane = reinterpret_cast<const float*>(lds) + lds_row;
-    const rsrc_t ov = tile_view(ob, ((long long)(kWM - 1) * ld + G::WN) * 4);
-    unsigned lane_out = (unsigned)(((lane / VPR) * ld + (lane % VPR) * 4) * 4);
+    const rsrc_t ov = tile_view(ob, ((long long)(kWM - 1) * ld + G::WN) * OSZ);
+    unsigned lane_out = (unsigned)(((lane / VPR) * ld + (lane % VPR) * 4) * OSZ);
     asm volatile("" : "+v"(lane_out));
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi) {
@@ -312,7 +347,15 @@ __device__ __forceinline__ void store_part_rowmajor(const f32x16 (&acc)[kMI][G::
 #pragma unroll
         for (int i = 0; i < 32 / RPS; ++i) {
             const u32x4 o = *(const u32x4*)(gather_lane + RPS * i * G::kEpiStride);
-            st16<POL_PLAIN>(o, ov, lane_out + (unsigned)(((mi * 32 + RPS * i) * ld) * 4));
+            const unsigned at = lane_out + (unsigned)(((mi * 32 + RPS * i) * ld) * OSZ);
+            if constexpr (EPI == EPI_F32) {
+                st16<POL_PLAIN>(o, ov, at);
+            } else {
+                u32x2 h;
+                h[0] = epi_bf16<EPI>(o[0]) | (epi_bf16<EPI>(o[1]) << 16);
+                h[1] = epi_bf16<EPI>(o[2]) | (epi_bf16<EPI>(o[3]) << 16);
+                st8<POL_PLAIN>(h, ov, at);
+            }
         }
     }
 }

@@ -48,7 +48,7 @@ namespace ringc {
 struct GemmParams {
     const unsigned short* A[RING_MAX_RANKS];   // bf16 M x K, row-major
     const unsigned short* B[RING_MAX_RANKS];   // bf16 K x N, row-major
-    float* out[RING_MAX_RANKS];                // fp32 (M / P) x N, row-major
+    void* out[RING_MAX_RANKS];                 // (M / P) x N row-major, fp32 or bf16
     float* work;                               // P x (M x N) fp32, tiles in fragment order
     int* flags;                                // [P-1][P][tpc][4] flags
     Status* status;
@@ -58,6 +58,7 @@ struct GemmParams {
     int tn;                                    // tile columns (N / BN)
     int tpc;                                   // tiles per chunk
     int groups;                                // rings of workgroups (gridDim.x / P)
+    int out_bf16;                              // out is bf16 (the fp32 sum rounded once)
 };
 
 template <class G>
@@ -143,11 +144,19 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
                 }
                 signal_flag(gflag<G>(p, phase, q, pos, wave), lane);
             } else {
-                // Final sum of chunk q, row-major into out[q].
+                // Final sum of chunk q, row-major into out[q]: fp32, or
+                // rounded once to bf16.
                 const int lrow0 = (tr - q * p.tm_chunk) * kBM + wr * kWM;
-                float* ob = p.out[q] + (size_t)lrow0 * p.N + tc * BN + wc * G::WN;
-                if (phase > 0) store_part_rowmajor<G, true>(acc, rv, ob, p.N, lds, lane, wave);
-                else store_part_rowmajor<G, false>(acc, rv, ob, p.N, lds, lane, wave);
+                const size_t at = (size_t)lrow0 * p.N + tc * BN + wc * G::WN;
+                if (p.out_bf16) {
+                    char* ob = (char*)p.out[q] + at * 2;
+                    if (phase > 0) store_part_rowmajor<G, true, EPI_BF16>(acc, rv, ob, p.N, lds, lane, wave);
+                    else store_part_rowmajor<G, false, EPI_BF16>(acc, rv, ob, p.N, lds, lane, wave);
+                } else {
+                    char* ob = (char*)p.out[q] + at * 4;
+                    if (phase > 0) store_part_rowmajor<G, true, EPI_F32>(acc, rv, ob, p.N, lds, lane, wave);
+                    else store_part_rowmajor<G, false, EPI_F32>(acc, rv, ob, p.N, lds, lane, wave);
+                }
             }
         }
     }
@@ -199,13 +208,11 @@ static int launch_gemm_rs(GemmParams& prm, const DevInfo& di, hipStream_t stream
     return hipGetLastError() == hipSuccess ? RING_OK : RING_EHIP;
 }
 
-}  // namespace ringc
-
-using namespace ringc;
-
-extern "C" int gemm_reduce_scatter(const void* const* A, const void* const* B, void* const* out,
-                                   int P, int M, int N, int K, void* ws, size_t ws_bytes,
-                                   void* stream) {
+// The status word sits at ws; the flag table and the partial tiles start
+// region_off bytes later than in a call of its own (the MLP layer puts them
+// behind the all-gather's flags).
+int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, int P, int M, int N, int K,
+                void* ws, size_t ws_bytes, void* stream, int out_bf16, size_t region_off) {
     if (P < 1 || P > RING_MAX_RANKS || M < 0 || N < 0 || K < 0) return RING_EINVAL;
     if (!A || !B || !out) return RING_EINVAL;
     if (M == 0 || N == 0) return RING_OK;
@@ -215,15 +222,18 @@ extern "C" int gemm_reduce_scatter(const void* const* A, const void* const* B, v
         if (((uintptr_t)A[r] | (uintptr_t)B[r] | (uintptr_t)out[r]) & 15) return RING_EINVAL;
     }
     const size_t MN = (size_t)M * N;
-    const GemmWs lay = gemm_ws_layout(P, MN);
-    if (!ws || ((uintptr_t)ws & 255) || ws_bytes < lay.total) return RING_EWORKSPACE;
+    GemmWs lay = gemm_ws_layout(P, MN);
+    lay.flags_off += region_off;
+    lay.work_off += region_off;
+    lay.total += region_off;
+    if (!ws || ((uintptr_t)ws & 255) || (region_off & 255) || ws_bytes < lay.total) return RING_EWORKSPACE;
 
     GemmParams prm;
     memset(&prm, 0, sizeof prm);
     for (int r = 0; r < P; ++r) {
         prm.A[r] = (const unsigned short*)A[r];
         prm.B[r] = (const unsigned short*)B[r];
-        prm.out[r] = (float*)out[r];
+        prm.out[r] = out[r];
     }
     prm.work = (float*)((char*)ws + lay.work_off);
     prm.flags = (int*)((char*)ws + lay.flags_off);
@@ -245,6 +255,15 @@ extern "C" int gemm_reduce_scatter(const void* const* A, const void* const* B, v
         bn = (N % 256 == 0 && wide_tiles >= (long long)(di.cus / P)) ? 256 : 128;
     }
     if (bn == 256 && N % 256) return RING_EUNSUPPORTED;
-    return bn == 256 ? launch_gemm_rs<Geo<256, 8>>(prm, di, (hipStream_t)stream)
-                     : launch_gemm_rs<Geo<128, 4>>(prm, di, (hipStream_t)stream);
+    prm.out_bf16 = out_bf16 ? 1 : 0;
+    const hipStream_t st = (hipStream_t)stream;
+    return bn == 256 ? launch_gemm_rs<Geo<256, 8>>(prm, di, st) : launch_gemm_rs<Geo<128, 4>>(prm, di, st);
+}
+
+}  // namespace ringc
+
+extern "C" int gemm_reduce_scatter(const void* const* A, const void* const* B, void* const* out,
+                                   int P, int M, int N, int K, void* ws, size_t ws_bytes,
+                                   void* stream) {
+    return ringc::gemm_rs_run(A, B, out, P, M, N, K, ws, ws_bytes, stream, 0, 0);
 }

@@ -1,0 +1,260 @@
+"""GPU parity of the tensor-parallel MLP layer against the CPU oracle
+("TPU 与分布式通信原语", collective matmul: out_shard = ReduceScatter(
+gelu(AllGather(x_shard) @ W1_i) @ W2_i)), through the C ABI.
+
+The gathered input must equal the oracle's ring all-gather bit for bit.  The
+products are accumulated by the matrix cores in an order the hardware fixes
+and gelu is evaluated in fp32, so:
+  * on integer-valued operands whose every partial sum is exact in fp32, h
+    and the output are compared bit for bit;
+  * on the workload's inputs (x and W1 on fixed-point grids, which makes the
+    first product exact) every h must lie in the oracle's interval -- one
+    value except where gelu's fp32 evaluation error reaches a bf16 rounding
+    boundary -- and every output in [bf16(s - t), bf16(s + t)] with s the
+    fp64 sum and t the fp32 error bound of the second product and the ring
+    sum (oracle.tp_mlp_bounds).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_collectives_amd import _native as N
+from ring_collectives_amd import collectives as rc
+from ring_collectives_amd import inputs
+
+from _gpu_helpers import note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    N.lib()
+    yield
+
+
+@pytest.fixture(autouse=True)
+def _default_tuning():
+    old = N.get_tuning()
+    yield
+    N.set_tuning(**old)
+
+
+@pytest.fixture(params=[128, 256])
+def tile_n(request):
+    N.set_tuning(gemm_tile_n=request.param)
+    return request.param
+
+
+def _dev(a):
+    return [torch.from_numpy(np.ascontiguousarray(a[q]).view(np.int16)).cuda().view(torch.bfloat16)
+            for q in range(a.shape[0])]
+
+
+def _host(ts):
+    return np.stack([t.view(torch.int16).cpu().numpy().view(np.uint16) for t in ts])
+
+
+def _nan_bf16(shape):
+    return torch.full(shape, 0x7FC1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+def _run(x, w1, w2, ws=None, out=None):
+    P, Mq, D = x.shape
+    Fr = w1.shape[2]
+    M = Mq * P
+    xs, W1, W2 = _dev(x), _dev(w1), _dev(w2)
+    full = [_nan_bf16((M, D)) for _ in range(P)]
+    h = [_nan_bf16((M, Fr)) for _ in range(P)]
+    out = [_nan_bf16((Mq, D)) for _ in range(P)] if out is None else out
+    ws = rc.tp_mlp_layer(xs, W1, W2, full, h, out, ws=ws)
+    torch.cuda.synchronize()
+    assert rc.last_error(ws)[0] == 0
+    return _host(full), _host(h), _host(out), ws
+
+
+def _int_operands(P, M, D, F, seed):
+    """x rows with three ones, W1 in {0, 1}: x @ W1 in {0..3}, so h is one of
+    bf16(gelu(0..3)) = 0, 215/256, 250/128, 3; W2 in {-1, 0, 1}: every
+    partial sum of the second product and of the ring is a multiple of 2^-8
+    below 2^16 in magnitude, exact in fp32."""
+    rng = np.random.default_rng(seed)
+    Mq, Fr = M // P, F // P
+    x = np.zeros((P, Mq, D), dtype=np.float32)
+    for q in range(P):
+        for i in range(Mq):
+            x[q, i, rng.choice(D, size=3, replace=False)] = 1.0
+    w1 = rng.integers(0, 1, size=(P, D, Fr), endpoint=True).astype(np.float32)
+    w2 = rng.integers(-1, 1, size=(P, Fr, D), endpoint=True).astype(np.float32)
+    assert F * 3 * 256 < 2 ** 24
+    return inputs.bf16_bits(x), inputs.bf16_bits(w1), inputs.bf16_bits(w2)
+
+
+@pytest.mark.parametrize("P,M,D,F", [(1, 256, 128, 128), (2, 512, 256, 256), (4, 1024, 128, 512),
+                                     (3, 768, 384, 384), (4, 2048, 256, 1024)])
+def test_integer_valued_exact(P, M, D, F, tile_n):
+    if tile_n == 256 and (D % 256 or (F // P) % 256):
+        pytest.skip("256-wide tiles need both products' N % 256 == 0")
+    note("tp_mlp integer P=%d M=%d D=%d F=%d tile_n=%d" % (P, M, D, F, tile_n))
+    x, w1, w2 = _int_operands(P, M, D, F, seed=600 + P)
+    gf, gh, go, _ = _run(x, w1, w2)
+    full, h, out = oracle.tp_mlp_layer(x, w1, w2)
+    np.testing.assert_array_equal(gf, full)
+    np.testing.assert_array_equal(gh, h)
+    np.testing.assert_array_equal(go, out)
+
+
+def _check_bounds(x, w1, w2, gh, go, ranks_rows):
+    P, Mq, _ = x.shape
+    ambiguous = 0
+    total = 0
+    for r, rows in ranks_rows:
+        _, lo, hi, s, t = oracle.tp_mlp_bounds(x, w1, w2, r, rows)
+        for q in range(P):
+            hv = oracle.bf16_to_f32(gh[q][r * Mq + rows]).astype(np.float64)
+            bad = ~((lo[q] <= hv) & (hv <= hi[q]))
+            assert not bad.any(), "h of rank %d, rows of block %d: %d outside" % (q, r, int(bad.sum()))
+            ambiguous += int(np.count_nonzero(lo[q] != hi[q]))
+            total += lo[q].size
+        ov = oracle.bf16_to_f32(go[r][rows]).astype(np.float64)
+        lo_o, hi_o = oracle.bf16_nearest(s - t), oracle.bf16_nearest(s + t)
+        bad = ~((lo_o <= ov) & (ov <= hi_o))
+        assert not bad.any(), "out of rank %d: %d outside" % (r, int(bad.sum()))
+    # the check is tight: h has one admissible value almost everywhere
+    assert ambiguous <= 0.01 * total, (ambiguous, total)
+
+
+@pytest.mark.parametrize("P,M,D,F", [(2, 512, 256, 512), (4, 1024, 512, 1024), (3, 768, 128, 768)])
+def test_grid_inputs_within_bounds(P, M, D, F, tile_n):
+    if tile_n == 256 and (D % 256 or (F // P) % 256):
+        pytest.skip("256-wide tiles need both products' N % 256 == 0")
+    note("tp_mlp grid P=%d M=%d D=%d F=%d tile_n=%d" % (P, M, D, F, tile_n))
+    x, w1, w2 = inputs.mlp_operands(P, M, D, F, seed=610 + P)
+    gf, gh, go, _ = _run(x, w1, w2)
+    full, h, out = oracle.tp_mlp_layer(x, w1, w2)
+    np.testing.assert_array_equal(gf, full)
+    Mq = M // P
+    _check_bounds(x, w1, w2, gh, go, [(r, np.arange(Mq)) for r in range(P)])
+    # and mostly the oracle's own bits
+    assert np.mean(gh == h) > 0.99
+    assert np.mean(go == out) > 0.9
+
+
+def test_gelu_epilogue_over_its_range():
+    """One rank, x = e_k scaled: row i of x @ W1 is row k of W1, which holds
+    every multiple of 2^-6 in [-10, 10): gelu's fp32 evaluation and the two
+    bf16 roundings against the oracle, value by value."""
+    P, M, D, F = 1, 256, 128, 1280
+    grid = np.arange(-640, 640, dtype=np.float32) / 64.0          # 1280 values
+    rng = np.random.default_rng(620)
+    w1 = np.zeros((1, D, F), dtype=np.float32)
+    for k in range(D):
+        w1[0, k] = rng.permutation(grid)
+    x = np.zeros((1, M, D), dtype=np.float32)
+    x[0, np.arange(M), np.arange(M) % D] = 1.0
+    w2 = np.zeros((1, F, D), dtype=np.float32)
+    xb, w1b, w2b = inputs.bf16_bits(x), inputs.bf16_bits(w1), inputs.bf16_bits(w2)
+    note("tp_mlp gelu range")
+    _, gh, _, _ = _run(xb, w1b, w2b)
+    _, lo, hi, _, _ = oracle.tp_mlp_bounds(xb, w1b, w2b, 0, np.arange(M))
+    hv = oracle.bf16_to_f32(gh[0]).astype(np.float64)
+    assert np.all((lo[0] <= hv) & (hv <= hi[0]))
+    assert np.count_nonzero(lo != hi) <= 0.01 * lo.size
+
+
+def test_full_size_sampled_rows():
+    """P = 4, x [8192, 1024] in row blocks of 2048, W1 [1024, 16384],
+    W2 [16384, 1024] in the default launch configuration: the gathered input
+    everywhere, sampled tokens of h and of every rank's output."""
+    P, M, D, F = 4, 8192, 1024, 16384
+    note("tp_mlp full size generate")
+    x, w1, w2 = inputs.mlp_operands(P, M, D, F, seed=inputs.SEED_MLP)
+    note("tp_mlp full size run")
+    gf, gh, go, _ = _run(x, w1, w2)
+    for q in range(P):
+        np.testing.assert_array_equal(gf[q], x.reshape(M, D))
+    Mq = M // P
+    rows = np.unique(np.concatenate([[0, 255, 256, Mq - 1], np.random.default_rng(7).integers(0, Mq, 6)]))
+    note("tp_mlp full size check")
+    _check_bounds(x, w1, w2, gh, go, [(r, rows) for r in range(P)])
+
+
+def test_layers_in_place_match_out_of_place():
+    """Two layers with each output written over its input shard give the
+    bits of two layers with separate buffers, on one workspace."""
+    P, M, D, F = 4, 1024, 256, 1024
+    x, w1, w2 = inputs.mlp_operands(P, M, D, F, seed=630)
+    _, v1, u1 = inputs.mlp_operands(P, M, D, F, seed=631)
+    Mq, Fr = M // P, F // P
+    bf = torch.bfloat16
+    full = [torch.empty((M, D), dtype=bf, device="cuda") for _ in range(P)]
+    h = [torch.empty((M, Fr), dtype=bf, device="cuda") for _ in range(P)]
+    a, b = _dev(x), [torch.empty((Mq, D), dtype=bf, device="cuda") for _ in range(P)]
+    c = [torch.empty((Mq, D), dtype=bf, device="cuda") for _ in range(P)]
+    ws = rc.tp_mlp_workspace(P, M, D, F)
+    note("tp_mlp two layers out of place")
+    rc.tp_mlp_layer(a, _dev(w1), _dev(w2), full, h, b, ws=ws)
+    rc.tp_mlp_layer(b, _dev(v1), _dev(u1), full, h, c, ws=ws)
+    want = _host(c)
+    note("tp_mlp two layers in place")
+    y = _dev(x)
+    rc.tp_mlp_layer(y, _dev(w1), _dev(w2), full, h, y, ws=ws)
+    rc.tp_mlp_layer(y, _dev(v1), _dev(u1), full, h, y, ws=ws)
+    torch.cuda.synchronize()
+    assert rc.last_error(ws)[0] == 0
+    np.testing.assert_array_equal(_host(y), want)
+    # the first layer alone against the oracle
+    _, _, out1 = oracle.tp_mlp_layer(x, w1, w2)
+    assert np.mean(_host(b) == out1) > 0.9
+
+
+def test_errors():
+    P, M, D, F = 2, 512, 128, 256
+    x, w1, w2 = inputs.mlp_operands(P, M, D, F, seed=640)
+    xs, W1, W2 = _dev(x), _dev(w1), _dev(w2)
+    bf = torch.bfloat16
+    full = [torch.empty((M, D), dtype=bf, device="cuda") for _ in range(P)]
+    h = [torch.empty((M, F // P), dtype=bf, device="cuda") for _ in range(P)]
+    out = [torch.empty((M // P, D), dtype=bf, device="cuda") for _ in range(P)]
+    small = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(N.RingError) as e:
+        rc.tp_mlp_layer(xs, W1, W2, full, h, out, ws=small)
+    assert e.value.code == N.RING_EWORKSPACE
+    # h on top of the gathered input (both M x 128 here)
+    alias = [full[0].view(-1)[:M * (F // P)].view(M, F // P), h[1]]
+    with pytest.raises(N.RingError) as e:
+        rc.tp_mlp_layer(xs, W1, W2, full, alias, out)
+    assert e.value.code == N.RING_EINVAL
+    # out on top of h
+    with pytest.raises(N.RingError) as e:
+        rc.tp_mlp_layer(xs, W1, W2, full, h, [h[0].view(-1)[:(M // P) * D].view(M // P, D), out[1]])
+    assert e.value.code == N.RING_EINVAL
+    assert int(N.lib().tp_mlp_workspace_bytes(P, M, 96, F)) == 0
+    assert int(N.lib().tp_mlp_workspace_bytes(P, 300, D, F)) == 0
+
+
+def test_watchdog_reports_timeout_and_recovers():
+    """Rank 0 never flags its slices of the all-gather's phase 1: the layer
+    ends in RING_ETIMEOUT; the same workspace, cleared, then serves a normal
+    call."""
+    P, M, D, F = 4, 1024, 256, 1024
+    x, w1, w2 = _int_operands(P, M, D, F, seed=650)
+    note("tp_mlp watchdog drop_round=1")
+    N.set_tuning(drop_round=1, timeout_s=0.05)
+    xs, W1, W2 = _dev(x), _dev(w1), _dev(w2)
+    bf = torch.bfloat16
+    full = [torch.empty((M, D), dtype=bf, device="cuda") for _ in range(P)]
+    h = [torch.empty((M, F // P), dtype=bf, device="cuda") for _ in range(P)]
+    out = [torch.empty((M // P, D), dtype=bf, device="cuda") for _ in range(P)]
+    ws = rc.tp_mlp_layer(xs, W1, W2, full, h, out)
+    code, _ = rc.last_error(ws)
+    assert code == N.RING_ETIMEOUT
+    N.set_tuning(drop_round=0, timeout_s=5.0)
+    rc.workspace_init(ws)
+    _, gh, go, _ = _run(x, w1, w2, ws=ws)
+    _, h_ref, out_ref = oracle.tp_mlp_layer(x, w1, w2)
+    np.testing.assert_array_equal(gh, h_ref)
+    np.testing.assert_array_equal(go, out_ref)
