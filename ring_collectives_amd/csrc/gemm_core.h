@@ -267,23 +267,28 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
 
 // GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))),
 // the default of jax.nn.gelu, which the tensor-parallel MLP of "TPU 与分布式
-// 通信原语" (collective matmul) applies.  Since 1 + tanh(z) = 2 sigmoid(2z) it
-// is evaluated as x sigmoid(2z) in fp32, which stays accurate in the negative
-// tail where 1 + tanh(z) would cancel; the exponential only ever sees a
-// non-positive argument, so it cannot overflow.
+// 通信原语" (collective matmul) applies.  Since 0.5 (1 + tanh(z)) =
+// 1 / (1 + 2^-s) with s = 2 z log2(e), it is x / (1 + u) for x >= 0 and
+// x u / (1 + u) for x < 0, u = 2^-|s| <= 1: no cancellation in the negative
+// tail.  u is the square of 2^-|s|/2 so that it stays exact down to fp32's
+// subnormals (the hardware exp2 flushes results below 2^-126).  Error: about
+// 6 roundings in s (an absolute 6 2^-24 |s| ln 2 in the exponent, relative
+// in u), 1 ulp each for exp2 and the reciprocal, and a few roundings more.
 __device__ __forceinline__ float gelu_tanh(float x) {
-    const float t = 1.5957691216057308f * (x + 0.044715f * x * x * x);   // 2 sqrt(2/pi) (...)
-    const float e = expf(-fabsf(t));
-    const float sig = (t >= 0.0f ? 1.0f : e) / (1.0f + e);
-    return x * sig;
+    const float s = 2.3022081985f * (x + 0.044715f * x * x * x);   // 2 sqrt(2/pi) log2(e) (...)
+    const float v = __builtin_amdgcn_exp2f(-0.5f * fabsf(s));
+    const float u = v * v;
+    const float d = __builtin_amdgcn_rcpf(1.0f + u);
+    return x * (s >= 0.0f ? d : u * d);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ unsigned bf16_rne_bits(float f) {
-    unsigned u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// Two fp32 values -> two bf16 (round to nearest even) packed low, high
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+    typedef float f32x2v __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    const f32x2v f = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2v));
 }
 
 // Output element of the row-major store: the fp32 sum itself, its bf16
@@ -291,11 +296,22 @@ __device__ __forceinline__ unsigned bf16_rne_bits(float f) {
 // product to bf16 before the activation and the activation to bf16 after.
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_GELU_BF16 = 2 };
 
+// Four fp32 values (bits) -> four bf16 in two dwords, with the epilogue EPI.
 template <int EPI>
-__device__ __forceinline__ unsigned epi_bf16(unsigned v) {
-    unsigned b = bf16_rne_bits(__uint_as_float(v));
-    if constexpr (EPI == EPI_GELU_BF16) b = bf16_rne_bits(gelu_tanh(__uint_as_float(b << 16)));
-    return b;
+__device__ __forceinline__ u32x2 epi_bf16x4(const u32x4 o) {
+    float f0 = __uint_as_float(o[0]), f1 = __uint_as_float(o[1]);
+    float f2 = __uint_as_float(o[2]), f3 = __uint_as_float(o[3]);
+    if constexpr (EPI == EPI_GELU_BF16) {
+        const unsigned p01 = pack_bf16x2(f0, f1), p23 = pack_bf16x2(f2, f3);
+        f0 = gelu_tanh(__uint_as_float(p01 << 16));
+        f1 = gelu_tanh(__uint_as_float(p01 & 0xFFFF0000u));
+        f2 = gelu_tanh(__uint_as_float(p23 << 16));
+        f3 = gelu_tanh(__uint_as_float(p23 & 0xFFFF0000u));
+    }
+    u32x2 h;
+    h[0] = pack_bf16x2(f0, f1);
+    h[1] = pack_bf16x2(f2, f3);
+    return h;
 }
 
 // Store a wave's part of a finished tile row-major: element (i, j) of the
@@ -351,10 +367,7 @@ __device__ __forceinline__ void store_part_rowmajor(const f32x16 (&acc)[kMI][G::
             if constexpr (EPI == EPI_F32) {
                 st16<POL_PLAIN>(o, ov, at);
             } else {
-                u32x2 h;
-                h[0] = epi_bf16<EPI>(o[0]) | (epi_bf16<EPI>(o[1]) << 16);
-                h[1] = epi_bf16<EPI>(o[2]) | (epi_bf16<EPI>(o[3]) << 16);
-                st8<POL_PLAIN>(h, ov, at);
+                st8<POL_PLAIN>(epi_bf16x4<EPI>(o), ov, at);
             }
         }
     }
