@@ -284,11 +284,13 @@ const char *ring_strerror(int code);
  *   drop_round     test hook: if >= 1, rank 0 never signals round drop_round
  *                  (all_gather_gemm: never flags its slices of that phase),
  *                  so the waits on it must end in RING_ETIMEOUT.
- *   gemm_tile_n    output tile width of gemm_reduce_scatter: 128 (two
- *                  4-wave workgroups per compute unit), 256 (one 8-wave
- *                  workgroup; needs N % 256 == 0), or 0 to choose per call:
- *                  256 when there are at least as many 256 x 256 tiles per
- *                  chunk as compute units per rank, else 128.
+ *   gemm_tile_n    output tile width of the fused GEMMs: 128 (two 4-wave
+ *                  workgroups per compute unit), 256 (one 8-wave workgroup;
+ *                  needs N % 256 == 0), or 0 to choose per call: 256 when
+ *                  the 256 x 256 tiles give every compute unit work (for
+ *                  gemm_reduce_scatter, counting the tiles of all phases;
+ *                  for all_gather_gemm, those of one chunk per rank), else
+ *                  128.
  */
 typedef struct {
     int tile_vecs;

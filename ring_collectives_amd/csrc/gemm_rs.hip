@@ -33,11 +33,15 @@
 // wave's part, so producer wave w and consumer wave w of the next rank pair
 // up directly.
 //
-// Work assignment: workgroup g serves rank g % P and tile positions
-// g / P, g / P + G / P, ... of every chunk, phase by phase.  A tile of phase
-// f waits only for the left rank's tile at the same position of phase f-1,
-// held by the neighbouring workgroup and earlier in its order, and the P
-// workgroups of a ring are consecutive, so resident rings always finish.
+// Work assignment: the work items (phase, position, rank) are numbered phase
+// by phase, position by position, the P ranks of a position consecutive, and
+// workgroup g of G takes items g, g + G, g + 2G, ...  An item waits only for
+// the left rank's item at the same position of the phase before, which has
+// a smaller number.  Every workgroup is resident (G is at most what the CUs
+// hold) and works through its items in increasing order, so the smallest
+// unfinished item always has its input ready and its workgroup at it: the
+// launch always finishes.  Numbering across phases lets a small problem
+// (fewer tiles per chunk than workgroup slots) run several phases at once.
 #include "gemm_core.h"
 
 #include <hip/hip_runtime.h>
@@ -57,7 +61,6 @@ struct GemmParams {
     int tm_chunk;                              // tile rows per chunk (M / P / 256)
     int tn;                                    // tile columns (N / BN)
     int tpc;                                   // tiles per chunk
-    int groups;                                // rings of workgroups (gridDim.x / P)
     int out_bf16;                              // out is bf16 (the fp32 sum rounded once)
 };
 
@@ -82,17 +85,19 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave / G::WC, wc = wave % G::WC;
     const int P = p.P;
-    const int q = blockIdx.x % P;
-    const int grp = blockIdx.x / P;
-    const int left = (q - 1 + P) % P;
-    const unsigned short* A = p.A[q];
-    const unsigned short* B = p.B[q];
+    const int items = P * P * p.tpc;
 
-    for (int phase = 0; phase < P; ++phase) {
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int phase = it / (P * p.tpc);
+        const int pos = (it / P) % p.tpc;
+        const int q = it % P;
+        const int left = (q - 1 + P) % P;
+        const unsigned short* A = p.A[q];
+        const unsigned short* B = p.B[q];
         // chunk of this phase (see the schedule above); P = 1 has one phase
         const int c = P == 1 ? 0 : (phase == 0 ? (q - 1 + P) % P : (q - phase - 1 + 2 * P) % P);
         const bool final_phase = (phase == P - 1);
-        for (int pos = grp; pos < p.tpc; pos += p.groups) {
+        {
             const int tr = c * p.tm_chunk + pos / p.tn;
             const int tc = pos % p.tn;
             f32x16 acc[kMI][G::NI];
@@ -194,17 +199,16 @@ template <class G>
 static int launch_gemm_rs(GemmParams& prm, const DevInfo& di, hipStream_t stream) {
     prm.tn = prm.N / G::BN;
     prm.tpc = prm.tm_chunk * prm.tn;
-    // at most G::kWGsPerCU workgroups per CU, so every ring of P workgroups is
-    // resident; the occupancy query confirms the hardware agrees
+    // at most G::kWGsPerCU workgroups per CU, so every workgroup is resident;
+    // the occupancy query confirms the hardware agrees
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_rs_kernel<G>, 64 * G::NW, 0) != hipSuccess ||
         occ < G::kWGsPerCU)
         return RING_EHIP;
-    long long groups = (long long)di.cus * G::kWGsPerCU / prm.P;
-    if (groups > prm.tpc) groups = prm.tpc;
-    if (groups < 1) return RING_EUNSUPPORTED;   // more ranks than workgroup slots
-    prm.groups = (int)groups;
-    hipLaunchKernelGGL(gemm_rs_kernel<G>, dim3((unsigned)(groups * prm.P)), dim3(64 * G::NW), 0, stream, prm);
+    long long grid = (long long)di.cus * G::kWGsPerCU;
+    const long long items = (long long)prm.P * prm.P * prm.tpc;
+    if (grid > items) grid = items;
+    hipLaunchKernelGGL(gemm_rs_kernel<G>, dim3((unsigned)grid), dim3(64 * G::NW), 0, stream, prm);
     return hipGetLastError() == hipSuccess ? RING_OK : RING_EHIP;
 }
 
@@ -249,10 +253,10 @@ int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, in
     int bn = tu.gemm_tile_n;
     if (bn == 0) {
         // Wide tiles need less operand traffic per flop but make half as
-        // many workgroups; they pay off once every CU gets at least one wide
-        // tile per chunk.
-        const long long wide_tiles = (long long)prm.tm_chunk * (N / 256);
-        bn = (N % 256 == 0 && wide_tiles >= (long long)(di.cus / P)) ? 256 : 128;
+        // many work items; they pay off once there is at least one wide
+        // item per CU (the items of all phases count: phases overlap).
+        const long long wide_items = (long long)P * P * prm.tm_chunk * (N / 256);
+        bn = (N % 256 == 0 && wide_items >= (long long)di.cus) ? 256 : 128;
     }
     if (bn == 256 && N % 256) return RING_EUNSUPPORTED;
     prm.out_bf16 = out_bf16 ? 1 : 0;
