@@ -13,21 +13,24 @@
 // Schedule.  Phase f = 0 .. P-1 handles chunk c = (q - f) mod P, the order in
 // which the ring delivers the blocks (round t of the ring all-gather brings
 // chunk (q - t - 1) mod P from the left neighbour), local block first:
-//   forwarding: at phase f >= 1 rank q copies chunk c from its left
+//   forwarding of phase f >= 1: rank q copies chunk c from its left
 //     neighbour (from A_shard[left] at f = 1, the left rank's own block; from
 //     A_full[left] after) into A_full[q], slice by slice, each slice once the
-//     left neighbour has flagged it, and flags it in turn.  At f = 0 it
-//     places its own block.
+//     left neighbour has flagged it, and flags it in turn.  A workgroup
+//     forwards its slices of phase f + 1 just before its tiles of phase f,
+//     so forwarding runs a phase ahead of the tiles that need it.  The local
+//     block is placed first.
 //   GEMM: the tiles of chunk c, each once every slice of its row panel is
 //     flagged (phase 0 reads the local block straight from A_shard[q]).
 // A slice is the part of a 256-row panel that one tile position forwards:
 // rows 256 t / tn .. 256 (t + 1) / tn of the panel for column tile t, all K
 // columns, so the tn workgroups of a panel forward it together.
 //
-// Progress.  Every workgroup forwards all its slices of a phase before it
-// waits for any slice of that phase, and forwarding waits only for the left
-// rank's previous phase; so by induction on the phase every slice gets
-// forwarded, provided all workgroups are resident (the grid is sized so).
+// Progress.  In its iteration f a workgroup forwards phase f + 1, which waits
+// only for the left rank's forwarding of phase f (its iteration f - 1), and
+// computes tiles of phase f, which wait only for slices forwarded in
+// iteration f - 1; so by induction on f every workgroup finishes every
+// iteration, provided all workgroups are resident (the grid is sized so).
 // The slice flags have several readers (the panel's GEMM tiles and the right
 // neighbour), so readers leave them set and the last workgroup to finish
 // clears the table for the next call.
@@ -116,25 +119,33 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
     const int left = (q - 1 + P) % P;
     const int Mc = p.M / P;
 
+    // place the local block (nobody waits for it in A_full)
+    for (int pos = grp; pos < p.tpc; pos += p.groups) {
+        int r0, r1;
+        slice_rows(p, pos, r0, r1);
+        copy_rows<POL_PLAIN>(p.As[q] + (size_t)r0 * p.K, p.Af[q] + ((size_t)q * Mc + r0) * p.K, r1 - r0, p.K,
+                             tid, nthreads);
+    }
     for (int f = 0; f < P; ++f) {
         const int c = (q - f + P) % P;
-        // forward (or place) this workgroup's slices of chunk c
-        for (int pos = grp; pos < p.tpc; pos += p.groups) {
-            int r0, r1;
-            slice_rows(p, pos, r0, r1);
-            unsigned short* dst = p.Af[q] + ((size_t)c * Mc + r0) * p.K;
-            if (f == 0) {
-                copy_rows<POL_PLAIN>(p.As[q] + (size_t)r0 * p.K, dst, r1 - r0, p.K, tid, nthreads);
-                continue;   // nobody waits for the local block in A_full
+        // forward this workgroup's slices of phase g = f + 1 before the tiles
+        // of phase f, so the tiles of phase g find their panel forwarded a
+        // whole phase earlier
+        const int g = f + 1;
+        if (g < P) {
+            const int cg = (q - g + P) % P;
+            for (int pos = grp; pos < p.tpc; pos += p.groups) {
+                int r0, r1;
+                slice_rows(p, pos, r0, r1);
+                unsigned short* dst = p.Af[q] + ((size_t)cg * Mc + r0) * p.K;
+                if (g >= 2 && !wg_wait(p, ag_flag(p, g - 1, left, pos), wave, lane, q, g, pos)) return;
+                if (g == 1)   // the left rank's own block, straight from its input
+                    copy_rows<POL_PLAIN>(p.As[left] + (size_t)r0 * p.K, dst, r1 - r0, p.K, tid, nthreads);
+                else
+                    copy_rows<POL_DEV>(p.Af[left] + ((size_t)cg * Mc + r0) * p.K, dst, r1 - r0, p.K, tid,
+                                       nthreads);
+                if (!(q == 0 && p.drop_round > 0 && g == p.drop_round)) wg_signal(ag_flag(p, g, q, pos), tid);
             }
-            if (f >= 2 && !wg_wait(p, ag_flag(p, f - 1, left, pos), wave, lane, q, f, pos))
-                return;
-            if (f == 1)   // the left rank's own block, straight from its input
-                copy_rows<POL_PLAIN>(p.As[left] + (size_t)r0 * p.K, dst, r1 - r0, p.K, tid, nthreads);
-            else
-                copy_rows<POL_DEV>(p.Af[left] + ((size_t)c * Mc + r0) * p.K, dst, r1 - r0, p.K, tid,
-                                   nthreads);
-            if (!(q == 0 && p.drop_round > 0 && f == p.drop_round)) wg_signal(ag_flag(p, f, q, pos), tid);
         }
         // GEMM tiles of chunk c
         for (int pos = grp; pos < p.tpc; pos += p.groups) {
