@@ -270,8 +270,9 @@ const char *ring_strerror(int code);
  * Tuning and debug knobs of the chunk-step kernel, process-wide.  Changing
  * them while calls are in flight is not supported.  Results never depend on
  * them (fp32 bits included); only speed does, except for the debug hooks.
- *   tile_vecs      16-byte vectors per lane per tile: 4, 8 or 16 (a tile is
- *                  the unit of one flag: 64 lanes x tile_vecs x 16 bytes).
+ *   tile_vecs      16-byte vectors per lane per tile: 4, 8 or 16 (default;
+ *                  a tile is the unit of one flag: 64 lanes x tile_vecs x 16
+ *                  bytes).
  *   waves_per_cu   resident wavefronts to aim for per compute unit (4..16;
  *                  never more than half the occupancy limit is used).
  *   map_mode       wavefront -> (rank, tile) mapping: 0 the P ranks of a tile
