@@ -35,6 +35,10 @@ WORKLOADS = {
     "ar_f32_p8_64Mi": dict(op="all_reduce", P=8, n=64 << 20, kind="f32", seed=2, std=1.0),
     "ar_bf16_p16_128Mi": dict(op="all_reduce", P=16, n=128 << 20, kind="bf16", seed=3, std=1e-2),
     "ar_f32_p4_small": dict(op="all_reduce", P=4, n=4096, kind="f32", seed=0, std=None),
+    # int32 (8, 128 P) per rank, uniform [-1000, 1000], seed 1: reduce-scatter
+    # and all-gather on their own (latency-bound)
+    "rs_i32_p8_small": dict(op="reduce_scatter", P=8, n=8 * 128 * 8, kind="i32", seed=1, std=None),
+    "ag_i32_p8_small": dict(op="all_gather", P=8, n=8 * 128 * 8, kind="i32", seed=1, std=None),
     # fused GEMM + reduce-scatter: P = 4, A_q, B_q bf16 4096 x 4096, normal(0, 1/64)
     "gemm_rs_p4_4096": dict(op="gemm_rs", P=4, M=4096, N=4096, K=4096, kind="bf16", seed=4,
                             std=1.0 / 64, n=4096 * 4096),
@@ -145,6 +149,10 @@ def _traffic(workload: str, kernel: str):
         return None
 
 
+def _size(nbytes: int) -> str:
+    return "%d MiB" % (nbytes >> 20) if nbytes >= 1 << 20 else "%d KiB" % (nbytes >> 10)
+
+
 def _make_inputs(w):
     import numpy as np
     from ring_collectives_amd import inputs
@@ -153,6 +161,8 @@ def _make_inputs(w):
     if w["op"] == "ag_gemm":   # rank q's row block of A (M / P rows), and its B_q
         return inputs.gemm_operands(w["P"], w["M"] // w["P"], w["N"], w["K"], std=w["std"],
                                     seed=w["seed"])
+    if w["kind"] == "i32":
+        return inputs.to_chunk_major(inputs.ring_i32(w["P"], 8, w["n"] // (8 * w["P"])), w["P"])
     if w["kind"] == "f32" and w["std"] is None:
         return inputs.to_chunk_major(inputs.small_f32(w["P"], (8, 512)), w["P"])
     if w["kind"] == "f32":
@@ -187,6 +197,8 @@ def _cpu_baseline(w, x):
     elif w["op"] == "psum_circulating":
         want = (oracle.psum_circulating_bf16(x) if w["kind"] == "bf16"
                 else oracle.psum_circulating(x)[0])
+    elif w["op"] == "all_gather":
+        want = oracle.all_gather(x)
     elif w["op"] == "reduce_scatter_bidir":
         want = (oracle.reduce_scatter_bidir_bf16(x)[0] if w["kind"] == "bf16"
                 else oracle.reduce_scatter_bidir(x))
@@ -250,6 +262,7 @@ def _gemm_main(args, w):
     ms_step = (t1 - t0) * 1e3 / args.steps
     avg = sum(kern_ms) / len(kern_ms)
     flop = 2.0 * P * M * Nn * K
+    overlap = _overlap(args, a, b, P, M, Nn, K, avg) if op == "gemm_rs" else None
     print("[bench] %d steps: %.4f ms/step (wall), kernel avg %.4f ms" % (args.steps, ms_step, avg),
           file=sys.stderr, flush=True)
     cpu = None
@@ -304,7 +317,56 @@ def _gemm_main(args, w):
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
     }
+    if overlap is not None:
+        line["overlap"] = overlap
     print(json.dumps(line), flush=True)
+
+
+def _timed(fn, steps, warmup):
+    """Average time of fn over `steps` calls after `warmup`, HIP events on
+    the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _overlap(args, a, b, P, M, Nn, K, t_fused):
+    """How much of the reduce-scatter the fused kernel hides: the same
+    products as P separate GEMMs (the P = 1 path of the same kernel, no
+    ring) and the same reduce-scatter on fp32 buffers of the products'
+    size (the ring kernel), timed apart; efficiency = (T_gemm + T_rs -
+    T_fused) / T_rs."""
+    import torch
+    from ring_collectives_amd import _native as N
+    from ring_collectives_amd import collectives as rc
+    C = [torch.empty((M, Nn), dtype=torch.float32, device="cuda") for _ in range(P)]
+    ws1 = rc.workspace(N.OP_GEMM_REDUCE_SCATTER, 1, M * Nn, torch.float32)
+
+    def gemms():
+        for q in range(P):
+            rc.gemm_reduce_scatter([a[q]], [b[q]], [C[q]], ws=ws1)
+    t_gemm = _timed(gemms, args.steps, args.warmup)
+    src = [c.view(-1) for c in C]
+    dst = [torch.empty(M * Nn, dtype=torch.float32, device="cuda") for _ in range(P)]
+    ws2 = rc.workspace(N.OP_REDUCE_SCATTER, P, M * Nn, torch.float32)
+    t_rs = _timed(lambda: rc.reduce_scatter(src, dst, ws=ws2), args.steps, args.warmup)
+    for w_ in (ws1, ws2):
+        code, info = rc.last_error(w_)
+        if code != 0:
+            raise SystemExit("overlap reference reported %s (info %#x)" % (N.strerror(code), info))
+    eff = (t_gemm + t_rs - t_fused) / t_rs
+    print("[bench] overlap: GEMMs alone %.4f ms, reduce-scatter alone %.4f ms, fused %.4f ms, "
+          "efficiency %.2f" % (t_gemm, t_rs, t_fused, eff), file=sys.stderr, flush=True)
+    return {"t_gemm_ms": round(t_gemm, 5), "t_rs_ms": round(t_rs, 5), "t_fused_ms": round(t_fused, 5),
+            "efficiency": round(eff, 3)}
 
 
 def _mlp_main(args, w):
@@ -435,14 +497,17 @@ def main():
     dst = [torch.empty_like(t) for t in src]
     op = w["op"]
     ws_op = {"reduce_scatter": N.OP_REDUCE_SCATTER, "reduce_scatter_bidir": N.OP_REDUCE_SCATTER_BIDIR,
-             "psum_circulating": N.OP_PSUM_CIRCULATING}
+             "psum_circulating": N.OP_PSUM_CIRCULATING, "all_gather": N.OP_ALL_GATHER}
+    C = n // P
+    pieces = [src[r][r * C:(r + 1) * C].clone() for r in range(P)]   # rank r's piece, compact
     ws = rc.workspace(ws_op.get(op, N.OP_ALL_REDUCE), P, n, src[0].dtype)
     stream = torch.cuda.current_stream()
     call = {"ppermute": lambda: rc.ppermute(src, dst),
             "all_reduce": lambda: rc.all_reduce(src, dst, ws=ws),
             "reduce_scatter": lambda: rc.reduce_scatter(src, dst, ws=ws),
             "reduce_scatter_bidir": lambda: rc.reduce_scatter_bidir(src, dst, ws=ws),
-            "psum_circulating": lambda: rc.psum_circulating(src, dst, ws=ws)}[op]
+            "psum_circulating": lambda: rc.psum_circulating(src, dst, ws=ws),
+            "all_gather": lambda: rc.all_gather(dst, src=pieces, ws=ws)}[op]
 
     def step():
         call()
@@ -502,9 +567,9 @@ def main():
 
     traffic = _traffic(args.workload, kernel)
     line = {
-        "metric": "ring %s HBM GB/s & %% of peak, P=%d virtual ranks, %d MiB %s/rank"
-                  % (w["op"].replace("_", "-"), P, n * (2 if kind == "bf16" else 4) >> 20,
-                     "fp32" if kind == "f32" else kind),
+        "metric": "ring %s HBM GB/s & %% of peak, P=%d virtual ranks, %s %s/rank"
+                  % (w["op"].replace("_", "-"), P, _size(n * (2 if kind == "bf16" else 4)),
+                     {"f32": "fp32", "i32": "int32"}.get(kind, kind)),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
