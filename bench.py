@@ -19,6 +19,7 @@ widths actually used) divided by the measured time per step.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -262,9 +263,9 @@ def _gemm_main(args, w):
     ms_step = (t1 - t0) * 1e3 / args.steps
     avg = sum(kern_ms) / len(kern_ms)
     flop = 2.0 * P * M * Nn * K
-    overlap = _overlap(args, a, b, P, M, Nn, K, avg) if op == "gemm_rs" else None
-    print("[bench] %d steps: %.4f ms/step (wall), kernel avg %.4f ms" % (args.steps, ms_step, avg),
-          file=sys.stderr, flush=True)
+    overlap = _overlap(args, a, b, P, M, Nn, K, avg) if op == "gemm_rs" and not args.no_cpu else None
+    print("[bench] %d steps: %.4f ms/step (wall), kernel avg %.4f ms min %.4f max %.4f"
+          % (args.steps, ms_step, avg, min(kern_ms), max(kern_ms)), file=sys.stderr, flush=True)
     cpu = None
     parity = None
     if not args.no_cpu:
@@ -414,8 +415,8 @@ def _mlp_main(args, w):
     avg = sum(kern_ms) / len(kern_ms)
     cost = mlp_layer_cost(P, M, D, F)
     flop = cost["flop"]
-    print("[bench] %d steps: %.4f ms/step (wall), layer avg %.4f ms" % (args.steps, ms_step, avg),
-          file=sys.stderr, flush=True)
+    print("[bench] %d steps: %.4f ms/step (wall), layer avg %.4f ms min %.4f max %.4f"
+          % (args.steps, ms_step, avg, min(kern_ms), max(kern_ms)), file=sys.stderr, flush=True)
     cpu = None
     parity = None
     if not args.no_cpu:
@@ -472,8 +473,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true",
+                    help="skip the oracle baseline (and the GEMM + RS overlap references)")
     args = ap.parse_args()
+    # No garbage collection while timing: a collection inside a step's Python
+    # call stalls the launching thread long enough for the GPU to drain its
+    # queue, and the stall then counts inside that step's events (seen as one
+    # step of 12-16 ms in 250 of the all-gather + GEMM).
+    gc.collect()
+    gc.disable()
     if args.gpus != 1:
         print("bench.py: this build runs P virtual ranks on ONE GPU; --gpus %d is not "
               "supported (the multi-GPU ring is a design note only)" % args.gpus, file=sys.stderr)
