@@ -1,0 +1,64 @@
+"""The bench's cost model and command line, on the CPU.
+
+The algorithmic byte counts are the ring's own: a reduce-scatter round reads
+two chunks and writes one, an all-gather round reads one and writes one
+("全归约 3：Ring——每步大小恒定", cost card: 2 (P - 1) / P N per rank over
+2 (P - 1) rounds), at the widths the kernels use (the bf16 all-reduce carries
+its partial sums in fp32).  The MLP's flops are the TPU chapter's closed
+form.
+"""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_headline_all_reduce_bytes():
+    # P = 8, 64 Mi fp32 per rank: 7 rounds of 12 B and 7 of 8 B per chunk element
+    P, n = 8, 64 << 20
+    C = n // P
+    assert bench.moved_bytes("all_reduce", P, n, "f32") == 7 * 8 * C * (12 + 8) == 9_395_240_960
+    assert bench.moved_bytes("reduce_scatter", P, n, "f32") == 7 * 8 * C * 12
+    assert bench.moved_bytes("all_gather", P, n, "f32") == 7 * 8 * C * 8
+
+
+def test_bf16_all_reduce_bytes():
+    # P = 16, 128 Mi bf16: round 0 reads 2 + 2 and writes 4; middle rounds read
+    # 2 + 4 and write 4; the owner's round writes 2; the gather moves 2 + 2
+    P, n = 16, 128 << 20
+    C = n // P
+    rs = C * P * ((2 + 2 + 4) + 13 * (2 + 4 + 4) + (2 + 4 + 2))
+    ag = 15 * C * P * 4
+    assert bench.moved_bytes("all_reduce", P, n, "bf16") == rs + ag == 27_648_851_968
+
+
+def test_other_workloads_bytes():
+    P, n = 8, 64 << 20
+    C = n // P
+    assert bench.moved_bytes("ppermute", 2, n, "f32") == 2 * 2 * n * 4
+    assert bench.moved_bytes("psum_circulating", P, n, "f32") == 2 * (P + 1) * n * 4 * P == 38_654_705_664
+    assert bench.moved_bytes("reduce_scatter_bidir", P, n, "f32") == 7 * 12 * C * P + 8 * C * P
+    assert bench.moved_bytes("all_reduce", 1, n, "f32") == 0
+
+
+def test_mlp_cost_scales_with_tokens():
+    small = bench.mlp_layer_cost(P=4, M=256, D=1024, F=16384)
+    big = bench.mlp_layer_cost(P=4, M=8192, D=1024, F=16384)
+    assert big["flop"] == 32 * small["flop"] == 549_755_813_888
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "ONE GPU" in r.stderr and r.stdout == ""
+
+
+def test_every_workload_names_a_profiled_kernel_source():
+    for k, files in bench.KERNEL_SOURCE.items():
+        for f in files:
+            assert os.path.exists(os.path.join(ROOT, "ring_collectives_amd", "csrc", f)), (k, f)
+    assert len(bench._sha_source("tp_mlp_layer")) == 64
