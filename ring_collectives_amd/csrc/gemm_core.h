@@ -270,16 +270,18 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
 // 通信原语" (collective matmul) applies.  Since 0.5 (1 + tanh(z)) =
 // 1 / (1 + 2^-s) with s = 2 z log2(e), it is x / (1 + u) for x >= 0 and
 // x u / (1 + u) for x < 0, u = 2^-|s| <= 1: no cancellation in the negative
-// tail.  u is the square of 2^-|s|/2 so that it stays exact down to fp32's
-// subnormals (the hardware exp2 flushes results below 2^-126).  Error: about
-// 6 roundings in s (an absolute 6 2^-24 |s| ln 2 in the exponent, relative
-// in u), 1 ulp each for exp2 and the reciprocal, and a few roundings more.
+// tail.  h = s / 2 = x (c1 + c3 x^2) takes one fused multiply-add, and u is
+// the square of 2^-|h| so that it stays exact down to fp32's subnormals (the
+// hardware exp2 flushes results below 2^-126).  Error: about 4 roundings in
+// h (an absolute 4 2^-24 |s| ln 2 in the exponent, relative in u), 1 ulp
+// each for exp2 and the reciprocal, and a few roundings more.
 __device__ __forceinline__ float gelu_tanh(float x) {
-    const float s = 2.3022081985f * (x + 0.044715f * x * x * x);   // 2 sqrt(2/pi) log2(e) (...)
-    const float v = __builtin_amdgcn_exp2f(-0.5f * fabsf(s));
+    // c1 = sqrt(2/pi) log2(e), c3 = 0.044715 c1
+    const float h = x * __builtin_fmaf(x * x, 0.05147162f, 1.1511041f);
+    const float v = __builtin_amdgcn_exp2f(-fabsf(h));
     const float u = v * v;
     const float d = __builtin_amdgcn_rcpf(1.0f + u);
-    return x * (s >= 0.0f ? d : u * d);
+    return x * (h >= 0.0f ? d : u * d);
 }
 
 // Two fp32 values -> two bf16 (round to nearest even) packed low, high
