@@ -128,7 +128,8 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
                         for (int ni = 0; ni < G::NI; ++ni)
 #pragma unroll
                             for (int part = 0; part < 4; ++part)
-                                x[ni][part] = ld16s<POL_DEV>(rv, lane16, frag_soff<G>(mi, ni, part));
+                                // the neighbour's partial, read once: device scope, streamed
+                                x[ni][part] = ld16s<POL_DEV | POL_NT>(rv, lane16, frag_soff<G>(mi, ni, part));
                     }
 #pragma unroll
                     for (int ni = 0; ni < G::NI; ++ni) {
