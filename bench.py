@@ -53,6 +53,9 @@ WORKLOADS = {
     # one tensor-parallel MLP layer: P = 4, x [8192, 1024] in row blocks of
     # 2048 tokens, W1 [1024, 16384] by columns, W2 [16384, 1024] by rows
     "tp_mlp_p4_8192": dict(op="tp_mlp", P=4, M=8192, D=1024, F=16384, kind="bf16", seed=6),
+    # the same layer at the chapter's own 256 tokens (64 per rank: the
+    # unfused path; latency-bound)
+    "tp_mlp_p4_256": dict(op="tp_mlp", P=4, M=256, D=1024, F=16384, kind="bf16", seed=6),
     # a plain copy of known size (2 x 256 MiB read + written): counter calibration
     "ppermute_f32_p2_64Mi": dict(op="ppermute", P=2, n=64 << 20, kind="f32", seed=2, std=1.0),
     # reduce-scatter alone on the headline inputs: one-way ring, and the
@@ -457,7 +460,9 @@ def _mlp_main(args, w):
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flop / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                      "traffic": _traffic(args.workload, "tp_mlp_layer"),
-                     "kernel": "tp_mlp_layer (ag_gemm_kernel + gemm_rs_kernel)",
+                     "kernel": ("tp_mlp_layer (ag_gemm_kernel + gemm_rs_kernel)" if M % (256 * P) == 0 else
+                                "tp_mlp_layer (unfused: ring all-gather, 2P GEMMs, ring reduce-scatter, "
+                                "bf16 rounding)"),
                      "kernel_ms_avg": round(avg, 5)},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,

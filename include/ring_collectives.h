@@ -245,9 +245,14 @@ int all_gather_gemm(const void *const *A_shard, const void *const *B, void *cons
  * memory as x_shard (a layer in place); h must not overlap any input, x_full
  * or another h; out_shard must not overlap h or W2; none may overlap ws.
  * ws: at least tp_mlp_workspace_bytes(P, M, D, F) bytes, 256-byte aligned,
- * zeroed once; ring_last_error reports a watchdog timeout of either launch.
- * Shapes this version accepts: M % (256 P) == 0, D % 128 == 0,
- * F % (128 P) == 0.
+ * zeroed once; ring_last_error reports a watchdog timeout of any launch.
+ * Shapes this version accepts: M % 256 == 0, M % P == 0, D % 128 == 0,
+ * F % (128 P) == 0.  With M % (256 P) != 0 (fewer than 256 tokens per rank,
+ * as at the chapter's own 256 tokens over 4 ranks) the same steps run
+ * unfused, one kernel each: ring_all_gather, per-rank GEMMs (gelu epilogue,
+ * then fp32 partials in the workspace), ring_reduce_scatter of the partials
+ * in place, and the owner's block rounded once to bf16; the results are the
+ * same.
  */
 int tp_mlp_layer(const void *const *x_shard, const void *const *W1, const void *const *W2,
                  void *const *x_full, void *const *h, void *const *out_shard, int P, int M, int D,

@@ -61,7 +61,9 @@ struct GemmParams {
     int tm_chunk;                              // tile rows per chunk (M / P / 256)
     int tn;                                    // tile columns (N / BN)
     int tpc;                                   // tiles per chunk
-    int out_bf16;                              // out is bf16 (the fp32 sum rounded once)
+    int batched;                               // P independent products, no reduce-scatter
+    int epi;                                   // what out holds: EPI_F32, EPI_BF16 (the fp32 sum
+                                               // rounded once) or EPI_GELU_BF16
 };
 
 template <class G>
@@ -85,18 +87,21 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave / G::WC, wc = wave % G::WC;
     const int P = p.P;
-    const int items = P * P * p.tpc;
+    // batched: P independent products, no reduce-scatter (each rank's whole
+    // product is one chunk, stored straight to out[q])
+    const int items = p.batched ? P * p.tpc : P * P * p.tpc;
 
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        const int phase = it / (P * p.tpc);
+        const int phase = p.batched ? 0 : it / (P * p.tpc);
         const int pos = (it / P) % p.tpc;
         const int q = it % P;
         const int left = (q - 1 + P) % P;
         const unsigned short* A = p.A[q];
         const unsigned short* B = p.B[q];
         // chunk of this phase (see the schedule above); P = 1 has one phase
-        const int c = P == 1 ? 0 : (phase == 0 ? (q - 1 + P) % P : (q - phase - 1 + 2 * P) % P);
-        const bool final_phase = (phase == P - 1);
+        const int c = (P == 1 || p.batched) ? 0
+                                            : (phase == 0 ? (q - 1 + P) % P : (q - phase - 1 + 2 * P) % P);
+        const bool final_phase = p.batched || (phase == P - 1);
         {
             const int tr = c * p.tm_chunk + pos / p.tn;
             const int tc = pos % p.tn;
@@ -150,14 +155,18 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
                 }
                 signal_flag(gflag<G>(p, phase, q, pos, wave), lane);
             } else {
-                // Final sum of chunk q, row-major into out[q]: fp32, or
-                // rounded once to bf16.
-                const int lrow0 = (tr - q * p.tm_chunk) * kBM + wr * kWM;
+                // Final sum of chunk q, row-major into out[q]: fp32, rounded
+                // once to bf16, or bf16(gelu(bf16(sum))).
+                const int lrow0 = (tr - c * p.tm_chunk) * kBM + wr * kWM;   // c == q unless batched
                 const size_t at = (size_t)lrow0 * p.N + tc * BN + wc * G::WN;
-                if (p.out_bf16) {
+                if (p.epi == EPI_BF16) {
                     char* ob = (char*)p.out[q] + at * 2;
                     if (phase > 0) store_part_rowmajor<G, true, EPI_BF16>(acc, rv, ob, p.N, lds, lane, wave);
                     else store_part_rowmajor<G, false, EPI_BF16>(acc, rv, ob, p.N, lds, lane, wave);
+                } else if (p.epi == EPI_GELU_BF16) {
+                    char* ob = (char*)p.out[q] + at * 2;
+                    if (phase > 0) store_part_rowmajor<G, true, EPI_GELU_BF16>(acc, rv, ob, p.N, lds, lane, wave);
+                    else store_part_rowmajor<G, false, EPI_GELU_BF16>(acc, rv, ob, p.N, lds, lane, wave);
                 } else {
                     char* ob = (char*)p.out[q] + at * 4;
                     if (phase > 0) store_part_rowmajor<G, true, EPI_F32>(acc, rv, ob, p.N, lds, lane, wave);
@@ -207,7 +216,7 @@ static int launch_gemm_rs(GemmParams& prm, const DevInfo& di, hipStream_t stream
         occ < G::kWGsPerCU)
         return RING_EHIP;
     long long grid = (long long)di.cus * G::kWGsPerCU;
-    const long long items = (long long)prm.P * prm.P * prm.tpc;
+    const long long items = (long long)prm.P * (prm.batched ? 1 : prm.P) * prm.tpc;
     if (grid > items) grid = items;
     hipLaunchKernelGGL(gemm_rs_kernel<G>, dim3((unsigned)grid), dim3(64 * G::NW), 0, stream, prm);
     return hipGetLastError() == hipSuccess ? RING_OK : RING_EHIP;
@@ -217,17 +226,18 @@ static int launch_gemm_rs(GemmParams& prm, const DevInfo& di, hipStream_t stream
 // region_off bytes later than in a call of its own (the MLP layer puts them
 // behind the all-gather's flags).
 int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, int P, int M, int N, int K,
-                void* ws, size_t ws_bytes, void* stream, int out_bf16, size_t region_off) {
+                void* ws, size_t ws_bytes, void* stream, int epi, size_t region_off, int batched) {
     if (P < 1 || P > RING_MAX_RANKS || M < 0 || N < 0 || K < 0) return RING_EINVAL;
     if (!A || !B || !out) return RING_EINVAL;
     if (M == 0 || N == 0) return RING_OK;
-    if (M % (kBM * P) || N % 128 || K % 64 || K == 0) return RING_EUNSUPPORTED;
+    const int chunks = batched ? 1 : P;   // row blocks each rank's product splits into
+    if (M % (kBM * chunks) || N % 128 || K % 64 || K == 0) return RING_EUNSUPPORTED;
     for (int r = 0; r < P; ++r) {
         if (!A[r] || !B[r] || !out[r]) return RING_EINVAL;
         if (((uintptr_t)A[r] | (uintptr_t)B[r] | (uintptr_t)out[r]) & 15) return RING_EINVAL;
     }
     const size_t MN = (size_t)M * N;
-    GemmWs lay = gemm_ws_layout(P, MN);
+    GemmWs lay = gemm_ws_layout(batched ? 1 : P, MN);
     lay.flags_off += region_off;
     lay.work_off += region_off;
     lay.total += region_off;
@@ -250,17 +260,19 @@ int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, in
     prm.M = M;
     prm.N = N;
     prm.K = K;
-    prm.tm_chunk = M / P / kBM;
+    prm.tm_chunk = M / chunks / kBM;
+    prm.batched = batched ? 1 : 0;
     int bn = tu.gemm_tile_n;
     if (bn == 0) {
         // Wide tiles need less operand traffic per flop but make half as
         // many work items; they pay off once there is at least one wide
         // item per CU (the items of all phases count: phases overlap).
-        const long long wide_items = (long long)P * P * prm.tm_chunk * (N / 256);
+        const long long wide_items = (long long)P * chunks * prm.tm_chunk * (N / 256);
         bn = (N % 256 == 0 && wide_items >= (long long)di.cus) ? 256 : 128;
     }
     if (bn == 256 && N % 256) return RING_EUNSUPPORTED;
-    prm.out_bf16 = out_bf16 ? 1 : 0;
+    if (epi != EPI_F32 && epi != EPI_BF16 && epi != EPI_GELU_BF16) return RING_EINVAL;
+    prm.epi = epi;
     const hipStream_t st = (hipStream_t)stream;
     return bn == 256 ? launch_gemm_rs<Geo<256, 8>>(prm, di, st) : launch_gemm_rs<Geo<128, 4>>(prm, di, st);
 }
@@ -270,5 +282,5 @@ int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, in
 extern "C" int gemm_reduce_scatter(const void* const* A, const void* const* B, void* const* out,
                                    int P, int M, int N, int K, void* ws, size_t ws_bytes,
                                    void* stream) {
-    return ringc::gemm_rs_run(A, B, out, P, M, N, K, ws, ws_bytes, stream, 0, 0);
+    return ringc::gemm_rs_run(A, B, out, P, M, N, K, ws, ws_bytes, stream, ringc::EPI_F32, 0, 0);
 }

@@ -22,6 +22,19 @@
 // Workspace: [status | all-gather slice flags | reduce-scatter flags and
 // partial tiles].  Both kernels leave their flag tables zeroed, and the
 // regions are disjoint, so one workspace serves any number of layers.
+//
+// Token counts below 256 per rank (the chapter's own 256 tokens over P = 4
+// ranks make 64-row shards, less than one 256-row tile) run the same steps
+// unfused, each on its own kernel, in stream order:
+//   ring_all_gather of the row blocks                 -> x_full
+//   every rank's product x_full @ W1 (the fused kernel's batched mode, no
+//   reduce-scatter) with the gelu epilogue              -> h
+//   every rank's product h @ W2 in fp32                 -> partial (workspace)
+//   ring_reduce_scatter of the partials, in place (the fp32 ring order)
+//   the owner's block rounded once to bf16              -> out_shard
+// The arithmetic is the same as the fused path's, so the results are too.
+// Workspace: [status | ring flags | GEMM flags | P partials of M x D fp32].
+#include "gemm_core.h"
 #include "ring_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -44,22 +57,85 @@ bool any_overlap(const void* const* a, size_t na, const void* const* b, size_t n
     return false;
 }
 
+bool fused_shape(int P, int M) { return M % (256 * P) == 0; }
+
 struct MlpWs {
-    size_t rs_off, total;   // where the reduce-scatter's flags start; bytes in all
+    // fused: where the reduce-scatter's flags start.  unfused: where the
+    // GEMMs' flags start and where the partials start.  Bytes in all.
+    size_t rs_off, gemm_off, part_off, total;
 };
 
 bool mlp_ws_layout(int P, int M, int D, int F, MlpWs& w) {
     const int Fr = F / P;
-    const size_t ag = ag_gemm_workspace_bytes(P, (size_t)M * Fr);
-    const size_t rs = gemm_rs_workspace_bytes(P, (size_t)M * D);
-    if (!ag || !rs) return false;
-    w.rs_off = align256_mlp(ag);
-    w.total = w.rs_off + rs - kStatusBytes;   // the status block is shared
+    if (fused_shape(P, M)) {
+        const size_t ag = ag_gemm_workspace_bytes(P, (size_t)M * Fr);
+        const size_t rs = gemm_rs_workspace_bytes(P, (size_t)M * D);
+        if (!ag || !rs) return false;
+        w.rs_off = align256_mlp(ag);
+        w.gemm_off = w.part_off = 0;
+        w.total = w.rs_off + rs - kStatusBytes;   // the status block is shared
+        return true;
+    }
+    const size_t nd = (size_t)M * D;
+    const size_t ring = ring_workspace_bytes(RING_OP_REDUCE_SCATTER, P, nd, RING_F32);
+    const size_t ring_ag = ring_workspace_bytes(RING_OP_ALL_GATHER, P, nd, RING_BF16);
+    const size_t g1 = gemm_rs_workspace_bytes(1, (size_t)M * Fr), g2 = gemm_rs_workspace_bytes(1, nd);
+    if (!ring || !ring_ag || !g1 || !g2) return false;
+    w.rs_off = 0;
+    w.gemm_off = align256_mlp(ring > ring_ag ? ring : ring_ag);
+    w.part_off = align256_mlp(w.gemm_off + (g1 > g2 ? g1 : g2) - kStatusBytes);
+    w.total = w.part_off + (size_t)P * nd * sizeof(float);
     return true;
 }
 
 bool mlp_shape_ok(int P, int M, int D, int F) {
-    return M % (256 * P) == 0 && D % 128 == 0 && F % (128 * P) == 0;
+    return M % P == 0 && M % 256 == 0 && D % 128 == 0 && F % (128 * P) == 0;
+}
+
+// out[r] = bf16(part[r][r * n .. (r + 1) * n)), round to nearest even.
+struct OwnerTab {
+    const float* part[RING_MAX_RANKS];
+    unsigned short* out[RING_MAX_RANKS];
+};
+
+__global__ __launch_bounds__(256) void owner_bf16_kernel(OwnerTab t, long long n) {
+    const int r = blockIdx.y;
+    const float* src = t.part[r] + (size_t)r * n;
+    unsigned* dst = (unsigned*)t.out[r];
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n / 2;
+         i += (long long)gridDim.x * blockDim.x)
+        dst[i] = pack_bf16x2(src[2 * i], src[2 * i + 1]);
+}
+
+int mlp_unfused(const void* const* x_shard, const void* const* W1, const void* const* W2,
+                void* const* x_full, void* const* h, void* const* out_shard, int P, int M, int D, int F,
+                void* ws, size_t ws_bytes, const MlpWs& lay, void* stream) {
+    const int Fr = F / P;
+    const size_t nd = (size_t)M * D;
+    int rc = ring_all_gather(x_shard, x_full, P, nd, RING_BF16, ws, lay.gemm_off, stream);
+    if (rc != RING_OK) return rc;
+    void* part[RING_MAX_RANKS];
+    for (int q = 0; q < P; ++q) part[q] = (char*)ws + lay.part_off + (size_t)q * nd * sizeof(float);
+    const size_t goff = lay.gemm_off - kStatusBytes;   // the GEMMs' flags after the ring's
+    // every rank's product in one launch each (the batched mode of the fused kernel)
+    rc = gemm_rs_run((const void* const*)x_full, W1, h, P, M, Fr, D, ws, lay.part_off, stream, EPI_GELU_BF16,
+                     goff, 1);
+    if (rc != RING_OK) return rc;
+    rc = gemm_rs_run((const void* const*)h, W2, part, P, M, D, Fr, ws, lay.part_off, stream, EPI_F32, goff, 1);
+    if (rc != RING_OK) return rc;
+    rc = ring_reduce_scatter((const void* const*)part, part, P, nd, RING_F32, ws, lay.gemm_off, stream);
+    if (rc != RING_OK) return rc;
+    OwnerTab t;
+    for (int q = 0; q < P; ++q) {
+        t.part[q] = (const float*)part[q];
+        t.out[q] = (unsigned short*)out_shard[q];
+    }
+    const long long n = (long long)(M / P) * D;   // even: D % 128 == 0
+    long long blocks = (n / 2 + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(owner_bf16_kernel, dim3((unsigned)blocks, (unsigned)P), dim3(256), 0,
+                       (hipStream_t)stream, t, n);
+    return hipGetLastError() == hipSuccess ? RING_OK : RING_EHIP;
 }
 
 }  // namespace
@@ -106,9 +182,11 @@ extern "C" int tp_mlp_layer(const void* const* x_shard, const void* const* W1, c
             mlp_overlap(ws, ws_bytes, out_shard[r], shard_b))
             return RING_EINVAL;
 
+    if (!fused_shape(P, M))
+        return mlp_unfused(x_shard, W1, W2, x_full, h, out_shard, P, M, D, F, ws, ws_bytes, lay, stream);
     int rc = ag_gemm_run(x_shard, W1, x_full, h, P, M, Fr, D, ws, lay.rs_off, stream, 1);
     if (rc != RING_OK) return rc;
     // gemm_rs_run's own layout puts its flags kStatusBytes in; shift them to rs_off
-    return gemm_rs_run((const void* const*)h, W2, out_shard, P, M, D, Fr, ws, ws_bytes, stream, 1,
+    return gemm_rs_run((const void* const*)h, W2, out_shard, P, M, D, Fr, ws, ws_bytes, stream, EPI_BF16,
                        lay.rs_off - kStatusBytes);
 }

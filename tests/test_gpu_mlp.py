@@ -143,6 +143,35 @@ def test_grid_inputs_within_bounds(P, M, D, F, tile_n):
     assert np.mean(go == out) > 0.9
 
 
+@pytest.mark.parametrize("P,M,D,F", [(4, 256, 1024, 16384), (2, 256, 256, 512), (4, 512, 256, 1024),
+                                     (8, 256, 128, 1024)])
+def test_small_token_counts_integer_exact(P, M, D, F):
+    """Fewer than 256 tokens per rank run the unfused steps (the chapter's
+    own x [256, 1024], W1 [1024, 16384] at P = 4 among them): every bit."""
+    note("tp_mlp unfused integer P=%d M=%d D=%d F=%d" % (P, M, D, F))
+    x, w1, w2 = _int_operands(P, M, D, F, seed=660 + P)
+    gf, gh, go, _ = _run(x, w1, w2)
+    full, h, out = oracle.tp_mlp_layer(x, w1, w2)
+    np.testing.assert_array_equal(gf, full)
+    np.testing.assert_array_equal(gh, h)
+    np.testing.assert_array_equal(go, out)
+
+
+def test_page_shape_within_bounds_and_repeated():
+    """x [256, 1024] in row blocks of 64, W1 [1024, 16384], W2 [16384, 1024],
+    P = 4, the workload's distributions: every token within the oracle's
+    intervals; a second call on the same workspace gives the same bits."""
+    P, M, D, F = 4, 256, 1024, 16384
+    note("tp_mlp page shape")
+    x, w1, w2 = inputs.mlp_operands(P, M, D, F, seed=670)
+    gf, gh, go, ws = _run(x, w1, w2)
+    np.testing.assert_array_equal(gf, np.stack([x.reshape(M, D)] * P))
+    _check_bounds(x, w1, w2, gh, go, [(r, np.arange(M // P)) for r in range(P)])
+    _, gh2, go2, _ = _run(x, w1, w2, ws=ws)
+    np.testing.assert_array_equal(gh2, gh)
+    np.testing.assert_array_equal(go2, go)
+
+
 def test_gelu_epilogue_over_its_range():
     """One rank, x rows that are unit vectors: row i of x @ W1 is row i % D of
     W1, which holds every bf16 value of a dense sweep of [-11, 11] (gelu's
