@@ -111,9 +111,10 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 
 // C tile (tr, tc) of A B into acc (the wave's part): rows 256 tr .. of A
-// (M x K row-major), columns BN tc .. of B (K x N row-major).  APOL is the
-// cache policy of the A loads (device scope when another workgroup of the
-// same launch wrote A).
+// (M x K row-major), columns BN tc .. of B (K x N row-major), over the K
+// range kbeg .. kbeg + kl (all of K by default).  APOL is the cache policy
+// of the A loads (device scope when another workgroup of the same launch
+// wrote A).
 //
 // MFMA operands (v_mfma_f32_32x32x16_bf16): lane l holds A[m = l % 32][k =
 // 8 (l / 32) + t] and B[k = 8 (l / 32) + t][n = l % 32], t = 0..7.  A is read
@@ -126,8 +127,9 @@ template <class G, int APOL = POL_PLAIN>
 __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __restrict__ A,
                                           const unsigned short* __restrict__ B, int tr, int tc,
                                           f32x16 (&acc)[kMI][G::NI], unsigned short* lds,
-                                          int lane, int wave, int wr, int wc) {
+                                          int lane, int wave, int wr, int wc, int kbeg = 0, int kl = -1) {
     constexpr int BN = G::BN;
+    if (kl < 0) kl = K;
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
@@ -135,9 +137,10 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
 
-    // A panel: 256 rows x K; B panel: K rows x BN columns (row stride N).
-    const rsrc_t Av = tile_view(A + (size_t)tr * kBM * K, (long long)kBM * K * 2);
-    const rsrc_t Bv = tile_view(B + (size_t)tc * BN, ((long long)(K - 1) * N + BN) * 2);
+    // A panel: 256 rows x kl (row stride K); B panel: kl rows x BN columns
+    // (row stride N); both views end at the last element the tile reads.
+    const rsrc_t Av = tile_view(A + (size_t)tr * kBM * K + kbeg, ((long long)(kBM - 1) * K + kl) * 2);
+    const rsrc_t Bv = tile_view(B + (size_t)kbeg * N + (size_t)tc * BN, ((long long)(kl - 1) * N + BN) * 2);
 
     // Direct loads.  A instruction i of wave w fills rows 8 (kLoadsA w + i)
     // .. +7 (lane: row + lane / 8, stored chunk lane % 8); B instruction i
@@ -222,8 +225,8 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
     // step this wave can wait for its B loads and leave the A loads of the
     // stage after in flight (R = 2, odd steps).  Past the end of K the issues
     // re-read the last stage into the free buffer (never read again).
-    const int KT = K / G::BKB;                 // steps
-    const int KA = K / G::BKA;                 // A stages
+    const int KT = kl / G::BKB;                // steps
+    const int KA = kl / G::BKA;                // A stages
     __syncthreads();   // the previous tile's epilogue may still be reading LDS
     issue_b(0, 0);
     issue_a(0, 0);

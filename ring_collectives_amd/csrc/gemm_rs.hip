@@ -62,6 +62,8 @@ struct GemmParams {
     int tn;                                    // tile columns (N / BN)
     int tpc;                                   // tiles per chunk
     int batched;                               // P independent products, no reduce-scatter
+    int ksplit;                                // batched: K split in this many ranges, each
+    float* split;                              //   range's fp32 product at split[(s P + q) M N ..]
     int epi;                                   // what out holds: EPI_F32, EPI_BF16 (the fp32 sum
                                                // rounded once) or EPI_GELU_BF16
 };
@@ -88,11 +90,14 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
     const int wr = wave / G::WC, wc = wave % G::WC;
     const int P = p.P;
     // batched: P independent products, no reduce-scatter (each rank's whole
-    // product is one chunk, stored straight to out[q])
-    const int items = p.batched ? P * p.tpc : P * P * p.tpc;
+    // product is one chunk, stored straight to out[q]), optionally with K in
+    // ksplit ranges whose products go to split (summed by the caller)
+    const int S = p.batched ? p.ksplit : 1;
+    const int items = p.batched ? P * p.tpc * S : P * P * p.tpc;
 
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int phase = p.batched ? 0 : it / (P * p.tpc);
+        const int ks = p.batched ? it / (P * p.tpc) : 0;   // K range of a batched item
         const int pos = (it / P) % p.tpc;
         const int q = it % P;
         const int left = (q - 1 + P) % P;
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
             const int tr = c * p.tm_chunk + pos / p.tn;
             const int tc = pos % p.tn;
             f32x16 acc[kMI][G::NI];
-            gemm_tile<G>(p.K, p.N, A, B, tr, tc, acc, lds, lane, wave, wr, wc);
+            gemm_tile<G>(p.K, p.N, A, B, tr, tc, acc, lds, lane, wave, wr, wc, ks * (p.K / S), p.K / S);
 
             // Epilogue.  Each row of 32 x 32 blocks is loaded, added and stored
             // in one go so only a few accumulators are live outside the
@@ -159,7 +164,10 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
                 // once to bf16, or bf16(gelu(bf16(sum))).
                 const int lrow0 = (tr - c * p.tm_chunk) * kBM + wr * kWM;   // c == q unless batched
                 const size_t at = (size_t)lrow0 * p.N + tc * BN + wc * G::WN;
-                if (p.epi == EPI_BF16) {
+                if (S > 1) {
+                    char* ob = (char*)(p.split + (size_t)(ks * P + q) * p.M * p.N) + at * 4;
+                    store_part_rowmajor<G, false, EPI_F32>(acc, rv, ob, p.N, lds, lane, wave);
+                } else if (p.epi == EPI_BF16) {
                     char* ob = (char*)p.out[q] + at * 2;
                     if (phase > 0) store_part_rowmajor<G, true, EPI_BF16>(acc, rv, ob, p.N, lds, lane, wave);
                     else store_part_rowmajor<G, false, EPI_BF16>(acc, rv, ob, p.N, lds, lane, wave);
@@ -216,7 +224,7 @@ static int launch_gemm_rs(GemmParams& prm, const DevInfo& di, hipStream_t stream
         occ < G::kWGsPerCU)
         return RING_EHIP;
     long long grid = (long long)di.cus * G::kWGsPerCU;
-    const long long items = (long long)prm.P * (prm.batched ? 1 : prm.P) * prm.tpc;
+    const long long items = (long long)prm.P * (prm.batched ? prm.ksplit : prm.P) * prm.tpc;
     if (grid > items) grid = items;
     hipLaunchKernelGGL(gemm_rs_kernel<G>, dim3((unsigned)grid), dim3(64 * G::NW), 0, stream, prm);
     return hipGetLastError() == hipSuccess ? RING_OK : RING_EHIP;
@@ -226,12 +234,15 @@ static int launch_gemm_rs(GemmParams& prm, const DevInfo& di, hipStream_t stream
 // region_off bytes later than in a call of its own (the MLP layer puts them
 // behind the all-gather's flags).
 int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, int P, int M, int N, int K,
-                void* ws, size_t ws_bytes, void* stream, int epi, size_t region_off, int batched) {
+                void* ws, size_t ws_bytes, void* stream, int epi, size_t region_off, int batched, int ksplit,
+                float* split) {
     if (P < 1 || P > RING_MAX_RANKS || M < 0 || N < 0 || K < 0) return RING_EINVAL;
     if (!A || !B || !out) return RING_EINVAL;
     if (M == 0 || N == 0) return RING_OK;
     const int chunks = batched ? 1 : P;   // row blocks each rank's product splits into
     if (M % (kBM * chunks) || N % 128 || K % 64 || K == 0) return RING_EUNSUPPORTED;
+    if (ksplit < 1 || (ksplit > 1 && (!batched || !split || epi != EPI_F32 || K % (64 * ksplit))))
+        return RING_EINVAL;
     for (int r = 0; r < P; ++r) {
         if (!A[r] || !B[r] || !out[r]) return RING_EINVAL;
         if (((uintptr_t)A[r] | (uintptr_t)B[r] | (uintptr_t)out[r]) & 15) return RING_EINVAL;
@@ -262,12 +273,14 @@ int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, in
     prm.K = K;
     prm.tm_chunk = M / chunks / kBM;
     prm.batched = batched ? 1 : 0;
+    prm.ksplit = ksplit;
+    prm.split = split;
     int bn = tu.gemm_tile_n;
     if (bn == 0) {
         // Wide tiles need less operand traffic per flop but make half as
         // many work items; they pay off once there is at least one wide
         // item per CU (the items of all phases count: phases overlap).
-        const long long wide_items = (long long)P * chunks * prm.tm_chunk * (N / 256);
+        const long long wide_items = (long long)P * (batched ? ksplit : P) * prm.tm_chunk * (N / 256);
         bn = (N % 256 == 0 && wide_items >= (long long)di.cus) ? 256 : 128;
     }
     if (bn == 256 && N % 256) return RING_EUNSUPPORTED;
@@ -282,5 +295,5 @@ int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, in
 extern "C" int gemm_reduce_scatter(const void* const* A, const void* const* B, void* const* out,
                                    int P, int M, int N, int K, void* ws, size_t ws_bytes,
                                    void* stream) {
-    return ringc::gemm_rs_run(A, B, out, P, M, N, K, ws, ws_bytes, stream, ringc::EPI_F32, 0, 0);
+    return ringc::gemm_rs_run(A, B, out, P, M, N, K, ws, ws_bytes, stream, ringc::EPI_F32, 0, 0, 1, nullptr);
 }

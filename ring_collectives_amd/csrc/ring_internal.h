@@ -83,10 +83,13 @@ size_t ag_gemm_workspace_bytes(int P, size_t n);
 // holds (0 the fp32 sums, 1 their bf16 rounding, 2 bf16(gelu(bf16(sum)))),
 // its flags and partial tiles sit region_off bytes further into ws than in a
 // call of its own (the status word stays at ws); batched makes it P
-// independent products with no reduce-scatter (out[q] = A_q B_q, M % 256).  ag_gemm_run: gelu_bf16 stores
+// independent products with no reduce-scatter (out[q] = A_q B_q, M % 256),
+// and ksplit > 1 then splits K into that many ranges whose fp32 products go
+// to split[(s P + q) M N ..] instead (epi must be EPI_F32; out unused).  ag_gemm_run: gelu_bf16 stores
 // bf16(gelu(bf16(product))) instead of the fp32 product.
 int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, int P, int M, int N, int K,
-                void* ws, size_t ws_bytes, void* stream, int epi, size_t region_off, int batched = 0);
+                void* ws, size_t ws_bytes, void* stream, int epi, size_t region_off, int batched = 0,
+                int ksplit = 1, float* split = nullptr);
 int ag_gemm_run(const void* const* A_shard, const void* const* B, void* const* A_full, void* const* C,
                 int P, int M, int N, int K, void* ws, size_t ws_bytes, void* stream, int gelu_bf16);
 

@@ -29,11 +29,13 @@
 //   ring_all_gather of the row blocks                 -> x_full
 //   every rank's product x_full @ W1 (the fused kernel's batched mode, no
 //   reduce-scatter) with the gelu epilogue              -> h
-//   every rank's product h @ W2 in fp32                 -> partial (workspace)
+//   every rank's product h @ W2 in fp32, its K split into S ranges so the
+//   few tiles still fill the GPU, the ranges summed in order -> partial
 //   ring_reduce_scatter of the partials, in place (the fp32 ring order)
 //   the owner's block rounded once to bf16              -> out_shard
 // The arithmetic is the same as the fused path's, so the results are too.
-// Workspace: [status | ring flags | GEMM flags | P partials of M x D fp32].
+// Workspace: [status | ring flags | GEMM flags | P partials of M x D fp32 |
+// S P range products of M x D fp32].
 #include "gemm_core.h"
 #include "ring_internal.h"
 
@@ -59,10 +61,22 @@ bool any_overlap(const void* const* a, size_t na, const void* const* b, size_t n
 
 bool fused_shape(int P, int M) { return M % (256 * P) == 0; }
 
+constexpr int kMaxSplit = 8;
+
+// K ranges of the unfused second product: about 256 work items of 256 x 128
+// tiles in all, at most kMaxSplit, each range a multiple of 64.
+int mlp_split(int P, int M, int D, int F) {
+    const int Fr = F / P;
+    const long long tiles = (long long)P * (M / 256) * (D / 128);
+    int S = 1;
+    while (S < kMaxSplit && tiles * S * 2 <= 256 && Fr % (64 * S * 2) == 0) S *= 2;
+    return S;
+}
+
 struct MlpWs {
     // fused: where the reduce-scatter's flags start.  unfused: where the
-    // GEMMs' flags start and where the partials start.  Bytes in all.
-    size_t rs_off, gemm_off, part_off, total;
+    // GEMMs' flags, the partials and the range products start.  Bytes in all.
+    size_t rs_off, gemm_off, part_off, split_off, total;
 };
 
 bool mlp_ws_layout(int P, int M, int D, int F, MlpWs& w) {
@@ -72,7 +86,7 @@ bool mlp_ws_layout(int P, int M, int D, int F, MlpWs& w) {
         const size_t rs = gemm_rs_workspace_bytes(P, (size_t)M * D);
         if (!ag || !rs) return false;
         w.rs_off = align256_mlp(ag);
-        w.gemm_off = w.part_off = 0;
+        w.gemm_off = w.part_off = w.split_off = 0;
         w.total = w.rs_off + rs - kStatusBytes;   // the status block is shared
         return true;
     }
@@ -84,12 +98,30 @@ bool mlp_ws_layout(int P, int M, int D, int F, MlpWs& w) {
     w.rs_off = 0;
     w.gemm_off = align256_mlp(ring > ring_ag ? ring : ring_ag);
     w.part_off = align256_mlp(w.gemm_off + (g1 > g2 ? g1 : g2) - kStatusBytes);
-    w.total = w.part_off + (size_t)P * nd * sizeof(float);
+    w.split_off = w.part_off + (size_t)P * nd * sizeof(float);
+    w.total = w.split_off + (size_t)mlp_split(P, M, D, F) * P * nd * sizeof(float);
     return true;
 }
 
 bool mlp_shape_ok(int P, int M, int D, int F) {
     return M % P == 0 && M % 256 == 0 && D % 128 == 0 && F % (128 * P) == 0;
+}
+
+// part[q][i] = sum over s = 0 .. S-1, in that order, of split[s P + q][i].
+struct PartTab {
+    float* p[RING_MAX_RANKS];
+};
+
+__global__ __launch_bounds__(256) void sum_ranges_kernel(const float* split, PartTab t, int P, int S,
+                                                             long long n) {
+    const int q = blockIdx.y;
+    float* out = t.p[q];
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (long long)gridDim.x * blockDim.x) {
+        float a = split[(size_t)q * n + i];
+        for (int s = 1; s < S; ++s) a += split[((size_t)s * P + q) * n + i];
+        out[i] = a;
+    }
 }
 
 // out[r] = bf16(part[r][r * n .. (r + 1) * n)), round to nearest even.
@@ -121,8 +153,20 @@ int mlp_unfused(const void* const* x_shard, const void* const* W1, const void* c
     rc = gemm_rs_run((const void* const*)x_full, W1, h, P, M, Fr, D, ws, lay.part_off, stream, EPI_GELU_BF16,
                      goff, 1);
     if (rc != RING_OK) return rc;
-    rc = gemm_rs_run((const void* const*)h, W2, part, P, M, D, Fr, ws, lay.part_off, stream, EPI_F32, goff, 1);
+    const int S = mlp_split(P, M, D, F);
+    float* split = (float*)((char*)ws + lay.split_off);
+    rc = gemm_rs_run((const void* const*)h, W2, part, P, M, D, Fr, ws, lay.part_off, stream, EPI_F32, goff, 1,
+                     S, S > 1 ? split : nullptr);
     if (rc != RING_OK) return rc;
+    if (S > 1) {
+        PartTab pt;
+        for (int q = 0; q < P; ++q) pt.p[q] = (float*)part[q];
+        long long blocks = ((long long)nd + 255) / 256;
+        if (blocks > 1024) blocks = 1024;
+        hipLaunchKernelGGL(sum_ranges_kernel, dim3((unsigned)blocks, (unsigned)P), dim3(256), 0,
+                           (hipStream_t)stream, split, pt, P, S, (long long)nd);
+        if (hipGetLastError() != hipSuccess) return RING_EHIP;
+    }
     rc = ring_reduce_scatter((const void* const*)part, part, P, nd, RING_F32, ws, lay.gemm_off, stream);
     if (rc != RING_OK) return rc;
     OwnerTab t;
