@@ -290,13 +290,16 @@ const char *ring_strerror(int code);
  *   drop_round     test hook: if >= 1, rank 0 never signals round drop_round
  *                  (all_gather_gemm: never flags its slices of that phase),
  *                  so the waits on it must end in RING_ETIMEOUT.
- *   gemm_tile_n    output tile width of the fused GEMMs: 128 (two 4-wave
- *                  workgroups per compute unit), 256 (one 8-wave workgroup;
- *                  needs N % 256 == 0), or 0 to choose per call: 256 when
- *                  the 256 x 256 tiles give every compute unit work (for
+ *   gemm_tile_n    output tile width of the fused GEMMs: 64 or 128 (two
+ *                  4-wave workgroups per compute unit; all_gather_gemm
+ *                  takes 128 for 64), 256 (one 8-wave workgroup; needs
+ *                  N % 256 == 0), or 0 to choose per call: 256 when the
+ *                  256 x 256 tiles give every compute unit work (for
  *                  gemm_reduce_scatter, counting the tiles of all phases;
  *                  for all_gather_gemm, those of one chunk per rank), else
- *                  128.
+ *                  128 when the 256 x 128 ones do, else 64
+ *                  (gemm_reduce_scatter and tp_mlp_layer; 128 for
+ *                  all_gather_gemm).
  */
 typedef struct {
     int tile_vecs;

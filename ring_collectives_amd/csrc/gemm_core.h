@@ -23,12 +23,16 @@ constexpr int kMI = kWM / 32; // 32 x 32 MFMA blocks down a wave's part
 // Tile geometry for an output tile of kBM x BN computed by NW waves, arranged
 // 2 down x NW / 2 across: wave w owns rows (w / WC) * 128 .. +127 and columns
 // (w % WC) * WN .. + WN - 1, a part of 128 x 64 (4 x 2 MFMA blocks of 32 x 32,
-// 128 accumulator registers, so two waves fit on a SIMD).
+// 128 accumulator registers, so two waves fit on a SIMD) or, for BN = 64,
+// 128 x 32.
 //   BN = 256, NW = 8: one workgroup per CU; a compute step covers 64 of K;
-//   BN = 128, NW = 4: two workgroups per CU; a step covers 32 of K.
-// Both run two waves per SIMD, so one wave's LDS reads and waits overlap the
-// other's matrix-core work.  The wide tile needs a third less operand traffic
-// per flop and wins once there are enough tiles to fill the CUs.
+//   BN = 128, NW = 4: two workgroups per CU; a step covers 32 of K;
+//   BN = 64,  NW = 4: as 128, on half the columns.
+// With enough tiles all run two waves per SIMD, so one wave's LDS reads and
+// waits overlap the other's matrix-core work.  The wide tile needs a third
+// less operand traffic per flop and wins once there are enough tiles to fill
+// the CUs; the narrow one is for products with too few 128-wide tiles to give
+// every CU one (a few hundred tokens), where it halves each tile's work.
 // A is staged 64 deep in K whatever the step, so every A row of a stage is one
 // whole 128-byte line: rows of 64 bytes cost about twice the fabric requests
 // per byte (each load instruction touches 16 half-used lines instead of 8
@@ -62,6 +66,8 @@ template <int BN_, int NW_> struct Geo {
     static constexpr int kWGsPerCU = BN == 256 ? 1 : 2;
     // XOR applied to the 16-byte chunk index of A row m in LDS
     static __device__ __forceinline__ int swz_a(int m) { return (m >> 1) & 7; }
+    // ... and of B row k (see the LDS layout below)
+    static __device__ __forceinline__ int swz_b(int k) { return BN == 64 ? 4 * ((k >> 1) & 1) : 4 * (k & 3); }
     static_assert(kLds * kWGsPerCU <= 160 * 1024, "LDS");
     static_assert(NW * kEpiWave * 4 <= kLds, "epilogue LDS");
     static_assert(kBM % (NW * kARows) == 0 && BKB % (NW * kBRows) == 0, "load split");
@@ -81,7 +87,8 @@ __device__ __forceinline__ unsigned frag_soff(int mi, int ni, int part) {
 // instruction = 64 lanes x 16 B = 1 KiB of consecutive LDS) and spread over
 // the banks by XOR-ing the 16-byte chunk index:
 //   A: chunk c of row m is stored at chunk c ^ ((m >> 1) & 7)
-//   B: chunk c of row k is stored at chunk c ^ (4 (k & 3))
+//   B: chunk c of row k is stored at chunk c ^ (4 (k & 3)), or, for BN = 64
+//      (rows of 128 bytes, two to a bank cycle), at c ^ (4 ((k >> 1) & 1))
 // The LDS has 64 banks of 4 bytes and serves 16 lanes of a 16-byte read, or
 // 32 lanes of an 8-byte read, per cycle; with these swizzles the 16 rows of an
 // A fragment read, and the 4 rows x 2 column groups of a transposed B read,
@@ -155,8 +162,8 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
     for (int par = 0; par < 2; ++par) {
         const int m = par * G::kARows + lane / G::kAC;     // row mod 16 of this lane
         a_voff[par] = (unsigned)(((lane / G::kAC) * K + ((lane % G::kAC) ^ G::swz_a(m)) * 8) * 2);
-        const int kr = par * G::kBRows + lane / BC;        // row mod 4 of this lane
-        const int cb = (lane % BC) ^ (4 * (kr & 3));
+        const int kr = par * G::kBRows + lane / BC;        // row (mod 4) of this lane
+        const int cb = (lane % BC) ^ G::swz_b(kr);
         b_voff[par] = (unsigned)(((lane / BC) * N + cb * 8) * 2);
     }
     auto issue_a = [&](int st, int slot) {                 // A stage st (K 64 st ..)
@@ -196,7 +203,7 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
 #pragma unroll
         for (int ni = 0; ni < G::NI; ++ni) {
             const int n = wc * G::WN + ni * 32 + 16 * (g & 1) + 4 * (i & 3);
-            const int chunk = (n >> 3) ^ (4 * (krow & 3));
+            const int chunk = (n >> 3) ^ G::swz_b(krow);
             b_off[ni] = (unsigned)(krow * G::kBRowBytes + chunk * 16 + (n & 7) * 2);
         }
     }

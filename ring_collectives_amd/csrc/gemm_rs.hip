@@ -24,7 +24,8 @@
 // are exactly the ring reduce-scatter's: ((C_{c+1} + C_{c+2}) + ...) + C_c.
 //
 // Tiles.  One workgroup computes one 256 x BN fp32 output tile (256 x 256
-// with 8 waves, one workgroup per CU, or 256 x 128 with 4 waves, two per CU)
+// with 8 waves, one workgroup per CU, or 256 x 128 or 256 x 64 with 4 waves,
+// two per CU)
 // with v_mfma_f32_32x32x16_bf16; every wave owns a 128 x 64 part as 32 x 32
 // MFMA blocks.  K advances through LDS buffers filled by direct global->LDS
 // loads one step ahead of the buffers the matrix cores read.  Partial tiles
@@ -188,9 +189,11 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
 // ---------------------------------------------------------------- host side
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Tiles are never narrower than 128 columns, so the flag table is sized for
-// 256 x 128 tiles whatever width a call uses.
-constexpr size_t kMinTileFloats = (size_t)kBM * 128;
+// Shapes come in multiples of 256 x 128 (kShapeFloats); tiles are never
+// narrower than 64 columns, so the flag table is sized for 256 x 64 tiles
+// whatever width a call uses.
+constexpr size_t kShapeFloats = (size_t)kBM * 128;
+constexpr size_t kMinTileFloats = (size_t)kBM * 64;
 
 struct GemmWs {
     size_t flags_off, flags_bytes, work_off, work_bytes, total;
@@ -209,7 +212,7 @@ static GemmWs gemm_ws_layout(int P, size_t MN) {
 }
 
 size_t gemm_rs_workspace_bytes(int P, size_t n) {
-    if (P < 1 || P > RING_MAX_RANKS || n == 0 || n % ((size_t)P * kMinTileFloats)) return 0;
+    if (P < 1 || P > RING_MAX_RANKS || n == 0 || n % ((size_t)P * kShapeFloats)) return 0;
     return gemm_ws_layout(P, n).total;
 }
 
@@ -280,14 +283,17 @@ int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, in
         // Wide tiles need less operand traffic per flop but make half as
         // many work items; they pay off once there is at least one wide
         // item per CU (the items of all phases count: phases overlap).
-        const long long wide_items = (long long)P * (batched ? ksplit : P) * prm.tm_chunk * (N / 256);
-        bn = (N % 256 == 0 && wide_items >= (long long)di.cus) ? 256 : 128;
+        // Below one 128-wide item per CU, 64-wide tiles spread the work
+        // over twice as many CUs.
+        const long long items128 = (long long)P * (batched ? ksplit : P) * prm.tm_chunk * (N / 128);
+        bn = (N % 256 == 0 && items128 / 2 >= (long long)di.cus) ? 256 : items128 >= (long long)di.cus ? 128 : 64;
     }
     if (bn == 256 && N % 256) return RING_EUNSUPPORTED;
     if (epi != EPI_F32 && epi != EPI_BF16 && epi != EPI_GELU_BF16) return RING_EINVAL;
     prm.epi = epi;
     const hipStream_t st = (hipStream_t)stream;
-    return bn == 256 ? launch_gemm_rs<Geo<256, 8>>(prm, di, st) : launch_gemm_rs<Geo<128, 4>>(prm, di, st);
+    return bn == 256 ? launch_gemm_rs<Geo<256, 8>>(prm, di, st)
+                     : bn == 128 ? launch_gemm_rs<Geo<128, 4>>(prm, di, st) : launch_gemm_rs<Geo<64, 4>>(prm, di, st);
 }
 
 }  // namespace ringc

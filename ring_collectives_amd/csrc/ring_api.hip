@@ -65,7 +65,7 @@ static bool tuning_valid(const ring_tuning_t& x) {
     return (x.tile_vecs == 4 || x.tile_vecs == 8 || x.tile_vecs == 16) && x.waves_per_cu >= 4 &&
            x.waves_per_cu <= 16 && (x.map_mode == 0 || x.map_mode == 2) && x.timeout_s > 0 &&
            x.timeout_s < 3600 && (x.stepwise == 0 || x.stepwise == 1) && x.drop_round >= 0 &&
-           (x.gemm_tile_n == 0 || x.gemm_tile_n == 128 || x.gemm_tile_n == 256);
+           (x.gemm_tile_n == 0 || x.gemm_tile_n == 64 || x.gemm_tile_n == 128 || x.gemm_tile_n == 256);
 }
 
 static ring_tuning_t& tuning_ref() {

@@ -63,11 +63,14 @@ bool fused_shape(int P, int M) { return M % (256 * P) == 0; }
 
 constexpr int kMaxSplit = 8;
 
-// K ranges of the unfused second product: about 256 work items of 256 x 128
-// tiles in all, at most kMaxSplit, each range a multiple of 64.
+// K ranges of the unfused second product: about 256 work items of 256 x 64
+// tiles in all (one per CU; the product's automatic tile width then takes
+// 64-wide tiles, as it does below one 128-wide item per CU), at most
+// kMaxSplit, each range a multiple of 64.  Every range's fp32 product is
+// written and read back once, so more ranges than the CUs need cost traffic.
 int mlp_split(int P, int M, int D, int F) {
     const int Fr = F / P;
-    const long long tiles = (long long)P * (M / 256) * (D / 128);
+    const long long tiles = (long long)P * (M / 256) * (D / 64);
     int S = 1;
     while (S < kMaxSplit && tiles * S * 2 <= 256 && Fr % (64 * S * 2) == 0) S *= 2;
     return S;

@@ -180,7 +180,7 @@ def test_tuning_roundtrip_and_validation():
         for bad in ({"tile_vecs": 5}, {"waves_per_cu": 1}, {"waves_per_cu": 32}, {"map_mode": 1},
                     {"map_mode": 7},
                     {"timeout_s": 0.0}, {"stepwise": 2}, {"drop_round": -1},
-                    {"gemm_tile_n": 64}, {"gemm_tile_n": 192}):
+                    {"gemm_tile_n": 32}, {"gemm_tile_n": 192}):
             with pytest.raises(N.RingError):
                 N.set_tuning(**bad)
     finally:

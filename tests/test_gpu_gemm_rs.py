@@ -32,10 +32,10 @@ def _needs_gpu():
     yield
 
 
-@pytest.fixture(params=[128, 256])
+@pytest.fixture(params=[64, 128, 256])
 def tile_n(request):
-    """Both output tile widths: 256 x 128 (two workgroups per compute unit)
-    and 256 x 256 (one)."""
+    """Every output tile width: 256 x 64 and 256 x 128 (two workgroups per
+    compute unit) and 256 x 256 (one)."""
     old = N.set_tuning(gemm_tile_n=request.param)
     yield request.param
     N.set_tuning(gemm_tile_n=old["gemm_tile_n"])

@@ -43,7 +43,7 @@ def _default_tuning():
     N.set_tuning(**old)
 
 
-@pytest.fixture(params=[128, 256])
+@pytest.fixture(params=[64, 128, 256])
 def tile_n(request):
     N.set_tuning(gemm_tile_n=request.param)
     return request.param
@@ -143,12 +143,15 @@ def test_grid_inputs_within_bounds(P, M, D, F, tile_n):
     assert np.mean(go == out) > 0.9
 
 
+@pytest.mark.parametrize("bn", [0, 128])
 @pytest.mark.parametrize("P,M,D,F", [(4, 256, 1024, 16384), (2, 256, 256, 512), (4, 512, 256, 1024),
                                      (8, 256, 128, 1024)])
-def test_small_token_counts_integer_exact(P, M, D, F):
+def test_small_token_counts_integer_exact(P, M, D, F, bn):
     """Fewer than 256 tokens per rank run the unfused steps (the chapter's
-    own x [256, 1024], W1 [1024, 16384] at P = 4 among them): every bit."""
-    note("tp_mlp unfused integer P=%d M=%d D=%d F=%d" % (P, M, D, F))
+    own x [256, 1024], W1 [1024, 16384] at P = 4 among them): every bit,
+    with the automatic tile widths (64 for these few tiles) and with 128."""
+    N.set_tuning(gemm_tile_n=bn)
+    note("tp_mlp unfused integer P=%d M=%d D=%d F=%d bn=%d" % (P, M, D, F, bn))
     x, w1, w2 = _int_operands(P, M, D, F, seed=660 + P)
     gf, gh, go, _ = _run(x, w1, w2)
     full, h, out = oracle.tp_mlp_layer(x, w1, w2)
