@@ -205,6 +205,46 @@ def test_gelu_epilogue_over_its_range():
     assert np.mean(gh == h_ref) > 0.99
 
 
+def _every_finite_bf16_layer(P, tile, D=256, F=256):
+    """A layer whose first product's outputs are every finite bf16 value:
+    rank q's W1 holds the values (each rank the same), x's rows are unit
+    vectors, so h[q][i] = gelu(W1 row i % D).  Returns (w1 bits, h)."""
+    u = np.arange(65536, dtype=np.uint32)
+    vals = u[((u >> 7) & 0xFF) != 255].astype(np.uint16)
+    vals = np.concatenate([vals, vals[:D * F - len(vals)]])
+    M = 256
+    w1b = np.stack([vals.reshape(D, F)] * P)
+    x = np.zeros((P, M // P, D), dtype=np.float32)
+    rows = np.arange(M)
+    x.reshape(M, D)[rows, rows % D] = 1.0
+    w2b = np.zeros((P, F, D), dtype=np.uint16)
+    N.set_tuning(gemm_tile_n=tile)
+    _, gh, _, _ = _run(inputs.bf16_bits(x), w1b, w2b)
+    return w1b, gh
+
+
+def test_gelu_epilogue_on_every_bf16():
+    """Every finite bf16 input of the activation (65,280 values, subnormals
+    included) through the epilogues of both GEMM kernels and three tile
+    widths: all-gather + GEMM with 256 x 128 and 256 x 256 tiles (P = 1,
+    fused) and the batched products of the unfused layer (P = 2, 256 x 64
+    tiles).  The bits must agree, and lie within the oracle's intervals."""
+    note("tp_mlp gelu: every finite bf16")
+    w1b, h_128 = _every_finite_bf16_layer(1, 128)
+    _, h_256 = _every_finite_bf16_layer(1, 256)
+    _, h_unfused = _every_finite_bf16_layer(2, 0)
+    np.testing.assert_array_equal(h_256, h_128)
+    for q in range(2):
+        np.testing.assert_array_equal(h_unfused[q], h_128[0])
+    x = np.zeros((1, 256, 256), dtype=np.float32)
+    x[0, np.arange(256), np.arange(256)] = 1.0
+    _, lo, hi, _, _ = oracle.tp_mlp_bounds(inputs.bf16_bits(x), w1b[:1], np.zeros((1, 256, 256), np.uint16), 0,
+                                           np.arange(256))
+    hv = oracle.bf16_to_f32(h_128[0]).astype(np.float64)
+    bad = ~((lo[0] <= hv) & (hv <= hi[0]))
+    assert not bad.any(), int(bad.sum())
+
+
 def test_full_size_sampled_rows():
     """P = 4, x [8192, 1024] in row blocks of 2048, W1 [1024, 16384],
     W2 [16384, 1024] in the default launch configuration: the gathered input
