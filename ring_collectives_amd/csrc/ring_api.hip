@@ -12,6 +12,7 @@ namespace ringc {
 int elem_bytes(int dtype) {
     switch (dtype) {
         case RING_F32: return 4;
+        case kDtF32Bf16Out: return 4;
         case RING_I32: return 4;
         case RING_BF16: return 2;
         default: return 0;
@@ -162,7 +163,7 @@ static hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 // bidirectional kernel over its rounds 0 .. P-1 when bidir is set).
 static int run_ring(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream, int k_begin, int k_end,
-                    int compact_src, int bidir = 0) {
+                    int compact_src, int bidir = 0, void* const* out16 = nullptr) {
     const RingWs lay = ring_ws_layout(P, n, dtype);
     // reduce-scatter rounds of bf16 data carry fp32 partial sums
     const bool need_carry = dtype == RING_BF16 && (bidir || k_begin < P - 1);
@@ -185,6 +186,12 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
         prm.dst[r] = dst[r];
         if ((uintptr_t)dst[r] & 15) vec_ok = 0;
         if (src && ((uintptr_t)src[r] & 15)) vec_ok = 0;
+    }
+    if (out16) {
+        for (int r = 0; r < P; ++r) {
+            prm.out16[r] = out16[r];
+            if ((uintptr_t)out16[r] & 15) vec_ok = 0;
+        }
     }
     prm.carry = need_carry ? (float*)((char*)ws + lay.carry_off) : nullptr;
     prm.flags = (int*)((char*)ws + lay.flags_off);
@@ -299,6 +306,16 @@ static int run_psum(const void* const* src, void* const* dst, int P, size_t n, i
 }
 
 // ------------------------------------------------------------------ C ABI
+int ringc::ring_reduce_scatter_bf16_out(const void* const* src, void* const* dst, void* const* out16, int P,
+                                        size_t n, void* ws, size_t ws_bytes, void* stream) {
+    if (P < 2 || P > RING_MAX_RANKS || !src || !dst || !out16) return RING_EINVAL;
+    if (n == 0) return RING_OK;
+    if (n % (size_t)P) return RING_EINVAL;
+    for (int q = 0; q < P; ++q)
+        if (!src[q] || !dst[q] || !out16[q]) return RING_EINVAL;
+    return run_ring(src, dst, P, n, kDtF32Bf16Out, ws, ws_bytes, stream, 0, P - 1, 0, 0, out16);
+}
+
 extern "C" {
 
 size_t ring_workspace_bytes(int op, int P, size_t n, int dtype) {

@@ -50,7 +50,13 @@ struct RingParams {
     int bidir;                        // 1: top halves travel left, bottom halves right
     int T_top;                        // positions 0 .. T_top-1 are top-half tiles
     long long h;                      // elements in the top half of a chunk
+    // fp32 reduce-scatter with a bf16 result only (kDtF32Bf16Out)
+    void* out16[RING_MAX_RANKS];      // the owner's chunk, rounded once to bf16
 };
+
+// Internal element type of the ring launchers: an fp32 reduce-scatter whose
+// owner stores its chunk's sum rounded once to bf16.
+constexpr int kDtF32Bf16Out = 16;
 
 // Workspace layout of the ring collectives for (P, n, dtype).
 struct RingWs {
@@ -74,6 +80,13 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_ring(RingParams& prm, int dtype, int tile_vecs, int grid_blocks,
                        hipStream_t s);   // prm.bidir selects the bidirectional kernel
 int ring_blocks_per_cu(int dtype, int tile_vecs, int kind);   // occupancy: 0 ring, 1 bidir, 2 psum
+
+// The fp32 ring reduce-scatter of src into dst (the ring's partial sums; dst
+// may be src), with the owner's chunk of the sum rounded once to bf16 into
+// out16[q] (n / P elements) instead of stored in dst.  P >= 2.  The MLP
+// layer's unfused path.
+int ring_reduce_scatter_bf16_out(const void* const* src, void* const* dst, void* const* out16, int P, size_t n,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 // GEMM + reduce-scatter workspace size (n = M * N per rank).
 size_t gemm_rs_workspace_bytes(int P, size_t n);

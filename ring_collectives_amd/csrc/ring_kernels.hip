@@ -52,7 +52,7 @@
 
 namespace ringc {
 
-enum { DT_F32 = RING_F32, DT_BF16 = RING_BF16, DT_I32 = RING_I32 };
+enum { DT_F32 = RING_F32, DT_BF16 = RING_BF16, DT_I32 = RING_I32, DT_F32B = kDtF32Bf16Out };
 
 __device__ __forceinline__ int left_of(int r, int P) { return (r - 1 + P) % P; }
 __device__ __forceinline__ int rs_chunk(int r, int s, int P) { return (r - s - 2 + 2 * P) % P; }
@@ -112,6 +112,7 @@ template <int DT> struct Elem;
 template <> struct Elem<DT_F32> { typedef float T; static constexpr int VPE = 4; };
 template <> struct Elem<DT_I32> { typedef int T; static constexpr int VPE = 4; };
 template <> struct Elem<DT_BF16> { typedef unsigned short T; static constexpr int VPE = 4; };
+template <> struct Elem<DT_F32B> { typedef float T; static constexpr int VPE = 4; };
 
 template <int DT> __device__ __forceinline__ unsigned add1(unsigned a, unsigned b);
 template <> __device__ __forceinline__ unsigned add1<DT_F32>(unsigned a, unsigned b) {
@@ -143,10 +144,13 @@ __device__ __forceinline__ TilePos tile_pos(const RingParams& p, int c, int j) {
 
 // One reduce-scatter round of tile t (position j) of one rank, fp32 / int32:
 //   dst[r][t] = src[r][t] + (first ? src[from][t] : dst[from][t])
-// after waiting for flag (k, from, j): rank `from` finished the tile.
-template <int DT, int U>
+// after waiting for flag (k, from, j): rank `from` finished the tile.  With
+// OUT16 (fp32 only) the owner's round (last) stores the sum rounded once to
+// bf16 into out16[r], at the tile's place in the chunk, instead.
+template <int DT, int U, bool OUT16 = false>
 __device__ bool rs_tile_at(const RingParams& p, int r, int from, int k, int j, const TilePos& t,
-                           bool first, int lane, bool wait) {
+                           bool first, int lane, bool wait, bool last = false) {
+    constexpr int DA = DT == DT_F32B ? DT_F32 : DT;   // the arithmetic
     const long long nb = t.len * 4;
     const rsrc_t own = tile_view((const char*)p.src[r] + t.e0 * 4, nb);
     const rsrc_t rcv = tile_view((const char*)(first ? p.src[from] : p.dst[from]) + t.e0 * 4, nb);
@@ -159,13 +163,35 @@ __device__ bool rs_tile_at(const RingParams& p, int r, int from, int k, int j, c
         if (wait && !wait_flag(p, k, from, r, j, lane, seen)) return false;
 #pragma unroll
         for (int i = 0; i < U; ++i) b[i] = ld16<POL_RCV>(rcv, (unsigned)(lane + i * kWave) * 16u);
+        if constexpr (OUT16) {
+            if (last) {
+                const rsrc_t o16 = tile_view((unsigned short*)p.out16[r] + t.off, t.len * 2);
 #pragma unroll
-        for (int i = 0; i < U; ++i) st16<POL_PUB>(add4<DT>(a[i], b[i]), out, (unsigned)(lane + i * kWave) * 16u);
+                for (int i = 0; i < U; ++i) {
+                    const u32x4 x = add4<DA>(a[i], b[i]);
+                    u32x2 h;
+                    h[0] = pack_bf16(__uint_as_float(x[0]), __uint_as_float(x[1]));
+                    h[1] = pack_bf16(__uint_as_float(x[2]), __uint_as_float(x[3]));
+                    st8<POL_FIN>(h, o16, (unsigned)(lane + i * kWave) * 8u);
+                }
+                return true;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < U; ++i) st16<POL_PUB>(add4<DA>(a[i], b[i]), out, (unsigned)(lane + i * kWave) * 16u);
     } else {
         if (wait && !wait_flag(p, k, from, r, j, lane, seen)) return false;
         for (long long i = lane; i < t.len; i += kWave) {
             const unsigned o = (unsigned)i * 4u;
-            st4<POL_PUB>(add1<DT>(ld4<POL_OWN>(own, o), ld4<POL_RCV>(rcv, o)), out, o);
+            const unsigned x = add1<DA>(ld4<POL_OWN>(own, o), ld4<POL_RCV>(rcv, o));
+            if constexpr (OUT16) {
+                if (last) {
+                    st2<POL_FIN>((unsigned short)bf16_rne(__uint_as_float(x)),
+                                 tile_view((unsigned short*)p.out16[r] + t.off, t.len * 2), (unsigned)i * 2u);
+                    continue;
+                }
+            }
+            st4<POL_PUB>(x, out, o);
         }
     }
     return true;
@@ -176,7 +202,8 @@ template <int DT, int U>
 __device__ __forceinline__ bool rs_tile(const RingParams& p, int r, int left, int k, int j, int lane,
                                         bool wait) {
     const TilePos t = tile_pos(p, rs_chunk(r, k, p.P), j);
-    return rs_tile_at<DT, U>(p, r, left, k, j, t, k == 0, lane, wait);
+    if constexpr (DT == DT_F32B) return rs_tile_at<DT, U, true>(p, r, left, k, j, t, k == 0, lane, wait, k == p.P - 2);
+    else return rs_tile_at<DT, U>(p, r, left, k, j, t, k == 0, lane, wait);
 }
 
 // The fp32 carry of a whole bf16 tile (p.tile = 256 U elements) is kept in
@@ -420,7 +447,8 @@ __global__ __launch_bounds__(kBlock) void ring_step_kernel(RingParams p) {
                 if constexpr (DT == DT_BF16) ok = rs_tile_bf16<U>(p, r, left, k, j, lane, wait);
                 else ok = rs_tile<DT, U>(p, r, left, k, j, lane, wait);
             } else {
-                ok = ag_tile<DT, U>(p, r, left, k, j, lane, wait);
+                if constexpr (DT == DT_F32B) ok = false;   // reduce-scatter rounds only
+                else ok = ag_tile<DT, U>(p, r, left, k, j, lane, wait);
             }
             if (!ok) return;
             if (k + 1 < p.k_end && !(r == 0 && k + 1 == p.drop_round))
@@ -789,12 +817,16 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 
 template <int DT, int U>
 static hipError_t launch_ring_t(RingParams& prm, int grid, hipStream_t s) {
-    if (prm.psum)
-        hipLaunchKernelGGL((ring_psum_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
-    else if (prm.bidir)
-        hipLaunchKernelGGL((ring_bidir_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
-    else
+    if constexpr (DT == DT_F32B) {   // the one-way reduce-scatter only
         hipLaunchKernelGGL((ring_step_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
+    } else {
+        if (prm.psum)
+            hipLaunchKernelGGL((ring_psum_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
+        else if (prm.bidir)
+            hipLaunchKernelGGL((ring_bidir_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
+        else
+            hipLaunchKernelGGL((ring_step_kernel<DT, U>), dim3(grid), dim3(kBlock), 0, s, prm);
+    }
     return hipGetLastError();
 }
 
@@ -811,11 +843,16 @@ static hipError_t launch_ring_dt(RingParams& prm, int tile_vecs, int grid, hipSt
 template <int DT, int U>
 static int blocks_per_cu_t(int kind) {
     int nb = 0;
-    const hipError_t e =
-        kind == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_psum_kernel<DT, U>, kBlock, 0)
-        : kind == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_bidir_kernel<DT, U>, kBlock, 0)
-                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_step_kernel<DT, U>, kBlock, 0);
-    return e == hipSuccess ? nb : 0;
+    if constexpr (DT == DT_F32B) {   // the one-way reduce-scatter only
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_step_kernel<DT, U>, kBlock, 0);
+        return e == hipSuccess ? nb : 0;
+    } else {
+        const hipError_t e =
+            kind == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_psum_kernel<DT, U>, kBlock, 0)
+            : kind == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_bidir_kernel<DT, U>, kBlock, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_step_kernel<DT, U>, kBlock, 0);
+        return e == hipSuccess ? nb : 0;
+    }
 }
 
 template <int DT>
@@ -831,6 +868,7 @@ static int blocks_per_cu_dt(int tile_vecs, int kind) {
 int ring_blocks_per_cu(int dtype, int tile_vecs, int kind) {
     switch (dtype) {
         case RING_F32: return blocks_per_cu_dt<DT_F32>(tile_vecs, kind);
+        case kDtF32Bf16Out: return blocks_per_cu_dt<DT_F32B>(tile_vecs, kind);
         case RING_I32: return blocks_per_cu_dt<DT_I32>(tile_vecs, kind);
         case RING_BF16: return blocks_per_cu_dt<DT_BF16>(tile_vecs, kind);
         default: return 0;
@@ -840,6 +878,7 @@ int ring_blocks_per_cu(int dtype, int tile_vecs, int kind) {
 hipError_t launch_ring(RingParams& prm, int dtype, int tile_vecs, int grid, hipStream_t s) {
     switch (dtype) {
         case RING_F32: return launch_ring_dt<DT_F32>(prm, tile_vecs, grid, s);
+        case kDtF32Bf16Out: return launch_ring_dt<DT_F32B>(prm, tile_vecs, grid, s);
         case RING_I32: return launch_ring_dt<DT_I32>(prm, tile_vecs, grid, s);
         case RING_BF16: return launch_ring_dt<DT_BF16>(prm, tile_vecs, grid, s);
         default: return hipErrorInvalidValue;

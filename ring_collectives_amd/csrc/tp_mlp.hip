@@ -31,11 +31,13 @@
 //   reduce-scatter) with the gelu epilogue              -> h
 //   every rank's product h @ W2 in fp32, its K split into S ranges so the
 //   few tiles still fill the GPU, the ranges summed in order -> partial
-//   ring_reduce_scatter of the partials, in place (the fp32 ring order)
-//   the owner's block rounded once to bf16              -> out_shard
-// The arithmetic is the same as the fused path's, so the results are too.
-// Workspace: [status | ring flags | GEMM flags | P partials of M x D fp32 |
-// S P range products of M x D fp32].
+//   the fp32 ring reduce-scatter of the partials, in place, the owner's
+//   block rounded once to bf16 as the ring's last round stores it
+//                                                       -> out_shard
+// The arithmetic is the fused path's except for the order of the second
+// product's sums over K (the ranges).
+// Workspace: [status | ring flags | GEMM flags | P ring partial sums of
+// M x D fp32 | S P range products of M x D fp32].
 #include "gemm_core.h"
 #include "ring_internal.h"
 
@@ -127,21 +129,6 @@ __global__ __launch_bounds__(256) void sum_ranges_kernel(const float* split, Par
     }
 }
 
-// out[r] = bf16(part[r][r * n .. (r + 1) * n)), round to nearest even.
-struct OwnerTab {
-    const float* part[RING_MAX_RANKS];
-    unsigned short* out[RING_MAX_RANKS];
-};
-
-__global__ __launch_bounds__(256) void owner_bf16_kernel(OwnerTab t, long long n) {
-    const int r = blockIdx.y;
-    const float* src = t.part[r] + (size_t)r * n;
-    unsigned* dst = (unsigned*)t.out[r];
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n / 2;
-         i += (long long)gridDim.x * blockDim.x)
-        dst[i] = pack_bf16x2(src[2 * i], src[2 * i + 1]);
-}
-
 int mlp_unfused(const void* const* x_shard, const void* const* W1, const void* const* W2,
                 void* const* x_full, void* const* h, void* const* out_shard, int P, int M, int D, int F,
                 void* ws, size_t ws_bytes, const MlpWs& lay, void* stream) {
@@ -170,19 +157,10 @@ int mlp_unfused(const void* const* x_shard, const void* const* W1, const void* c
                            (hipStream_t)stream, split, pt, P, S, (long long)nd);
         if (hipGetLastError() != hipSuccess) return RING_EHIP;
     }
-    rc = ring_reduce_scatter((const void* const*)part, part, P, nd, RING_F32, ws, lay.gemm_off, stream);
-    if (rc != RING_OK) return rc;
-    OwnerTab t;
-    for (int q = 0; q < P; ++q) {
-        t.part[q] = (const float*)part[q];
-        t.out[q] = (unsigned short*)out_shard[q];
-    }
-    const long long n = (long long)(M / P) * D;   // even: D % 128 == 0
-    long long blocks = (n / 2 + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(owner_bf16_kernel, dim3((unsigned)blocks, (unsigned)P), dim3(256), 0,
-                       (hipStream_t)stream, t, n);
-    return hipGetLastError() == hipSuccess ? RING_OK : RING_EHIP;
+    // in place: a rank's chunk is rewritten only in a round after the ones
+    // that read it as input
+    return ring_reduce_scatter_bf16_out((const void* const*)part, part, out_shard, P, nd, ws, lay.gemm_off,
+                                        stream);
 }
 
 }  // namespace
