@@ -112,19 +112,28 @@ bool mlp_shape_ok(int P, int M, int D, int F) {
     return M % P == 0 && M % 256 == 0 && D % 128 == 0 && F % (128 * P) == 0;
 }
 
-// part[q][i] = sum over s = 0 .. S-1, in that order, of split[s P + q][i].
+// part[q][i] = sum over s = 0 .. S-1, in that order, of split[s P + q][i]
+// (n a multiple of 4; 16-byte accesses, all S loads of a vector in flight).
 struct PartTab {
     float* p[RING_MAX_RANKS];
 };
 
 __global__ __launch_bounds__(256) void sum_ranges_kernel(const float* split, PartTab t, int P, int S,
                                                              long long n) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
     const int q = blockIdx.y;
-    float* out = t.p[q];
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+    f4* out = (f4*)t.p[q];
+    const long long nv = n / 4;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nv;
          i += (long long)gridDim.x * blockDim.x) {
-        float a = split[(size_t)q * n + i];
-        for (int s = 1; s < S; ++s) a += split[((size_t)s * P + q) * n + i];
+        f4 x[kMaxSplit];
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s)
+            if (s < S) x[s] = __builtin_nontemporal_load((const f4*)(split + ((size_t)s * P + q) * n) + i);
+        f4 a = x[0];
+#pragma unroll
+        for (int s = 1; s < kMaxSplit; ++s)
+            if (s < S) a = a + x[s];
         out[i] = a;
     }
 }
