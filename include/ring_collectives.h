@@ -32,8 +32,8 @@
  *              Every call is asynchronous on that stream; nothing is
  *              allocated, printed or thrown by the library.  A call
  *              records no memset and leaves its flags zeroed, so it can be
- *              captured in a HIP graph and the graph replayed like the call
- *              (not in stepwise mode, whose launches are per round).
+ *              captured in a HIP graph and the graph replayed like the
+ *              call.
  *
  * Errors: argument errors are returned synchronously (RING_EINVAL,
  * RING_EUNSUPPORTED, RING_EWORKSPACE); a failed HIP launch returns RING_EHIP.
