@@ -189,32 +189,46 @@ def _to_dev(x, kind):
     return out
 
 
+CPU_BASELINE_SECONDS = 10.0   # the oracle runs its sample again until this much time has passed
+
+
 def _cpu_baseline(w, x):
-    """The oracle as it stands, single-threaded, on the same inputs."""
+    """The oracle as it stands, single-threaded, on the same inputs: the
+    whole workload, repeated until CPU_BASELINE_SECONDS have passed; the
+    rate is that of one pass."""
     import oracle
     P, n = x.shape
+
+    def run():
+        if w["op"] == "ppermute":
+            return oracle.ppermute(x)
+        if w["op"] == "reduce_scatter":
+            return oracle.reduce_scatter_bf16(x)[0] if w["kind"] == "bf16" else oracle.reduce_scatter(x)
+        if w["op"] == "psum_circulating":
+            return (oracle.psum_circulating_bf16(x) if w["kind"] == "bf16"
+                    else oracle.psum_circulating(x)[0])
+        if w["op"] == "all_gather":
+            return oracle.all_gather(x)
+        if w["op"] == "reduce_scatter_bidir":
+            return (oracle.reduce_scatter_bidir_bf16(x)[0] if w["kind"] == "bf16"
+                    else oracle.reduce_scatter_bidir(x))
+        if w["kind"] == "bf16":
+            return oracle.all_reduce_bf16(x)
+        return oracle.all_reduce(x)
+
     t0 = time.perf_counter()
-    if w["op"] == "ppermute":
-        want = oracle.ppermute(x)
-    elif w["op"] == "reduce_scatter":
-        want = oracle.reduce_scatter_bf16(x)[0] if w["kind"] == "bf16" else oracle.reduce_scatter(x)
-    elif w["op"] == "psum_circulating":
-        want = (oracle.psum_circulating_bf16(x) if w["kind"] == "bf16"
-                else oracle.psum_circulating(x)[0])
-    elif w["op"] == "all_gather":
-        want = oracle.all_gather(x)
-    elif w["op"] == "reduce_scatter_bidir":
-        want = (oracle.reduce_scatter_bidir_bf16(x)[0] if w["kind"] == "bf16"
-                else oracle.reduce_scatter_bidir(x))
-    elif w["kind"] == "bf16":
-        want = oracle.all_reduce_bf16(x)
-    else:
-        want = oracle.all_reduce(x)
-    dt = time.perf_counter() - t0
+    want = run()
+    reps = 1
+    while time.perf_counter() - t0 < CPU_BASELINE_SECONDS:
+        run()
+        reps += 1
+    total = time.perf_counter() - t0
+    dt = total / reps
     gbs = moved_bytes(w["op"], P, n, w["kind"]) / dt / 1e9
     return want, {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                  "seconds": round(dt, 3),
-                  "sample": "the whole workload (%d ranks x %d elements), one thread" % (P, n)}
+                  "seconds": round(total, 3),
+                  "sample": "the whole workload (%d ranks x %d elements), one thread, %d passes"
+                            % (P, n, reps)}
 
 
 def _gemm_main(args, w):
@@ -273,34 +287,37 @@ def _gemm_main(args, w):
     parity = None
     if not args.no_cpu:
         import oracle
-        t = time.perf_counter()
-        worst = 0.0
         if op == "gemm_rs":
-            rows = np.arange(0, M // P, (M // P) // 16)          # 16 sampled rows per rank
-            for r in range(P):
-                ref, mag = oracle.gemm_reduce_scatter_rows_f64(A, B, r, rows)
-                got = out[r].cpu().numpy()[rows].astype(np.float64)
-                worst = max(worst, float((np.abs(got - ref) / mag).max()))
+            rows = np.arange(0, M // P, max((M // P) // 256, 1))  # 256 sampled rows per rank
+            rows_f64 = lambda r: oracle.gemm_reduce_scatter_rows_f64(A, B, r, rows)
             sflop = 2.0 * P * P * len(rows) * Nn * K
             bound = (K + P) * 2.0 ** -24
-            sample = "%d output rows per rank (fp64 rows of sum_q A_q B_q, NumPy BLAS)" % len(rows)
+            what_rows = "fp64 rows of sum_q A_q B_q"
             same = True
         else:
-            rows = np.arange(0, M, M // 16)                     # 16 sampled rows per rank
-            for r in range(P):
-                ref, mag = oracle.all_gather_gemm_rows_f64(A, B, r, rows)
-                got = out[r].cpu().numpy()[rows].astype(np.float64)
-                worst = max(worst, float((np.abs(got - ref) / mag).max()))
+            rows = np.arange(0, M, max(M // 512, 1))            # 512 sampled rows per rank
+            rows_f64 = lambda r: oracle.all_gather_gemm_rows_f64(A, B, r, rows)
             sflop = 2.0 * P * len(rows) * Nn * K
             bound = K * 2.0 ** -24
-            sample = "%d output rows per rank (fp64 rows of A_full @ B_q, NumPy BLAS)" % len(rows)
+            what_rows = "fp64 rows of A_full @ B_q"
             gathered = A.reshape(M, K)
             same = all(np.array_equal(t_.view(torch.int16).cpu().numpy().view(np.uint16), gathered)
                        for t_ in full)
-        dt = time.perf_counter() - t
+        got = [out[r].cpu().numpy()[rows].astype(np.float64) for r in range(P)]
+        # the oracle's rows, again until CPU_BASELINE_SECONDS have passed
+        t = time.perf_counter()
+        refs = [rows_f64(r) for r in range(P)]
+        reps = 1
+        while time.perf_counter() - t < CPU_BASELINE_SECONDS:
+            for r in range(P):
+                rows_f64(r)
+            reps += 1
+        total = time.perf_counter() - t
+        dt = total / reps
+        worst = max(float((np.abs(got[r] - refs[r][0]) / refs[r][1]).max()) for r in range(P))
         cpu = {"value": round(sflop / dt / 1e12, 6), "unit": "TFLOP/s",
-               "cores": len(os.sched_getaffinity(0)), "kind": "oracle", "seconds": round(dt, 3),
-               "sample": sample}
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle", "seconds": round(total, 3),
+               "sample": "%d output rows per rank (%s, NumPy BLAS), %d passes" % (len(rows), what_rows, reps)}
         parity = bool(worst <= bound and same)
         print("[bench] sampled rows max normalised error %.3e (bound %.3e)%s"
               % (worst, bound, "" if op == "gemm_rs" else ", gathered A exact: %s" % same),
