@@ -189,12 +189,12 @@ def _to_dev(x, kind):
     return out
 
 
-CPU_BASELINE_SECONDS = 10.0   # the oracle runs its sample again until this much time has passed
+ORACLE_SAMPLE_SECONDS = 10.0   # the oracle runs its sample again until this much time has passed
 
 
 def _cpu_baseline(w, x):
     """The oracle as it stands, single-threaded, on the same inputs: the
-    whole workload, repeated until CPU_BASELINE_SECONDS have passed; the
+    whole workload, repeated until ORACLE_SAMPLE_SECONDS have passed; the
     rate is that of one pass."""
     import oracle
     P, n = x.shape
@@ -219,7 +219,7 @@ def _cpu_baseline(w, x):
     t0 = time.perf_counter()
     want = run()
     reps = 1
-    while time.perf_counter() - t0 < CPU_BASELINE_SECONDS:
+    while time.perf_counter() - t0 < ORACLE_SAMPLE_SECONDS:
         run()
         reps += 1
     total = time.perf_counter() - t0
@@ -304,11 +304,11 @@ def _gemm_main(args, w):
             same = all(np.array_equal(t_.view(torch.int16).cpu().numpy().view(np.uint16), gathered)
                        for t_ in full)
         got = [out[r].cpu().numpy()[rows].astype(np.float64) for r in range(P)]
-        # the oracle's rows, again until CPU_BASELINE_SECONDS have passed
+        # the oracle's rows, again until ORACLE_SAMPLE_SECONDS have passed
         t = time.perf_counter()
         refs = [rows_f64(r) for r in range(P)]
         reps = 1
-        while time.perf_counter() - t < CPU_BASELINE_SECONDS:
+        while time.perf_counter() - t < ORACLE_SAMPLE_SECONDS:
             for r in range(P):
                 rows_f64(r)
             reps += 1
