@@ -248,24 +248,30 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
             if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
             const unsigned abase = (unsigned)((p & 1) * G::kStageA);
             const unsigned bbase = (unsigned)(G::kBBase + (t & 1) * G::kStageB);
-            // The reads of k-step kk + 1 are issued before the MFMAs of k-step
-            // kk, each MFMA waiting only for the reads it consumes.  The
-            // scheduling fences hold that order; left alone, the compiler pairs
-            // each read with its use through one register set and exposes the
-            // LDS latency once per block.
+            // The reads of k-step kk + 1 are issued among the MFMAs of k-step
+            // kk (one after each), each MFMA waiting only for the reads it
+            // consumes.  The scheduling fences and groups hold that order; left
+            // alone, the compiler pairs each read with its use through one
+            // register set and exposes the LDS latency once per block.
             bf16x8 af[2][kMI], bf[2][G::NI];
             read_frags(abase, r * G::KK, bbase, 0, af[0], bf[0]);
 #pragma unroll
             for (int kk = 0; kk < G::KK; ++kk) {
                 if (kk + 1 < G::KK)
                     read_frags(abase, r * G::KK + kk + 1, bbase, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < G::NI; ++ni)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             af[kk & 1][mi], bf[kk & 1][ni], acc[mi][ni], 0, 0, 0);
+                if (kk + 1 < G::KK) {
+#pragma unroll
+                    for (int g = 0; g < kMI * G::NI; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // an MFMA,
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then an LDS read
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
