@@ -180,3 +180,28 @@ def test_watchdog_reports_timeout_and_recovers():
     _, gc, _ = _run(As, B, ws=ws)
     _, want_c = oracle.all_gather_gemm(As, B)
     np.testing.assert_array_equal(gc.view(np.uint32), want_c.view(np.uint32))
+
+
+def _random_shapes(seed, count):
+    """Seeded shapes the kernel accepts: P of 2..8 (5, 6 and 7 included),
+    row blocks of one or two 256-row tiles per rank, N a multiple of 128,
+    K a multiple of 64."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for P in (5, 6, 7, 3, 8, 2)[:count]:
+        out.append((P, 256 * P * int(rng.integers(1, 3)), 128 * int(rng.integers(1, 6)), 64 * int(rng.integers(1, 6))))
+    return out
+
+
+@pytest.mark.parametrize("P,M,N,K", _random_shapes(1420, 6))
+def test_random_shapes_integer_exact(P, M, N, K):
+    """Odd rank counts and sizes with the automatic tile width: the gathered
+    rows and every product bit, against the oracle."""
+    note("ag_gemm random P=%d M=%d N=%d K=%d" % (P, M, N, K))
+    rng = np.random.default_rng(1430 + P)
+    As = inputs.small_int_bf16(rng, (P, M // P, K))
+    B = inputs.small_int_bf16(rng, (P, K, N))
+    gf, gc, _ = _run(As, B)
+    want_full, want_c = oracle.all_gather_gemm(As, B)
+    np.testing.assert_array_equal(gf, want_full)
+    np.testing.assert_array_equal(gc.view(np.uint32), want_c.view(np.uint32))

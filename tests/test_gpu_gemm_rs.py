@@ -199,3 +199,27 @@ def test_repeated_calls_and_errors():
     with pytest.raises(N.RingError) as e:
         rc.gemm_reduce_scatter(a, b, out, ws=small)
     assert e.value.code == N.RING_EWORKSPACE
+
+
+def _random_shapes(seed, count):
+    """Seeded shapes the kernel accepts: P of 2..8 (5, 6 and 7 included),
+    row blocks of one or two 256-row tiles per rank, N a multiple of 128,
+    K a multiple of 64."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for P in (5, 6, 7, 3, 8, 2)[:count]:
+        out.append((P, 256 * P * int(rng.integers(1, 3)), 128 * int(rng.integers(1, 6)), 64 * int(rng.integers(1, 6))))
+    return out
+
+
+@pytest.mark.parametrize("P,M,N,K", _random_shapes(1400, 6))
+def test_random_shapes_integer_exact(P, M, N, K):
+    """Odd rank counts and sizes with the automatic tile width: every bit,
+    against the oracle."""
+    note("gemm_rs random P=%d M=%d N=%d K=%d" % (P, M, N, K))
+    rng = np.random.default_rng(1410 + P)
+    A = inputs.small_int_bf16(rng, (P, M, K))
+    B = inputs.small_int_bf16(rng, (P, K, N))
+    got, _ = _run(A, B)
+    want = oracle.gemm_reduce_scatter(A, B)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))

@@ -338,3 +338,28 @@ def test_watchdog_reports_timeout_and_recovers():
     _, h_ref, out_ref = oracle.tp_mlp_layer(x, w1, w2)
     np.testing.assert_array_equal(gh, h_ref)
     np.testing.assert_array_equal(go, out_ref)
+
+
+def _random_mlp_shapes(seed):
+    """Seeded layer shapes with rank counts 3, 5, 6 and 7: fused ones (256 P
+    or 512 P tokens) and, for P = 6, the unfused path (768 tokens: 128 per
+    rank; with an odd P the token count, a multiple of 256 and of P, is
+    always a multiple of 256 P).  D a multiple of 128, F of 128 P."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for P, M in ((3, 768 * int(rng.integers(1, 3))), (5, 1280), (6, 768), (6, 1536), (7, 1792)):
+        out.append((P, M, 128 * int(rng.integers(1, 3)), 128 * P * int(rng.integers(1, 4))))
+    return out
+
+
+@pytest.mark.parametrize("P,M,D,F", _random_mlp_shapes(1440))
+def test_random_shapes_integer_exact(P, M, D, F):
+    """Rank counts 3, 5, 6 and 7 on both paths with the automatic tile
+    widths: the gathered activations, h and the output, every bit."""
+    note("tp_mlp random P=%d M=%d D=%d F=%d" % (P, M, D, F))
+    x, w1, w2 = _int_operands(P, M, D, F, seed=1450 + P)
+    gf, gh, go, _ = _run(x, w1, w2)
+    full, h, out = oracle.tp_mlp_layer(x, w1, w2)
+    np.testing.assert_array_equal(gf, full)
+    np.testing.assert_array_equal(gh, h)
+    np.testing.assert_array_equal(go, out)
