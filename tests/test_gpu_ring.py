@@ -325,3 +325,60 @@ def test_full_size_bf16_p16_128Mi():
     ref, mag = oracle.rank_sum_f64(np.ascontiguousarray(x[:, idx]), bf16=True)
     err = np.abs(oracle.bf16_to_f32(got[0, idx]).astype(np.float64) - ref) / mag
     assert err.max() <= 1e-2
+
+
+# ---------------------------------------------------------------- more ranks
+@pytest.mark.parametrize("P,C", [(6, 2048 * 3 + 40), (7, 1001), (12, 4096 + 8), (32, 520), (64, 100)])
+@pytest.mark.parametrize("kind", ["f32", "i32", "bf16"])
+def test_more_ranks_every_collective(P, C, kind):
+    """Rank counts 6, 7, 12, 32 and 64 (the library's maximum), ragged
+    chunks: ppermute, reduce-scatter (each owner's chunk), all-gather,
+    all-reduce, the bidirectional reduce-scatter and the circulating psum,
+    every bit against the oracle."""
+    note("more ranks P=%d C=%d %s" % (P, C, kind))
+    n = P * C
+    rng = np.random.default_rng(1500 + P)
+    if kind == "i32":
+        x = rng.integers(-1000, 1000, size=(P, n), endpoint=True, dtype=np.int32)
+    elif kind == "f32":
+        x = rng.standard_normal((P, n), dtype=np.float32)
+    else:
+        x = oracle.bf16_from_f32((rng.standard_normal((P, n)) * 0.01).astype(np.float32))
+    dt = {"f32": torch.float32, "i32": torch.int32, "bf16": torch.bfloat16}[kind]
+    ws = rc.workspace(N.OP_REDUCE_SCATTER_BIDIR, P, n, dt)    # the ring calls, one after the other
+    ws_psum = rc.workspace(N.OP_PSUM_CIRCULATING, P, n, dt)
+    src = to_dev(x, kind)
+
+    dst = empty_ranks(P, n, kind)
+    rc.ppermute(src, dst)
+    np.testing.assert_array_equal(bits(to_host(dst, kind)), bits(oracle.ppermute(x)))
+
+    ar = oracle.all_reduce_bf16(x) if kind == "bf16" else oracle.all_reduce(x)
+    dst = empty_ranks(P, n, kind)
+    rc.all_reduce(src, dst, ws=ws)
+    np.testing.assert_array_equal(bits(to_host(dst, kind)), bits(ar))
+
+    for name, fn in (("reduce_scatter", rc.reduce_scatter), ("bidir", rc.reduce_scatter_bidir)):
+        dst = empty_ranks(P, n, kind)
+        fn(src, dst, ws=ws)
+        got = to_host(dst, kind)
+        if kind == "bf16":
+            want = (oracle.reduce_scatter_bf16(x)[0] if name == "reduce_scatter"
+                    else oracle.reduce_scatter_bidir_bf16(x)[0])
+        else:
+            want = oracle.reduce_scatter(x) if name == "reduce_scatter" else oracle.reduce_scatter_bidir(x)
+        for r in range(P):
+            np.testing.assert_array_equal(bits(got[r, r * C:(r + 1) * C]), bits(want[r, r * C:(r + 1) * C]),
+                                          err_msg="%s rank %d" % (name, r))
+
+    state = np.stack([x[r] for r in range(P)])
+    dst = to_dev(state, kind)
+    rc.all_gather(dst, ws=ws)
+    np.testing.assert_array_equal(bits(to_host(dst, kind)), bits(oracle.all_gather(state)))
+
+    dst = empty_ranks(P, n, kind)
+    rc.psum_circulating(src, dst, ws=ws_psum)
+    want = oracle.psum_circulating_bf16(x) if kind == "bf16" else oracle.psum_circulating(x)[0]
+    np.testing.assert_array_equal(bits(to_host(dst, kind)), bits(want))
+    torch.cuda.synchronize()
+    assert rc.last_error(ws)[0] == 0 and rc.last_error(ws_psum)[0] == 0
