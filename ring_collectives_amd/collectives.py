@@ -51,9 +51,17 @@ def workspace(op: int, P: int, n: int, dtype: torch.dtype, device=None) -> torch
                        device=device if device is not None else "cuda")
 
 
-def _ws(ws, op, P, n, dtype, device):
+def _ordered(ws: torch.Tensor, stream) -> torch.Tensor:
+    """A workspace just zero-filled on torch's current stream, made ready for
+    a call on `stream`: that stream waits for the fill."""
+    if stream is not None and stream != torch.cuda.current_stream(ws.device):
+        stream.wait_stream(torch.cuda.current_stream(ws.device))
+    return ws
+
+
+def _ws(ws, op, P, n, dtype, device, stream=None):
     if ws is None:
-        ws = workspace(op, P, n, dtype, device)
+        ws = _ordered(workspace(op, P, n, dtype, device), stream)
     return ws
 
 
@@ -77,7 +85,7 @@ def _rs_ar(fn, name, op, src, dst, ws, stream):
     pd = _ranks(dst, name, n, src[0].dtype)
     if len(pd) != P:
         raise ValueError("%s: src and dst rank counts differ" % name)
-    ws = _ws(ws, op, P, n, src[0].dtype, src[0].device)
+    ws = _ws(ws, op, P, n, src[0].dtype, src[0].device, stream)
     a, ka = N.ptr_array(ps)
     b, kb = N.ptr_array(pd)
     N.check(fn(a, b, P, n, _dtype(src[0]), ws.data_ptr(), ws.numel(), _stream(stream)), name)
@@ -125,7 +133,7 @@ def all_gather(dst, src=None, ws=None, stream=None):
         keep.append(ka)
     else:
         a = None
-    ws = _ws(ws, N.OP_ALL_GATHER, P, n, dst[0].dtype, dst[0].device)
+    ws = _ws(ws, N.OP_ALL_GATHER, P, n, dst[0].dtype, dst[0].device, stream)
     b, kb = N.ptr_array(pd)
     N.check(N.lib().ring_all_gather(a, b, P, n, _dtype(dst[0]), ws.data_ptr(), ws.numel(),
                                     _stream(stream)), "ring_all_gather")
@@ -144,7 +152,7 @@ def gemm_reduce_scatter(A, B, out, ws=None, stream=None):
     po = _ranks(out, "gemm_reduce_scatter", (M // P) * Nn, torch.float32)
     if ws is None:
         nb = int(N.lib().ring_workspace_bytes(N.OP_GEMM_REDUCE_SCATTER, P, M * Nn, N.RING_F32))
-        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=A[0].device)
+        ws = _ordered(torch.zeros(max(nb, 256), dtype=torch.uint8, device=A[0].device), stream)
     a, ka = N.ptr_array(pa)
     b, kb = N.ptr_array(pb)
     o, ko = N.ptr_array(po)
@@ -168,7 +176,7 @@ def all_gather_gemm(A_shard, B, A_full, C, ws=None, stream=None):
     pc = _ranks(C, "all_gather_gemm", M * Nn, torch.float32)
     if ws is None:
         nb = int(N.lib().ring_workspace_bytes(N.OP_ALL_GATHER_GEMM, P, M * Nn, N.RING_F32))
-        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=A_shard[0].device)
+        ws = _ordered(torch.zeros(max(nb, 256), dtype=torch.uint8, device=A_shard[0].device), stream)
     a, ka = N.ptr_array(pa)
     b, kb = N.ptr_array(pb)
     f, kf = N.ptr_array(pf)
@@ -203,7 +211,7 @@ def tp_mlp_layer(x_shard, W1, W2, x_full, h, out, ws=None, stream=None):
             _ranks(W2, "tp_mlp_layer", Fr * D, bf), _ranks(x_full, "tp_mlp_layer", M * D, bf),
             _ranks(h, "tp_mlp_layer", M * Fr, bf), _ranks(out, "tp_mlp_layer", Mq * D, bf)]
     if ws is None:
-        ws = tp_mlp_workspace(P, M, D, F, device=x_shard[0].device)
+        ws = _ordered(tp_mlp_workspace(P, M, D, F, device=x_shard[0].device), stream)
     arrs = [N.ptr_array(p_) for p_ in ptrs]
     N.check(N.lib().tp_mlp_layer(*[a_ for a_, _ in arrs], P, M, D, F, ws.data_ptr(), ws.numel(),
                                  _stream(stream)), "tp_mlp_layer")

@@ -382,3 +382,20 @@ def test_more_ranks_every_collective(P, C, kind):
     np.testing.assert_array_equal(bits(to_host(dst, kind)), bits(want))
     torch.cuda.synchronize()
     assert rc.last_error(ws)[0] == 0 and rc.last_error(ws_psum)[0] == 0
+
+
+def test_side_stream_with_a_fresh_workspace():
+    """A call on a stream other than torch's current one, with no workspace
+    given: the binding zero-fills one on the current stream and makes the
+    call's stream wait for it; the result is the oracle's."""
+    note("side stream, fresh workspace")
+    P = 4
+    x = inputs.to_chunk_major(inputs.small_f32(P, (8, 512)), P)
+    src = to_dev(x, "f32")
+    dst = empty_ranks(P, x.shape[1], "f32")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    ws = rc.all_reduce(src, dst, stream=side)
+    side.synchronize()
+    np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.all_reduce(x)))
+    assert rc.last_error(ws, stream=side)[0] == 0
