@@ -197,8 +197,8 @@ int ring_all_reduce(const void *const *src, void *const *dst, int P, size_t n,
  * matrix cores; the sum over ranks follows the fp32 ring reduce-scatter over
  * row-block chunks (chunk c = rows [c M/P, (c+1) M/P)).
  * Shapes this version accepts: M % (256 P) == 0, N % 128 == 0, K % 64 == 0.
- * Output tiles are 256 x 256 or 256 x 128 (see gemm_tile_n below); results
- * are the same bits either way.
+ * Output tiles are 256 x 256, 256 x 128 or 256 x 64 (see gemm_tile_n
+ * below); results are the same bits either way.
  */
 int gemm_reduce_scatter(const void *const *A, const void *const *B, void *const *out,
                         int P, int M, int N, int K, void *ws, size_t ws_bytes,
@@ -293,16 +293,17 @@ const char *ring_strerror(int code);
  *   drop_round     test hook: if >= 1, rank 0 never signals round drop_round
  *                  (all_gather_gemm: never flags its slices of that phase),
  *                  so the waits on it must end in RING_ETIMEOUT.
- *   gemm_tile_n    output tile width of the fused GEMMs: 64 or 128 (two
- *                  4-wave workgroups per compute unit; all_gather_gemm
- *                  takes 128 for 64), 256 (one 8-wave workgroup; needs
- *                  N % 256 == 0), or 0 to choose per call: 256 when the
- *                  256 x 256 tiles give every compute unit work (for
+ *   gemm_tile_n    output tile width of the fused GEMMs: 128 (two 4-wave
+ *                  workgroups per compute unit), 64 (one 4-wave workgroup
+ *                  with a deeper load pipeline; all_gather_gemm takes 128
+ *                  for 64), 256 (one 8-wave workgroup; needs N % 256 ==
+ *                  0), or 0 to choose per call: 256 when the 256 x 256
+ *                  tiles give every compute unit work (for
  *                  gemm_reduce_scatter, counting the tiles of all phases;
  *                  for all_gather_gemm, those of one chunk per rank), else
- *                  128 when the 256 x 128 ones do, else 64
- *                  (gemm_reduce_scatter and tp_mlp_layer; 128 for
- *                  all_gather_gemm).
+ *                  64 when the 256 x 64 ones number at most one per
+ *                  compute unit (gemm_reduce_scatter and tp_mlp_layer),
+ *                  else 128.
  */
 typedef struct {
     int tile_vecs;

@@ -27,31 +27,38 @@ constexpr int kMI = kWM / 32; // 32 x 32 MFMA blocks down a wave's part
 // 128 x 32.
 //   BN = 256, NW = 8: one workgroup per CU; a compute step covers 64 of K;
 //   BN = 128, NW = 4: two workgroups per CU; a step covers 32 of K;
-//   BN = 64,  NW = 4: as 128, on half the columns.
-// With enough tiles all run two waves per SIMD, so one wave's LDS reads and
-// waits overlap the other's matrix-core work.  The wide tile needs a third
-// less operand traffic per flop and wins once there are enough tiles to fill
-// the CUs; the narrow one is for products with too few 128-wide tiles to give
-// every CU one (a few hundred tokens), where it halves each tile's work.
+//   BN = 64,  NW = 4: one workgroup per CU, four stages deep; a step covers
+//                     64 of K.
+// With enough tiles the first two run two waves per SIMD, so one wave's LDS
+// reads and waits overlap the other's matrix-core work.  The wide tile needs
+// a third less operand traffic per flop and wins once there are enough tiles
+// to fill the CUs; the narrow one is for products with too few 128-wide tiles
+// to give every CU one (a few hundred tokens), where it halves each tile's
+// work.  There a CU holds one workgroup with one wave per SIMD and nothing
+// else to run while a stage loads, so the narrow tile keeps three stages in
+// flight instead of one: with one, every step waited out a whole load
+// latency.
 // A is staged 64 deep in K whatever the step, so every A row of a stage is one
 // whole 128-byte line: rows of 64 bytes cost about twice the fabric requests
 // per byte (each load instruction touches 16 half-used lines instead of 8
-// full ones).  With BN = 128 an A stage therefore serves two steps.  Two A
-// and two B buffers: 128 KiB for BN = 256, 80 KiB (twice per CU) for 128.
+// full ones).  With BN = 128 an A stage therefore serves two steps.  NS A and
+// NS B buffers: 128 KiB for BN = 256, 80 KiB (twice per CU) for 128, 160 KiB
+// for 64.
 template <int BN_, int NW_> struct Geo {
     static constexpr int BN = BN_;                       // output tile columns
     static constexpr int NW = NW_;                       // waves per workgroup
     static constexpr int WC = NW / 2;                    // waves across the tile
     static constexpr int BKA = 64;                       // K per A stage
-    static constexpr int BKB = BN == 256 ? 64 : 32;      // K per B stage = per step
+    static constexpr int BKB = BN == 128 ? 32 : 64;      // K per B stage = per step
+    static constexpr int NS = BN == 64 ? 4 : 2;          // buffers per operand
     static constexpr int R = BKA / BKB;                  // steps per A stage
     static constexpr int KK = BKB / 16;                  // MFMA k-steps per step
     static constexpr int WN = BN / WC;                   // columns of a wave's part
     static constexpr int NI = WN / 32;                   // 32 x 32 blocks across it
     static constexpr int kStageA = kBM * BKA * 2;        // bytes of one A buffer
     static constexpr int kStageB = BKB * BN * 2;         // bytes of one B buffer
-    static constexpr int kBBase = 2 * kStageA;           // B buffers follow the two A buffers
-    static constexpr int kLds = 2 * kStageA + 2 * kStageB;
+    static constexpr int kBBase = NS * kStageA;          // B buffers follow the A buffers
+    static constexpr int kLds = NS * (kStageA + kStageB);
     static constexpr int kARowBytes = BKA * 2;           // 128
     static constexpr int kAC = BKA / 8;                  // 16-byte chunks per A row
     static constexpr int kARows = 64 / kAC;              // A rows per 1-KiB load
@@ -63,7 +70,7 @@ template <int BN_, int NW_> struct Geo {
     static constexpr int kTile = kBM * BN;
     static constexpr int kEpiStride = WN + 4;            // LDS floats per row of the final transpose
     static constexpr int kEpiWave = 32 * kEpiStride;     // a wave's 32-row band
-    static constexpr int kWGsPerCU = BN == 256 ? 1 : 2;
+    static constexpr int kWGsPerCU = BN == 128 ? 2 : 1;
     // XOR applied to the 16-byte chunk index of A row m in LDS
     static __device__ __forceinline__ int swz_a(int m) { return (m >> 1) & 7; }
     // ... and of B row k (see the LDS layout below)
@@ -71,6 +78,7 @@ template <int BN_, int NW_> struct Geo {
     static_assert(kLds * kWGsPerCU <= 160 * 1024, "LDS");
     static_assert(NW * kEpiWave * 4 <= kLds, "epilogue LDS");
     static_assert(kBM % (NW * kARows) == 0 && BKB % (NW * kBRows) == 0, "load split");
+    static_assert(NS == 2 || R == 1, "a deep pipeline stages A and B together");
 };
 
 // Fragment order of a wave's part: the part-th 4 accumulators of block (mi, ni)
@@ -81,9 +89,9 @@ __device__ __forceinline__ unsigned frag_soff(int mi, int ni, int part) {
     return (unsigned)(((mi * G::NI + ni) * 4 + part) * 1024);
 }
 
-// LDS layout (bytes): A buffers at 0 and kStageA (256 rows m x 64 k, 128
-// bytes per row), B buffers at kBBase and kBBase + kStageB (BKB rows k x BN
-// n); no padding.  All are filled by direct global->LDS loads (one
+// LDS layout (bytes): A buffers at s kStageA (256 rows m x 64 k, 128 bytes
+// per row), B buffers at kBBase + s kStageB (BKB rows k x BN n), s = 0 ..
+// NS - 1; no padding.  All are filled by direct global->LDS loads (one
 // instruction = 64 lanes x 16 B = 1 KiB of consecutive LDS) and spread over
 // the banks by XOR-ing the 16-byte chunk index:
 //   A: chunk c of row m is stored at chunk c ^ ((m >> 1) & 7)
@@ -109,8 +117,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Wait until at most `n` of this wave's vector memory operations are in flight.
 __device__ __forceinline__ void wait_vm(int n) {
-    if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    if (n >= 20) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+    else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     else if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (n >= 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
     else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if (n >= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
@@ -224,56 +234,94 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
         }
     };
 
-    // Pipeline, in steps of BKB of K: A stage p serves steps R p .. R p + R - 1.
-    // At the start of step t (after the barrier, so every wave is done with
-    // step t - 1) the workgroup issues B stage t + 1 into the buffer step t - 1
-    // used and, on the first step of an A stage, A stage p + 1 into the
-    // buffer A stage p - 1 used.  B goes first, so at the top of the next
-    // step this wave can wait for its B loads and leave the A loads of the
-    // stage after in flight (R = 2, odd steps).  Past the end of K the issues
-    // re-read the last stage into the free buffer (never read again).
-    const int KT = kl / G::BKB;                // steps
-    const int KA = kl / G::BKA;                // A stages
-    __syncthreads();   // the previous tile's epilogue may still be reading LDS
-    issue_b(0, 0);
-    issue_a(0, 0);
-    for (int p = 0; p < KA; ++p) {
+    // One step of BKB of K from the A buffer at abase (its k-steps ka0 ..)
+    // and the B buffer at bbase.  The reads of k-step kk + 1 are issued
+    // among the MFMAs of k-step kk (one after each), each MFMA waiting only
+    // for the reads it consumes.  The scheduling fences and groups hold that
+    // order; left alone, the compiler pairs each read with its use through
+    // one register set and exposes the LDS latency once per block.
+    auto step = [&](unsigned abase, int ka0, unsigned bbase) {
+        bf16x8 af[2][kMI], bf[2][G::NI];
+        read_frags(abase, ka0, bbase, 0, af[0], bf[0]);
 #pragma unroll
-        for (int r = 0; r < G::R; ++r) {
-            const int t = p * G::R + r;
-            if (r == 0) wait_vm(0);                // B stage t and A stage p have landed
-            else wait_vm(G::kLoadsA);              // B stage t has; A stage p + 1 may be in flight
-            lds_barrier();                         // everyone's has; buffers of step t - 1 are free
-            issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
-            if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
-            const unsigned abase = (unsigned)((p & 1) * G::kStageA);
-            const unsigned bbase = (unsigned)(G::kBBase + (t & 1) * G::kStageB);
-            // The reads of k-step kk + 1 are issued among the MFMAs of k-step
-            // kk (one after each), each MFMA waiting only for the reads it
-            // consumes.  The scheduling fences and groups hold that order; left
-            // alone, the compiler pairs each read with its use through one
-            // register set and exposes the LDS latency once per block.
-            bf16x8 af[2][kMI], bf[2][G::NI];
-            read_frags(abase, r * G::KK, bbase, 0, af[0], bf[0]);
+        for (int kk = 0; kk < G::KK; ++kk) {
+            if (kk + 1 < G::KK)
+                read_frags(abase, ka0 + kk + 1, bbase, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
 #pragma unroll
-            for (int kk = 0; kk < G::KK; ++kk) {
-                if (kk + 1 < G::KK)
-                    read_frags(abase, r * G::KK + kk + 1, bbase, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+            for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-                for (int mi = 0; mi < kMI; ++mi)
+                for (int ni = 0; ni < G::NI; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[kk & 1][mi], bf[kk & 1][ni], acc[mi][ni], 0, 0, 0);
+            if (kk + 1 < G::KK) {
 #pragma unroll
-                    for (int ni = 0; ni < G::NI; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            af[kk & 1][mi], bf[kk & 1][ni], acc[mi][ni], 0, 0, 0);
-                if (kk + 1 < G::KK) {
-#pragma unroll
-                    for (int g = 0; g < kMI * G::NI; ++g) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // an MFMA,
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then an LDS read
-                    }
+                for (int g = 0; g < kMI * G::NI; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // an MFMA,
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then an LDS read
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int KT = kl / G::BKB;                // steps
+    __syncthreads();   // the previous tile's epilogue may still be reading LDS
+    if constexpr (G::NS == 2) {
+        // Two buffers, in steps of BKB of K: A stage p serves steps R p .. R p
+        // + R - 1.  At the start of step t (after the barrier, so every wave
+        // is done with step t - 1) the workgroup issues B stage t + 1 into the
+        // buffer step t - 1 used and, on the first step of an A stage, A stage
+        // p + 1 into the buffer A stage p - 1 used.  B goes first, so at the
+        // top of the next step this wave can wait for its B loads and leave
+        // the A loads of the stage after in flight (R = 2, odd steps).  Past
+        // the end of K the issues re-read the last stage into the free buffer
+        // (never read again).
+        const int KA = kl / G::BKA;            // A stages
+        issue_b(0, 0);
+        issue_a(0, 0);
+        for (int p = 0; p < KA; ++p) {
+#pragma unroll
+            for (int r = 0; r < G::R; ++r) {
+                const int t = p * G::R + r;
+                if (r == 0) wait_vm(0);            // B stage t and A stage p have landed
+                else wait_vm(G::kLoadsA);          // B stage t has; A stage p + 1 may be in flight
+                lds_barrier();                     // everyone's has; buffers of step t - 1 are free
+                issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
+                if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
+                step((unsigned)((p & 1) * G::kStageA), r * G::KK,
+                     (unsigned)(G::kBBase + (t & 1) * G::kStageB));
+            }
+        }
+    } else {
+        // NS buffers, A and B staged together (R = 1): stages 0 .. NS - 2 are
+        // issued up front; at the start of step t (after the barrier, so every
+        // wave is done with step t - 1) stage t + NS - 1 goes into the buffer
+        // step t - 1 used.  Stages past the end of K are not issued, so the
+        // wait allows only the stages after t that were.  Loads return in
+        // issue order and nothing else is counted (the previous tile's stores
+        // are drained first), so waiting for at most (stages after t) x
+        // (loads per stage) to be in flight waits for exactly stage t.
+        constexpr int L = G::kLoadsA + G::kLoadsB;  // this wave's loads per stage
+        wait_vm(0);
+#pragma unroll
+        for (int s = 0; s < G::NS - 1; ++s)
+            if (s < KT) {
+                issue_b(s, s);
+                issue_a(s, s);
+            }
+        int slot = 0;                          // buffer of step t
+        for (int t = 0; t < KT; ++t) {
+            const int after = KT - 1 - t < G::NS - 2 ? KT - 1 - t : G::NS - 2;
+            wait_vm(after * L);                // stage t has landed
+            lds_barrier();                     // everyone's has; the buffer of step t - 1 is free
+            const int nx = t + G::NS - 1;
+            if (nx < KT) {
+                const int ns = slot == 0 ? G::NS - 1 : slot - 1;
+                issue_b(nx, ns);
+                issue_a(nx, ns);
+            }
+            step((unsigned)(slot * G::kStageA), 0, (unsigned)(G::kBBase + slot * G::kStageB));
+            slot = slot + 1 == G::NS ? 0 : slot + 1;
         }
     }
     wait_vm(0);        // the trailing loads have landed

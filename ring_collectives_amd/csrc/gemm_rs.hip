@@ -283,10 +283,13 @@ int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, in
         // Wide tiles need less operand traffic per flop but make half as
         // many work items; they pay off once there is at least one wide
         // item per CU (the items of all phases count: phases overlap).
-        // Below one 128-wide item per CU, 64-wide tiles spread the work
-        // over twice as many CUs.
+        // When even the 64-wide items number at most one per CU, those
+        // spread the work over more CUs.  A CU holds one 64-wide workgroup,
+        // so with more of them some CUs would run two in turn, and the
+        // 128-wide tiles, two workgroups per CU at once, are faster.
         const long long items128 = (long long)P * (batched ? ksplit : P) * prm.tm_chunk * (N / 128);
-        bn = (N % 256 == 0 && items128 / 2 >= (long long)di.cus) ? 256 : items128 >= (long long)di.cus ? 128 : 64;
+        const long long cus = di.cus;
+        bn = (N % 256 == 0 && items128 / 2 >= cus) ? 256 : 2 * items128 <= cus ? 64 : 128;
     }
     if (bn == 256 && N % 256) return RING_EUNSUPPORTED;
     if (epi != EPI_F32 && epi != EPI_BF16 && epi != EPI_GELU_BF16) return RING_EINVAL;
