@@ -27,7 +27,12 @@
  *              first use (ring_workspace_init, or any zero fill); every call
  *              that completes normally leaves its flag table zero again, so
  *              back-to-back calls on one stream need no re-initialisation.
- *              Calls that share a workspace must be ordered (same stream).
+ *              The one exception: a bf16 reduce-scatter or all-reduce that
+ *              runs its flag rounds leaves its fp32 partial sums in the
+ *              workspace, so a call of another shape or dtype, whose flags
+ *              or words may lie there, needs the workspace zero-filled
+ *              again first.  Calls that share a workspace must be ordered
+ *              (same stream).
  *   - stream   a hipStream_t passed as void* (NULL = the default stream).
  *              Every call is asynchronous on that stream; nothing is
  *              allocated, printed or thrown by the library.  A call
@@ -80,6 +85,14 @@ enum {
  * RING_OP_GEMM_REDUCE_SCATTER and RING_OP_ALL_GATHER_GEMM pass n = M * N
  * (elements of one rank's product) and dtype RING_F32.  Returns 0 for invalid arguments (and for ppermute,
  * which needs none).
+ * The one-way ring collectives of small calls (chunks of at most 256 KiB,
+ * and 2 (P - 1) n at most 8 Mi) also get one 8-byte word per element and
+ * round of the ring, 16 (P - 1) n bytes: the low-latency rounds (see
+ * ll_max_chunk_bytes below) pass every value on in such a word, together
+ * with its ready mark, instead of behind a per-tile flag.  A call runs them
+ * only when its workspace holds those words; a smaller workspace that holds
+ * its flag table (one sized for a larger call, say) serves it with the flag
+ * rounds.
  */
 size_t ring_workspace_bytes(int op, int P, size_t n, int dtype);
 
@@ -304,6 +317,14 @@ const char *ring_strerror(int code);
  *                  64 when the 256 x 64 ones number at most one per
  *                  compute unit (gemm_reduce_scatter and tp_mlp_layer),
  *                  else 128.
+ *   ll_max_chunk_bytes  the one-way reduce-scatter, all-gather and
+ *                  all-reduce run their rounds in the low-latency form when
+ *                  a chunk (n / P elements) takes at most this many bytes
+ *                  and the workspace holds the words (see
+ *                  ring_workspace_bytes); 0 turns that off.  0 .. 262144
+ *                  (default).  Same chunks, same additions, same results;
+ *                  a round costs about half the latency.  Not in stepwise
+ *                  mode.
  */
 typedef struct {
     int tile_vecs;
@@ -313,6 +334,7 @@ typedef struct {
     int stepwise;
     int drop_round;
     int gemm_tile_n;
+    int ll_max_chunk_bytes;
 } ring_tuning_t;
 
 void ring_get_tuning(ring_tuning_t *t);

@@ -47,7 +47,7 @@ class Tuning(ctypes.Structure):
     _fields_ = [("tile_vecs", ctypes.c_int), ("waves_per_cu", ctypes.c_int),
                 ("map_mode", ctypes.c_int), ("timeout_s", ctypes.c_double),
                 ("stepwise", ctypes.c_int), ("drop_round", ctypes.c_int),
-                ("gemm_tile_n", ctypes.c_int)]
+                ("gemm_tile_n", ctypes.c_int), ("ll_max_chunk_bytes", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

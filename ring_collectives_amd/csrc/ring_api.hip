@@ -26,7 +26,18 @@ int elems_per_vec(int dtype) { return dtype == RING_BF16 ? 4 : (elem_bytes(dtype
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-RingWs ring_ws_layout(int P, size_t n, int dtype) {
+// Whether a call's workspace holds low-latency words: chunks of at most
+// kLlMaxChunkBytes, and the words of all 2(P-1) rounds (P n of them) within
+// kLlMaxBytes.  Fixed by the shape alone, so a workspace sized once serves
+// whatever the tuning says at call time.
+static bool ll_fits(int P, size_t n, int dtype) {
+    if (P < 2 || !elem_bytes(dtype)) return false;
+    const size_t C = n / (size_t)P;
+    return C * (size_t)elem_bytes(dtype) <= kLlMaxChunkBytes &&
+           2 * (size_t)(P - 1) * n * sizeof(unsigned long long) <= kLlMaxBytes;
+}
+
+RingWs ring_ws_layout(int P, size_t n, int dtype, bool with_ll) {
     RingWs w;
     const size_t C = n / (size_t)P;
     const size_t tile_min = (size_t)kWave * kMinTileVecs * elems_per_vec(dtype);
@@ -36,7 +47,9 @@ RingWs ring_ws_layout(int P, size_t n, int dtype) {
     const size_t rows = P > 1 ? 2 * (size_t)(P - 1) : 1;
     w.flags_off = kStatusBytes;
     w.flags_bytes = align_up(rows * (size_t)P * (T ? T : 1) * kFlagStride * sizeof(int), 256);
-    w.carry_off = w.flags_off + w.flags_bytes;
+    w.ll_off = w.flags_off + w.flags_bytes;
+    w.ll_bytes = with_ll && ll_fits(P, n, dtype) ? align_up(rows * n * sizeof(unsigned long long), 256) : 0;
+    w.carry_off = w.ll_off + w.ll_bytes;
     w.carry_bytes = dtype == RING_BF16 ? align_up((size_t)P * n * sizeof(float), 256) : 0;
     w.total = w.carry_off + w.carry_bytes;
     return w;
@@ -66,7 +79,8 @@ static bool tuning_valid(const ring_tuning_t& x) {
     return (x.tile_vecs == 4 || x.tile_vecs == 8 || x.tile_vecs == 16) && x.waves_per_cu >= 4 &&
            x.waves_per_cu <= 16 && (x.map_mode == 0 || x.map_mode == 2) && x.timeout_s > 0 &&
            x.timeout_s < 3600 && (x.stepwise == 0 || x.stepwise == 1) && x.drop_round >= 0 &&
-           (x.gemm_tile_n == 0 || x.gemm_tile_n == 64 || x.gemm_tile_n == 128 || x.gemm_tile_n == 256);
+           (x.gemm_tile_n == 0 || x.gemm_tile_n == 64 || x.gemm_tile_n == 128 || x.gemm_tile_n == 256) &&
+           x.ll_max_chunk_bytes >= 0 && (size_t)x.ll_max_chunk_bytes <= kLlMaxChunkBytes;
 }
 
 static ring_tuning_t& tuning_ref() {
@@ -83,6 +97,7 @@ static ring_tuning_t& tuning_ref() {
         d.stepwise = 0;
         d.drop_round = 0;
         d.gemm_tile_n = 0;
+        d.ll_max_chunk_bytes = (int)kLlMaxChunkBytes;
         ring_tuning_t x = d;
         x.tile_vecs = env_int("RING_TILE_VECS", d.tile_vecs);
         x.waves_per_cu = env_int("RING_WAVES_PER_CU", d.waves_per_cu);
@@ -91,6 +106,7 @@ static ring_tuning_t& tuning_ref() {
         if (to && *to) x.timeout_s = atof(to);
         x.stepwise = env_int("RING_STEPWISE", 0);
         x.gemm_tile_n = env_int("RING_GEMM_TILE_N", d.gemm_tile_n);
+        x.ll_max_chunk_bytes = env_int("RING_LL_MAX_CHUNK_BYTES", d.ll_max_chunk_bytes);
         return tuning_valid(x) ? x : d;
     }();
     return t;
@@ -164,16 +180,24 @@ static hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 static int run_ring(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream, int k_begin, int k_end,
                     int compact_src, int bidir = 0, void* const* out16 = nullptr) {
-    const RingWs lay = ring_ws_layout(P, n, dtype);
     // reduce-scatter rounds of bf16 data carry fp32 partial sums
     const bool need_carry = dtype == RING_BF16 && (bidir || k_begin < P - 1);
+    auto need = [&](const RingWs& l) { return need_carry ? l.total : l.total - l.carry_bytes; };
     if (!ws || ((uintptr_t)ws & 255)) return RING_EWORKSPACE;
-    if (ws_bytes < (need_carry ? lay.total : lay.total - lay.carry_bytes)) return RING_EWORKSPACE;
     const ring_tuning_t tu = tuning();
     const DevInfo di = dev_info();
     const int esz = elem_bytes(dtype);
     const long long C = (long long)(n / (size_t)P);
-    const int tile = kWave * tu.tile_vecs * elems_per_vec(dtype);
+    // Low-latency rounds for small one-way calls (not in stepwise mode,
+    // whose rounds are separate launches ordered by the stream), when the
+    // workspace holds their words: the size ring_workspace_bytes gives for
+    // this call does; one sized for a larger call may only cover the flags.
+    const RingWs with_ll = ring_ws_layout(P, n, dtype, true);
+    const bool ll = !bidir && !tu.stepwise && with_ll.ll_bytes && ws_bytes >= need(with_ll) &&
+                    (size_t)C * (size_t)esz <= (size_t)tu.ll_max_chunk_bytes;
+    const RingWs lay = ll ? with_ll : ring_ws_layout(P, n, dtype, false);
+    if (ws_bytes < need(lay)) return RING_EWORKSPACE;
+    const int tile = ll ? kWave * kLlVec : kWave * tu.tile_vecs * elems_per_vec(dtype);
     const long long h = C - C / 2;   // top half of a chunk (bidirectional)
     const int T_top = bidir ? (int)((h + tile - 1) / tile) : 0;
     const int T = bidir ? T_top + (int)((C - h + tile - 1) / tile) : (int)((C + tile - 1) / tile);
@@ -193,7 +217,8 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
             if ((uintptr_t)out16[r] & 15) vec_ok = 0;
         }
     }
-    prm.carry = need_carry ? (float*)((char*)ws + lay.carry_off) : nullptr;
+    prm.carry = need_carry && !ll ? (float*)((char*)ws + lay.carry_off) : nullptr;
+    prm.ll = ll ? (unsigned long long*)((char*)ws + lay.ll_off) : nullptr;
     prm.flags = (int*)((char*)ws + lay.flags_off);
     prm.status = (Status*)ws;
     prm.n = (long long)n;
@@ -212,13 +237,13 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
 
     // Grid: every wave must be resident at once (waves wait on each other).
     // Stay within half the occupancy limit: margin for anything else resident.
-    int occ = ring_blocks_per_cu(dtype, tu.tile_vecs, bidir);
+    int occ = ring_blocks_per_cu(dtype, tu.tile_vecs, ll ? 3 : bidir);
     if (occ < 1) return RING_EHIP;
     int bpc = (tu.waves_per_cu + kWavesPerBlock - 1) / kWavesPerBlock;
     if (bpc > occ / 2) bpc = occ / 2 > 0 ? occ / 2 : 1;
     const long long max_blocks = (long long)di.cus * bpc;
     const long long max_waves = max_blocks * kWavesPerBlock;
-    int map_mode = tu.map_mode;
+    int map_mode = ll ? 0 : tu.map_mode;
     long long blocks = 0;
     int W = 0;
     if (map_mode == 2) {

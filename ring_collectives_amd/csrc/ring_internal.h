@@ -18,6 +18,15 @@ constexpr int kFlagStride = 16;      // ints between flags: one flag per 64 byte
 constexpr size_t kStatusBytes = 256; // error word + info, at offset 0 of a workspace
 constexpr int kMinTileVecs = 4;      // smallest tile: 4 vectors of 16 B per lane
 
+// Low-latency rounds: a value travels to the right neighbour inside an 8-byte
+// word together with a ready mark, so the neighbour polls the data itself
+// instead of a flag it may read only after the data was stored.  Calls whose
+// chunks hold at most kLlMaxChunkBytes (and whose words take at most
+// kLlMaxBytes) get a region of such words in their workspace.
+constexpr size_t kLlMaxChunkBytes = 256 << 10;
+constexpr size_t kLlMaxBytes = 64 << 20;
+constexpr int kLlVec = 4;            // words per lane per tile position
+
 // The error header every workspace starts with.
 struct Status {
     int code;   // RING_OK or RING_ETIMEOUT
@@ -52,6 +61,8 @@ struct RingParams {
     long long h;                      // elements in the top half of a chunk
     // fp32 reduce-scatter with a bf16 result only (kDtF32Bf16Out)
     void* out16[RING_MAX_RANKS];      // the owner's chunk, rounded once to bf16
+    // low-latency rounds only: [2(P-1)][P][C] words (value | 1 << 32), or null
+    unsigned long long* ll;
 };
 
 // Internal element type of the ring launchers: an fp32 reduce-scatter whose
@@ -61,13 +72,14 @@ constexpr int kDtF32Bf16Out = 16;
 // Workspace layout of the ring collectives for (P, n, dtype).
 struct RingWs {
     size_t flags_off, flags_bytes;
-    size_t carry_off, carry_bytes;
+    size_t ll_off, ll_bytes;          // low-latency words (0 bytes: calls too large for them)
+    size_t carry_off, carry_bytes;    // last, so a call that needs no carry may omit it
     size_t total;
 };
 
 int elem_bytes(int dtype);
 int elems_per_vec(int dtype);
-RingWs ring_ws_layout(int P, size_t n, int dtype);
+RingWs ring_ws_layout(int P, size_t n, int dtype, bool with_ll = true);
 
 // Tuning knobs: defaults, overridable by RING_* environment variables at
 // first use and by ring_set_tuning().
@@ -78,8 +90,8 @@ hipError_t launch_copy(const void* const* src, void* const* dst, int P, size_t b
                        int shift, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_ring(RingParams& prm, int dtype, int tile_vecs, int grid_blocks,
-                       hipStream_t s);   // prm.bidir selects the bidirectional kernel
-int ring_blocks_per_cu(int dtype, int tile_vecs, int kind);   // occupancy: 0 ring, 1 bidir, 2 psum
+                       hipStream_t s);   // prm.bidir selects the bidirectional kernel, prm.ll the low-latency one
+int ring_blocks_per_cu(int dtype, int tile_vecs, int kind);   // occupancy: 0 ring, 1 bidir, 2 psum, 3 low-latency
 
 // The fp32 ring reduce-scatter of src into dst (the ring's partial sums; dst
 // may be src), with the owner's chunk of the sum rounded once to bf16 into

@@ -9,6 +9,8 @@
 //                         chunk travel both ways round the ring).
 //   * ring_psum_kernel  : the circulating-input psum (every input once round
 //                         the ring, double receive slots, capacity flags).
+//   * ring_ll_kernel    : the one-way rounds for small calls, each value
+//                         passed on with its own ready mark.
 //   * fill_zero_kernel  : workspace initialisation.
 //
 // Ring schedule ("全归约 3：Ring——每步大小恒定", Walkthrough).  P ranks, chunk
@@ -739,6 +741,198 @@ __global__ __launch_bounds__(kBlock) void ring_psum_kernel(RingParams p) {
 }
 
 // ---------------------------------------------------------------- copy / fill
+// ---------------------------------------------------------------- low-latency rounds
+// The one-way ring's rounds (same chunks, same additions in the same order)
+// for calls small enough that a round's time is its latency.  The value rank
+// r passes right in round k, for element o of the round's chunk, travels in
+// the 8-byte word (k, r, o) of p.ll as value | 1 << 32.  The right neighbour
+// polls that word until the mark is set and then clears it (it is the word's
+// only reader), so a finished launch leaves every word zero.  An aligned
+// 8-byte access is single-copy atomic, so a word never shows the mark with a
+// stale value.  With flags a round costs four trips to the device coherence
+// point one after the other (the data store and its acknowledgement, the
+// flag add, the poll that sees it, the data load); here two (the store, the
+// poll that returns the data).  fp32 partial sums of bf16 data travel as
+// fp32, bf16 values of the all-gather rounds in the low half of the value.
+// The outputs go to dst as in the flag rounds: the partial sums of fp32 and
+// int32 reduce-scatter rounds too, the owner's sum, every all-gather copy.
+// Tile position j of a chunk covers offsets 256 j + 64 i + lane, i < 4, so
+// each access instruction of a wave touches consecutive elements.  Waves
+// take positions and rounds in the flag kernel's order, so the argument
+// that every wave can finish is the same.
+typedef unsigned long long u64;
+constexpr int kLlTile = kWave * kLlVec;   // elements per tile position
+
+// Every access goes through a buffer view of one chunk (or one round's
+// words), so a lane past the chunk's end reads zeros and its stores are
+// dropped by the hardware: no branch per element, and the compiler keeps
+// each group of loads in flight together.
+__device__ __forceinline__ rsrc_t ll_words(const RingParams& p, int k, int r) {
+    return tile_view(p.ll + ((size_t)k * p.P + r) * (size_t)p.C, p.C * 8);
+}
+template <int DT> __device__ __forceinline__ rsrc_t ll_chunk(const void* base, long long e0, long long len) {
+    constexpr int ESZ = DT == DT_BF16 ? 2 : 4;
+    return tile_view((const char*)base + e0 * ESZ, len * ESZ);
+}
+// Element o of a view as 32 bits (bf16 zero-extended), and back.
+template <int DT> __device__ __forceinline__ unsigned ll_ld(rsrc_t v, long long o) {
+    if constexpr (DT == DT_BF16) return ld2<POL_PLAIN>(v, (unsigned)o * 2u);
+    else return ld4<POL_PLAIN>(v, (unsigned)o * 4u);
+}
+template <int DT> __device__ __forceinline__ void ll_st(rsrc_t v, long long o, unsigned x) {
+    if constexpr (DT == DT_BF16) st2<POL_PLAIN>((unsigned short)x, v, (unsigned)o * 2u);
+    else st4<POL_PLAIN>(x, v, (unsigned)o * 4u);
+}
+
+// Round k of rank r waits for the words (k - 1, from) at this lane's
+// offsets o0 + 64 i (those below C: the others read as zero and count as
+// ready), takes their values and clears them.  Every poll reloads all four
+// words under one wait.  False if the launch is being abandoned (a timeout
+// here or elsewhere).
+__device__ bool ll_recv(const RingParams& p, int k, int from, long long o0, unsigned (&v)[kLlVec], int r,
+                        int j, int lane) {
+    const rsrc_t w = ll_words(p, k - 1, from);
+    bool past[kLlVec];                     // offsets past the chunk: always ready
+#pragma unroll
+    for (int i = 0; i < kLlVec; ++i) past[i] = o0 + i * kWave >= p.C;
+    u32x2 x[kLlVec];
+    auto poll = [&] {
+#pragma unroll
+        for (int i = 0; i < kLlVec; ++i) x[i] = ld8<POL_DEV>(w, (unsigned)(o0 + i * kWave) * 8u);
+        bool all = true;
+#pragma unroll
+        for (int i = 0; i < kLlVec; ++i) all = all & (past[i] | (x[i][1] != 0u));
+        return all;
+    };
+    if (!__all(poll())) {
+        const long long t0 = wall_clock64();
+        unsigned spins = 0;
+        for (;;) {
+            __builtin_amdgcn_s_sleep(1);
+            if (__all(poll())) break;
+            if ((++spins & 31u) == 0) {
+                if (__hip_atomic_load(&p.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+                    return false;
+                if (wall_clock64() - t0 > p.spin_limit) {
+                    if (lane == 0) report_timeout(p.status, r, k, j);
+                    return false;
+                }
+            }
+        }
+    }
+    const u32x2 zero = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kLlVec; ++i) {
+        v[i] = x[i][0];
+        st8<POL_DEV>(zero, w, (unsigned)(o0 + i * kWave) * 8u);
+    }
+    return true;
+}
+
+// Pass this lane's values of round k on to the right neighbour.
+__device__ __forceinline__ void ll_send(const RingParams& p, int k, int r, long long o0,
+                                        const unsigned (&v)[kLlVec]) {
+    const rsrc_t w = ll_words(p, k, r);
+#pragma unroll
+    for (int i = 0; i < kLlVec; ++i) {
+        const u32x2 x = {v[i], 1u};
+        st8<POL_DEV>(x, w, (unsigned)(o0 + i * kWave) * 8u);
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void ring_ll_kernel(RingParams p) {
+    int r, w;
+    if (!map_wave(p, r, w)) return;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int P = p.P;
+    const int left = left_of(r, P);
+    const long long C = p.C;
+    for (int j = w; j < p.T; j += p.waves_per_rank) {
+        const long long o0 = (long long)j * kLlTile + lane;
+        for (int k = p.k_begin; k < p.k_end; ++k) {
+            const bool send = k + 1 < p.k_end && !(r == 0 && k + 1 == p.drop_round);
+            unsigned v[kLlVec];
+            if (k < P - 1) {
+                // reduce-scatter round s = k: chunk (r - k - 2) mod P
+                const long long e0 = (long long)rs_chunk(r, k, P) * C;
+                const rsrc_t own = ll_chunk<DT>(p.src[r], e0, C);
+                unsigned a[kLlVec];
+#pragma unroll
+                for (int i = 0; i < kLlVec; ++i) a[i] = ll_ld<DT>(own, o0 + i * kWave);
+                if (k == p.k_begin) {   // the left neighbour's input: complete before the launch
+                    const rsrc_t in = ll_chunk<DT>(p.src[left], e0, C);
+#pragma unroll
+                    for (int i = 0; i < kLlVec; ++i) {
+                        const unsigned x = ll_ld<DT>(in, o0 + i * kWave);
+                        v[i] = DT == DT_BF16 ? x << 16 : x;
+                    }
+                } else if (!ll_recv(p, k, left, o0, v, r, j, lane)) {
+                    return;
+                }
+#pragma unroll
+                for (int i = 0; i < kLlVec; ++i) {
+                    if constexpr (DT == DT_I32) v[i] = v[i] + a[i];
+                    else if constexpr (DT == DT_BF16)
+                        v[i] = __float_as_uint(__uint_as_float(v[i]) + __uint_as_float(a[i] << 16));
+                    else v[i] = __float_as_uint(__uint_as_float(v[i]) + __uint_as_float(a[i]));
+                }
+                const bool last = k == P - 2;   // this rank owns the chunk
+                const rsrc_t out = ll_chunk<DT>(p.dst[r], e0, C);
+                if constexpr (DT == DT_BF16) {
+                    if (last) {
+#pragma unroll
+                        for (int i = 0; i < kLlVec; ++i) {
+                            v[i] = bf16_rne(__uint_as_float(v[i]));   // the all-gather passes bf16 on
+                            ll_st<DT>(out, o0 + i * kWave, v[i]);
+                        }
+                    }
+                } else if constexpr (DT == DT_F32B) {
+                    if (last) {
+                        const rsrc_t o16 = tile_view(p.out16[r], C * 2);
+#pragma unroll
+                        for (int i = 0; i < kLlVec; ++i)
+                            st2<POL_PLAIN>((unsigned short)bf16_rne(__uint_as_float(v[i])), o16,
+                                           (unsigned)(o0 + i * kWave) * 2u);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < kLlVec; ++i) ll_st<DT>(out, o0 + i * kWave, v[i]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kLlVec; ++i) ll_st<DT>(out, o0 + i * kWave, v[i]);
+                }
+            } else {
+                // all-gather round t = k - (P - 1): chunk (r - t - 1) mod P
+                const int t = k - (P - 1);
+                const long long e0 = (long long)ag_chunk(r, t, P) * C;
+                if (k == p.k_begin) {   // inputs, complete before the launch
+                    if (p.compact_src) {   // place this rank's own piece, take the left one's
+                        const rsrc_t mine = ll_chunk<DT>(p.src[r], 0, C);
+                        const rsrc_t place = ll_chunk<DT>(p.dst[r], (long long)r * C, C);
+                        const rsrc_t in = ll_chunk<DT>(p.src[left], 0, C);
+#pragma unroll
+                        for (int i = 0; i < kLlVec; ++i) {
+                            ll_st<DT>(place, o0 + i * kWave, ll_ld<DT>(mine, o0 + i * kWave));
+                            v[i] = ll_ld<DT>(in, o0 + i * kWave);
+                        }
+                    } else {
+                        const rsrc_t in = ll_chunk<DT>(p.dst[left], e0, C);
+#pragma unroll
+                        for (int i = 0; i < kLlVec; ++i) v[i] = ll_ld<DT>(in, o0 + i * kWave);
+                    }
+                } else if (!ll_recv(p, k, left, o0, v, r, j, lane)) {
+                    return;
+                }
+                const rsrc_t out = ll_chunk<DT>(p.dst[r], e0, C);
+#pragma unroll
+                for (int i = 0; i < kLlVec; ++i) ll_st<DT>(out, o0 + i * kWave, v[i]);
+            }
+            if (send) ll_send(p, k, r, o0, v);
+        }
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void fill_zero_kernel(unsigned* p, long long words, long long tail_bytes) {
     const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const long long nth = (long long)gridDim.x * blockDim.x;
@@ -865,7 +1059,22 @@ static int blocks_per_cu_dt(int tile_vecs, int kind) {
     }
 }
 
+template <int DT>
+static int blocks_per_cu_ll() {
+    int nb = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ring_ll_kernel<DT>, kBlock, 0) == hipSuccess ? nb : 0;
+}
+
 int ring_blocks_per_cu(int dtype, int tile_vecs, int kind) {
+    if (kind == 3) {
+        switch (dtype) {
+            case RING_F32: return blocks_per_cu_ll<DT_F32>();
+            case kDtF32Bf16Out: return blocks_per_cu_ll<DT_F32B>();
+            case RING_I32: return blocks_per_cu_ll<DT_I32>();
+            case RING_BF16: return blocks_per_cu_ll<DT_BF16>();
+            default: return 0;
+        }
+    }
     switch (dtype) {
         case RING_F32: return blocks_per_cu_dt<DT_F32>(tile_vecs, kind);
         case kDtF32Bf16Out: return blocks_per_cu_dt<DT_F32B>(tile_vecs, kind);
@@ -875,7 +1084,22 @@ int ring_blocks_per_cu(int dtype, int tile_vecs, int kind) {
     }
 }
 
+template <int DT>
+static hipError_t launch_ll(RingParams& prm, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((ring_ll_kernel<DT>), dim3(grid), dim3(kBlock), 0, s, prm);
+    return hipGetLastError();
+}
+
 hipError_t launch_ring(RingParams& prm, int dtype, int tile_vecs, int grid, hipStream_t s) {
+    if (prm.ll) {
+        switch (dtype) {
+            case RING_F32: return launch_ll<DT_F32>(prm, grid, s);
+            case kDtF32Bf16Out: return launch_ll<DT_F32B>(prm, grid, s);
+            case RING_I32: return launch_ll<DT_I32>(prm, grid, s);
+            case RING_BF16: return launch_ll<DT_BF16>(prm, grid, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (dtype) {
         case RING_F32: return launch_ring_dt<DT_F32>(prm, tile_vecs, grid, s);
         case kDtF32Bf16Out: return launch_ring_dt<DT_F32B>(prm, tile_vecs, grid, s);

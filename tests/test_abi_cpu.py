@@ -70,6 +70,15 @@ def test_workspace_bytes():
     assert ag < 16 * (128 << 20) * 4
     # P = 1: a status header and a minimal flag table
     assert L.ring_workspace_bytes(N.OP_ALL_REDUCE, 1, 100, N.RING_I32) >= 256
+    # small calls also hold one 8-byte word per element and round, 16 (P - 1) n
+    # bytes; chunks over 256 KiB, or more than 8 Mi words, hold none
+    for op in (N.OP_ALL_REDUCE, N.OP_REDUCE_SCATTER, N.OP_ALL_GATHER):
+        small = L.ring_workspace_bytes(op, 4, 4096, N.RING_F32)
+        assert small >= 16 * 3 * 4096
+        edge = L.ring_workspace_bytes(op, 4, 4 * (64 << 10), N.RING_F32)      # 256 KiB chunks
+        over = L.ring_workspace_bytes(op, 4, 4 * ((64 << 10) + 4), N.RING_F32)
+        assert edge >= 16 * 3 * 4 * (64 << 10) > over
+    assert L.ring_workspace_bytes(N.OP_ALL_REDUCE, 64, 128 * 1024, N.RING_F32) < 16 * 63 * 128 * 1024
 
 
 def _fake(ptrs):
@@ -138,8 +147,11 @@ def test_overlap_rejected():
 
 def test_workspace_checks():
     L = N.lib()
-    need = L.ring_workspace_bytes(N.OP_REDUCE_SCATTER, 4, 4096, N.RING_F32)
-    assert _call_rs(4, 4096, ws_bytes=need - 1) == N.RING_EWORKSPACE
+    # chunks of 64 Ki + 4 fp32 are too large for low-latency words, so the
+    # size below is the flag table's and one byte less must be refused
+    n = 4 * ((64 << 10) + 4)
+    need = L.ring_workspace_bytes(N.OP_REDUCE_SCATTER, 4, n, N.RING_F32)
+    assert _call_rs(4, n, ws_bytes=need - 1) == N.RING_EWORKSPACE
     assert _call_rs(4, 4096, ws=0) == N.RING_EWORKSPACE
     assert _call_rs(4, 4096, ws=0x100010) == N.RING_EWORKSPACE      # not 256-byte aligned
 
@@ -174,13 +186,17 @@ def test_tuning_roundtrip_and_validation():
         prev = N.set_tuning(tile_vecs=16, map_mode=2)
         assert prev == old
         assert old["gemm_tile_n"] == 0
+        assert old["ll_max_chunk_bytes"] == 256 << 10
+        N.set_tuning(ll_max_chunk_bytes=0)
+        assert N.get_tuning()["ll_max_chunk_bytes"] == 0
         assert N.get_tuning()["tile_vecs"] == 16
         N.set_tuning(gemm_tile_n=256)
         assert N.get_tuning()["gemm_tile_n"] == 256
         for bad in ({"tile_vecs": 5}, {"waves_per_cu": 1}, {"waves_per_cu": 32}, {"map_mode": 1},
                     {"map_mode": 7},
                     {"timeout_s": 0.0}, {"stepwise": 2}, {"drop_round": -1},
-                    {"gemm_tile_n": 32}, {"gemm_tile_n": 192}):
+                    {"gemm_tile_n": 32}, {"gemm_tile_n": 192},
+                    {"ll_max_chunk_bytes": -1}, {"ll_max_chunk_bytes": (256 << 10) + 1}):
             with pytest.raises(N.RingError):
                 N.set_tuning(**bad)
     finally:
