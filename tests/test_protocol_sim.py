@@ -138,3 +138,97 @@ def test_planted_missing_wait_is_caught(drop):
             caught = True
             break
     assert caught
+
+
+# ---------------------------------------------------------------------------
+# The low-latency rounds: the value a rank passes right travels in a word
+# with a ready mark instead of behind a flag.  A wave's round k reads its own
+# input and (k > 0) the words (k - 1, left, j), clearing them as it takes
+# them; its write action stores the result into dst and sets the words
+# (k, r, j).  Nothing else orders the ranks: the in-place hazards (rank r's
+# all-gather overwriting the input chunk rank r+1 reads in round 0) must be
+# ordered by the chain of words alone.
+def _simulate_ll(x, T, rng, in_place, words, drop_wait=None):
+    P, n = x.shape
+    C = n // P
+    k_end = 2 * (P - 1)
+    src = x.copy()
+    dst = src if in_place else np.full_like(src, np.nan)
+    bounds = [(j * C // T, (j + 1) * C // T) for j in range(T)]
+
+    def left(r):
+        return (r - 1 + P) % P
+
+    def read(k, r, j):
+        lo, hi = bounds[j]
+        if k > 0:
+            got = words.pop((k - 1, left(r), j), None)
+            recv = got if got is not None else np.zeros(hi - lo, np.float32)
+        if k < P - 1:
+            c = (r - k - 2 + 2 * P) % P
+            own = src[r, c * C + lo:c * C + hi].copy()
+            if k == 0:
+                recv = src[left(r), c * C + lo:c * C + hi].copy()
+            return c, (own + recv).astype(np.float32)
+        t = k - (P - 1)
+        return (r - t - 1 + P) % P, recv
+
+    pending = {}
+    next_round = {(r, j): 0 for r in range(P) for j in range(T)}
+    while True:
+        reads = []
+        for (r, j), k in next_round.items():
+            if k >= k_end or (k, r, j) in pending:
+                continue
+            if k > 0 and drop_wait != (k, r) and (k - 1, left(r), j) not in words:
+                continue                             # the marks are not set yet
+            reads.append((k, r, j))
+        writes = list(pending)
+        if not reads and not writes:
+            break
+        pick = rng.choice(reads + writes)
+        if pick in pending:
+            k, r, j = pick
+            c, vals = pending.pop(pick)
+            lo, hi = bounds[j]
+            dst[r, c * C + lo:c * C + hi] = vals
+            if k + 1 < k_end:
+                words[(k, r, j)] = vals.copy()
+            next_round[(r, j)] = k + 1
+        else:
+            pending[pick] = read(*pick)
+    return dst
+
+
+@pytest.mark.parametrize("P", [2, 3, 4, 5])
+@pytest.mark.parametrize("in_place", [True, False])
+def test_ll_random_schedules_match_oracle(P, in_place):
+    """Two launches in a row on one set of words: each gives the oracle's
+    bits, and each leaves every word taken (cleared)."""
+    rng = random.Random(2000 + 10 * P + in_place)
+    T = 3
+    x = np.random.default_rng(20 + P).standard_normal((P, P * T * 2)).astype(np.float32)
+    want = oracle.all_reduce(x)
+    for _ in range(100):
+        words = {}
+        for launch in range(2):
+            got = _simulate_ll(x, T, rng, in_place, words)
+            np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32), err_msg="launch %d" % launch)
+            assert not words
+
+
+@pytest.mark.parametrize("drop", [(1, 0), (3, 2), (5, 1)])
+def test_ll_planted_missing_wait_is_caught(drop):
+    """Rank drop[1] takes round drop[0]'s words without waiting for their
+    marks: some schedule must then take a word before it was written."""
+    rng = random.Random(13)
+    P, T = 4, 2
+    x = np.random.default_rng(6).standard_normal((P, P * T * 2)).astype(np.float32)
+    want = oracle.all_reduce(x)
+    caught = False
+    for _ in range(300):
+        got = _simulate_ll(x, T, rng, True, {}, drop_wait=drop)
+        if not np.array_equal(got.view(np.uint32), want.view(np.uint32)):
+            caught = True
+            break
+    assert caught
