@@ -115,6 +115,7 @@ def mlp_layer_cost(P: int, M: int, D: int, F: int) -> dict:
 
 
 KERNEL_SOURCE = {"ring_step_kernel": ("ring_kernels.hip",), "copy_kernel_tab": ("ring_kernels.hip",),
+                 "ring_ll_kernel": ("ring_kernels.hip",),
                  "ring_bidir_kernel": ("ring_kernels.hip",), "ring_psum_kernel": ("ring_kernels.hip",),
                  "gemm_rs_kernel": ("gemm_rs.hip", "gemm_core.h"),
                  "ag_gemm_kernel": ("ag_gemm.hip", "gemm_core.h"),
@@ -122,6 +123,25 @@ KERNEL_SOURCE = {"ring_step_kernel": ("ring_kernels.hip",), "copy_kernel_tab": (
 
 
 KERNEL_HEADERS = ("ring_device.h", "ring_internal.h")
+
+# The low-latency rounds' limits (the library's kLlMaxChunkBytes, kLlMaxBytes).
+LL_MAX_CHUNK_BYTES = 256 << 10
+LL_MAX_WORD_BYTES = 64 << 20
+
+
+def _ring_kernel(op: str, P: int, n: int, kind: str) -> str:
+    """The kernel a ring call of this shape launches, with the current tuning
+    and a workspace of ring_workspace_bytes (which holds the low-latency words
+    whenever they fit): the one-way collectives of small chunks run
+    ring_ll_kernel."""
+    from ring_collectives_amd import _native as N
+    if op in ("all_reduce", "reduce_scatter", "all_gather") and P > 1 and not N.get_tuning()["stepwise"]:
+        chunk = (n // P) * (2 if kind == "bf16" else 4)
+        if (chunk <= min(LL_MAX_CHUNK_BYTES, N.get_tuning()["ll_max_chunk_bytes"])
+                and 16 * (P - 1) * n <= LL_MAX_WORD_BYTES):
+            return "ring_ll_kernel"
+    return {"ppermute": "copy_kernel_tab", "reduce_scatter_bidir": "ring_bidir_kernel",
+            "psum_circulating": "ring_psum_kernel"}.get(op, "ring_step_kernel")
 
 
 def _sha_source(kernel: str) -> str:
@@ -478,8 +498,8 @@ def _mlp_main(args, w):
                      "frac": round(flop / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                      "traffic": _traffic(args.workload, "tp_mlp_layer"),
                      "kernel": ("tp_mlp_layer (ag_gemm_kernel + gemm_rs_kernel)" if M % (256 * P) == 0 else
-                                "tp_mlp_layer (unfused: ring all-gather, 2P GEMMs, ring reduce-scatter, "
-                                "bf16 rounding)"),
+                                "tp_mlp_layer (unfused, 5 launches: ring all-gather, batched GEMM with gelu, "
+                                "batched split-K GEMM, range sum, ring reduce-scatter with the bf16 result)"),
                      "kernel_ms_avg": round(avg, 5)},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
@@ -541,8 +561,7 @@ def main():
 
     def step():
         call()
-    kernel = {"ppermute": "copy_kernel_tab", "reduce_scatter_bidir": "ring_bidir_kernel",
-              "psum_circulating": "ring_psum_kernel"}.get(op, "ring_step_kernel")
+    kernel = _ring_kernel(op, P, n, kind)
 
     print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
