@@ -498,8 +498,8 @@ def _mlp_main(args, w):
                      "frac": round(flop / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                      "traffic": _traffic(args.workload, "tp_mlp_layer"),
                      "kernel": ("tp_mlp_layer (ag_gemm_kernel + gemm_rs_kernel)" if M % (256 * P) == 0 else
-                                "tp_mlp_layer (unfused, 5 launches: ring all-gather, batched GEMM with gelu, "
-                                "batched split-K GEMM, range sum, ring reduce-scatter with the bf16 result)"),
+                                "tp_mlp_layer (unfused: ring all-gather, batched GEMM with gelu, batched "
+                                "split-K GEMM, ring reduce-scatter of the range sums with the bf16 result)"),
                      "kernel_ms_avg": round(avg, 5)},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,

@@ -179,7 +179,8 @@ static hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 // bidirectional kernel over its rounds 0 .. P-1 when bidir is set).
 static int run_ring(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream, int k_begin, int k_end,
-                    int compact_src, int bidir = 0, void* const* out16 = nullptr) {
+                    int compact_src, int bidir = 0, void* const* out16 = nullptr,
+                    const float* ranges = nullptr, int nranges = 0) {
     // reduce-scatter rounds of bf16 data carry fp32 partial sums
     const bool need_carry = dtype == RING_BF16 && (bidir || k_begin < P - 1);
     auto need = [&](const RingWs& l) { return need_carry ? l.total : l.total - l.carry_bytes; };
@@ -197,6 +198,7 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
                     (size_t)C * (size_t)esz <= (size_t)tu.ll_max_chunk_bytes;
     const RingWs lay = ll ? with_ll : ring_ws_layout(P, n, dtype, false);
     if (ws_bytes < need(lay)) return RING_EWORKSPACE;
+    if (nranges > 0 && !ll) return RING_EUNSUPPORTED;   // ranges are summed in those rounds only
     const int tile = ll ? kWave * kLlVec : kWave * tu.tile_vecs * elems_per_vec(dtype);
     const long long h = C - C / 2;   // top half of a chunk (bidirectional)
     const int T_top = bidir ? (int)((h + tile - 1) / tile) : 0;
@@ -219,6 +221,8 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
     }
     prm.carry = need_carry && !ll ? (float*)((char*)ws + lay.carry_off) : nullptr;
     prm.ll = ll ? (unsigned long long*)((char*)ws + lay.ll_off) : nullptr;
+    prm.ranges = ranges;
+    prm.nranges = nranges;
     prm.flags = (int*)((char*)ws + lay.flags_off);
     prm.status = (Status*)ws;
     prm.n = (long long)n;
@@ -339,6 +343,19 @@ int ringc::ring_reduce_scatter_bf16_out(const void* const* src, void* const* dst
     for (int q = 0; q < P; ++q)
         if (!src[q] || !dst[q] || !out16[q]) return RING_EINVAL;
     return run_ring(src, dst, P, n, kDtF32Bf16Out, ws, ws_bytes, stream, 0, P - 1, 0, 0, out16);
+}
+
+int ringc::ring_reduce_scatter_ranges_bf16_out(const float* ranges, int S, void* const* out16, int P, size_t n,
+                                               void* ws, size_t ws_bytes, void* stream) {
+    if (P < 2 || P > RING_MAX_RANKS || !ranges || !out16 || S < 1 || S > kLlMaxRanges) return RING_EINVAL;
+    if (n == 0) return RING_OK;
+    if (n % (size_t)P || ((uintptr_t)ranges & 3)) return RING_EINVAL;
+    void* dst[RING_MAX_RANKS];   // the kernel takes dst views; nothing is stored there
+    for (int q = 0; q < P; ++q) {
+        if (!out16[q]) return RING_EINVAL;
+        dst[q] = (void*)(ranges + (size_t)q * n);
+    }
+    return run_ring(nullptr, dst, P, n, kDtF32Bf16Out, ws, ws_bytes, stream, 0, P - 1, 0, 0, out16, ranges, S);
 }
 
 extern "C" {

@@ -26,6 +26,7 @@ constexpr int kMinTileVecs = 4;      // smallest tile: 4 vectors of 16 B per lan
 constexpr size_t kLlMaxChunkBytes = 256 << 10;
 constexpr size_t kLlMaxBytes = 64 << 20;
 constexpr int kLlVec = 4;            // words per lane per tile position
+constexpr int kLlMaxRanges = 8;      // K ranges a low-latency reduce-scatter can sum as it reads
 
 // The error header every workspace starts with.
 struct Status {
@@ -63,6 +64,11 @@ struct RingParams {
     void* out16[RING_MAX_RANKS];      // the owner's chunk, rounded once to bf16
     // low-latency rounds only: [2(P-1)][P][C] words (value | 1 << 32), or null
     unsigned long long* ll;
+    // fp32 reduce-scatter with a bf16 result in the low-latency rounds only:
+    // rank q's input is the sum, in order s = 0 .. nranges-1, of
+    // ranges[(s P + q) n ..] (0: the input is src)
+    const float* ranges;
+    int nranges;
 };
 
 // Internal element type of the ring launchers: an fp32 reduce-scatter whose
@@ -99,6 +105,12 @@ int ring_blocks_per_cu(int dtype, int tile_vecs, int kind);   // occupancy: 0 ri
 // layer's unfused path.
 int ring_reduce_scatter_bf16_out(const void* const* src, void* const* dst, void* const* out16, int P, size_t n,
                                  void* ws, size_t ws_bytes, void* stream);
+// The same reduce-scatter of inputs that are each the in-order sum of S
+// ranges (rank q's: ranges[(s P + q) n ..], s < S <= kLlMaxRanges), summed
+// as the rounds read them.  Only in the low-latency rounds: RING_EUNSUPPORTED,
+// with nothing launched, when the call does not take them.
+int ring_reduce_scatter_ranges_bf16_out(const float* ranges, int S, void* const* out16, int P, size_t n,
+                                        void* ws, size_t ws_bytes, void* stream);
 
 // GEMM + reduce-scatter workspace size (n = M * N per rank).
 size_t gemm_rs_workspace_bytes(int P, size_t n);

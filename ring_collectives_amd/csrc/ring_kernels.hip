@@ -784,6 +784,31 @@ template <int DT> __device__ __forceinline__ void ll_st(rsrc_t v, long long o, u
     else st4<POL_PLAIN>(x, v, (unsigned)o * 4u);
 }
 
+// Rank q's input at offsets o0 + 64 i of the chunk starting at element e0,
+// as the sum of its K ranges in order s = 0 .. nranges-1 (fp32).  Every
+// range's loads are issued before any is added; a range past nranges is
+// read through an empty view and never added (a select, not an add of
+// zero, so a sum of -0 keeps its sign).
+__device__ __forceinline__ void ll_ranges(const RingParams& p, int q, long long e0, long long o0,
+                                          unsigned (&v)[kLlVec]) {
+    float x[kLlMaxRanges][kLlVec];
+#pragma unroll
+    for (int s = 0; s < kLlMaxRanges; ++s) {
+        const int sc = s < p.nranges ? s : 0;
+        const rsrc_t in = tile_view(p.ranges + ((size_t)sc * p.P + q) * (size_t)p.n + e0,
+                                    s < p.nranges ? p.C * 4 : 0);
+#pragma unroll
+        for (int i = 0; i < kLlVec; ++i) x[s][i] = __uint_as_float(ld4<POL_NT>(in, (unsigned)(o0 + i * kWave) * 4u));
+    }
+#pragma unroll
+    for (int i = 0; i < kLlVec; ++i) {
+        float a = x[0][i];
+#pragma unroll
+        for (int s = 1; s < kLlMaxRanges; ++s) a = s < p.nranges ? a + x[s][i] : a;
+        v[i] = __float_as_uint(a);
+    }
+}
+
 // Round k of rank r waits for the words (k - 1, from) at this lane's
 // offsets o0 + 64 i (those below C: the others read as zero and count as
 // ready), takes their values and clears them.  Every poll reloads all four
@@ -856,16 +881,25 @@ __global__ __launch_bounds__(kBlock) void ring_ll_kernel(RingParams p) {
             if (k < P - 1) {
                 // reduce-scatter round s = k: chunk (r - k - 2) mod P
                 const long long e0 = (long long)rs_chunk(r, k, P) * C;
-                const rsrc_t own = ll_chunk<DT>(p.src[r], e0, C);
+                const bool summed = DT == DT_F32B && p.nranges > 0;   // inputs as sums of K ranges
                 unsigned a[kLlVec];
+                if (summed) {
+                    ll_ranges(p, r, e0, o0, a);
+                } else {
+                    const rsrc_t own = ll_chunk<DT>(p.src[r], e0, C);
 #pragma unroll
-                for (int i = 0; i < kLlVec; ++i) a[i] = ll_ld<DT>(own, o0 + i * kWave);
+                    for (int i = 0; i < kLlVec; ++i) a[i] = ll_ld<DT>(own, o0 + i * kWave);
+                }
                 if (k == p.k_begin) {   // the left neighbour's input: complete before the launch
-                    const rsrc_t in = ll_chunk<DT>(p.src[left], e0, C);
+                    if (summed) {
+                        ll_ranges(p, left, e0, o0, v);
+                    } else {
+                        const rsrc_t in = ll_chunk<DT>(p.src[left], e0, C);
 #pragma unroll
-                    for (int i = 0; i < kLlVec; ++i) {
-                        const unsigned x = ll_ld<DT>(in, o0 + i * kWave);
-                        v[i] = DT == DT_BF16 ? x << 16 : x;
+                        for (int i = 0; i < kLlVec; ++i) {
+                            const unsigned x = ll_ld<DT>(in, o0 + i * kWave);
+                            v[i] = DT == DT_BF16 ? x << 16 : x;
+                        }
                     }
                 } else if (!ll_recv(p, k, left, o0, v, r, j, lane)) {
                     return;
@@ -894,7 +928,7 @@ __global__ __launch_bounds__(kBlock) void ring_ll_kernel(RingParams p) {
                         for (int i = 0; i < kLlVec; ++i)
                             st2<POL_PLAIN>((unsigned short)bf16_rne(__uint_as_float(v[i])), o16,
                                            (unsigned)(o0 + i * kWave) * 2u);
-                    } else {
+                    } else if (!summed) {   // partial sums (unspecified outputs; none with ranges)
 #pragma unroll
                         for (int i = 0; i < kLlVec; ++i) ll_st<DT>(out, o0 + i * kWave, v[i]);
                     }

@@ -30,10 +30,13 @@
 //   every rank's product x_full @ W1 (the fused kernel's batched mode, no
 //   reduce-scatter) with the gelu epilogue              -> h
 //   every rank's product h @ W2 in fp32, its K split into S ranges so the
-//   few tiles still fill the GPU, the ranges summed in order -> partial
-//   the fp32 ring reduce-scatter of the partials, in place, the owner's
-//   block rounded once to bf16 as the ring's last round stores it
-//                                                       -> out_shard
+//   few tiles still fill the GPU                        -> range products
+//   the fp32 ring reduce-scatter of their sums, the owner's block rounded
+//   once to bf16 as the ring's last round stores it      -> out_shard
+// Where the reduce-scatter runs its low-latency rounds (small chunks, as at
+// the chapter's shape) it sums each input's ranges, in order, as it reads
+// them: four launches.  Otherwise a kernel first sums the ranges into the
+// partials and the reduce-scatter works on those in place: five.
 // The arithmetic is the fused path's except for the order of the second
 // product's sums over K (the ranges).
 // Workspace: [status | ring flags | GEMM flags | P ring partial sums of
@@ -64,6 +67,7 @@ bool any_overlap(const void* const* a, size_t na, const void* const* b, size_t n
 bool fused_shape(int P, int M) { return M % (256 * P) == 0; }
 
 constexpr int kMaxSplit = 8;
+static_assert(kMaxSplit <= kLlMaxRanges, "the low-latency reduce-scatter sums every range");
 
 // K ranges of the unfused second product: about 256 work items of 256 x 64
 // tiles in all (one per CU; the product's automatic tile width then takes
@@ -158,6 +162,11 @@ int mlp_unfused(const void* const* x_shard, const void* const* W1, const void* c
                      S, S > 1 ? split : nullptr);
     if (rc != RING_OK) return rc;
     if (S > 1) {
+        // Where the reduce-scatter takes its low-latency rounds it sums the
+        // ranges itself as it reads them, in the same order; otherwise a
+        // kernel sums them into the partials first.
+        rc = ring_reduce_scatter_ranges_bf16_out(split, S, out_shard, P, nd, ws, lay.gemm_off, stream);
+        if (rc != RING_EUNSUPPORTED) return rc;
         PartTab pt;
         for (int q = 0; q < P; ++q) pt.p[q] = (float*)part[q];
         long long blocks = ((long long)nd + 255) / 256;
