@@ -330,12 +330,16 @@ def test_full_size_bf16_p16_128Mi():
 # ---------------------------------------------------------------- more ranks
 @pytest.mark.parametrize("P,C", [(6, 2048 * 3 + 40), (7, 1001), (12, 4096 + 8), (32, 520), (64, 100)])
 @pytest.mark.parametrize("kind", ["f32", "i32", "bf16"])
-def test_more_ranks_every_collective(P, C, kind):
+@pytest.mark.parametrize("ll", [256 << 10, 0])
+def test_more_ranks_every_collective(P, C, kind, ll):
     """Rank counts 6, 7, 12, 32 and 64 (the library's maximum), ragged
     chunks: ppermute, reduce-scatter (each owner's chunk), all-gather,
     all-reduce, the bidirectional reduce-scatter and the circulating psum,
-    every bit against the oracle."""
-    note("more ranks P=%d C=%d %s" % (P, C, kind))
+    every bit against the oracle; the one-way collectives in both the
+    low-latency rounds (chunks this small take them by default) and the flag
+    rounds."""
+    note("more ranks P=%d C=%d %s ll=%d" % (P, C, kind, ll))
+    N.set_tuning(ll_max_chunk_bytes=ll)
     n = P * C
     rng = np.random.default_rng(1500 + P)
     if kind == "i32":
