@@ -368,9 +368,9 @@ size_t ring_workspace_bytes(int op, int P, size_t n, int dtype) {
         case RING_OP_ALL_REDUCE:
             if (!elem_bytes(dtype) || n % (size_t)P) return 0;
             return ring_ws_layout(P, n, dtype).total;
-        case RING_OP_REDUCE_SCATTER_BIDIR:
+        case RING_OP_REDUCE_SCATTER_BIDIR:   // never in the low-latency rounds
             if (!elem_bytes(dtype) || n % (size_t)P) return 0;
-            return ring_ws_layout(P, n, dtype).total;
+            return ring_ws_layout(P, n, dtype, false).total;
         case RING_OP_ALL_GATHER: {
             if (!elem_bytes(dtype) || n % (size_t)P) return 0;
             RingWs w = ring_ws_layout(P, n, dtype);

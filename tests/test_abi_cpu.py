@@ -109,8 +109,13 @@ def test_bidir_argument_checks():
     assert L.ring_reduce_scatter_bidir(a, b, 4, 0, N.RING_F32, 0x100000, 1 << 30, None) == N.RING_OK
     # too small a workspace is rejected before any launch
     assert L.ring_reduce_scatter_bidir(a, b, 4, 4096, N.RING_F32, 0x100000, 256, None) == N.RING_EWORKSPACE
-    w = L.ring_workspace_bytes(N.OP_REDUCE_SCATTER_BIDIR, 4, 4096, N.RING_F32)
-    assert w >= L.ring_workspace_bytes(N.OP_REDUCE_SCATTER, 4, 4096, N.RING_F32) > 0
+    # the bidirectional form tiles each half of a chunk, which can take one
+    # tile more than the one-way form (compared where chunks are too large
+    # for low-latency words), and never holds those words
+    big = 4 * ((64 << 10) + 4)
+    w = L.ring_workspace_bytes(N.OP_REDUCE_SCATTER_BIDIR, 4, big, N.RING_F32)
+    assert w >= L.ring_workspace_bytes(N.OP_REDUCE_SCATTER, 4, big, N.RING_F32) > 0
+    assert 0 < L.ring_workspace_bytes(N.OP_REDUCE_SCATTER_BIDIR, 4, 4096, N.RING_F32) < 16 * 3 * 4096
     assert L.ring_workspace_bytes(N.OP_REDUCE_SCATTER_BIDIR, 4, 4097, N.RING_F32) == 0
     wb = L.ring_workspace_bytes(N.OP_REDUCE_SCATTER_BIDIR, 4, 4096, N.RING_BF16)
     assert wb >= 4 * 4096 * 4     # the fp32 partial sums
