@@ -265,10 +265,15 @@ int all_gather_gemm(const void *const *A_shard, const void *const *B, void *cons
  * Shapes this version accepts: M % 256 == 0, M % P == 0, D % 128 == 0,
  * F % (128 P) == 0.  With M % (256 P) != 0 (fewer than 256 tokens per rank,
  * as at the chapter's own 256 tokens over 4 ranks) the same steps run
- * unfused, one kernel each: ring_all_gather, per-rank GEMMs (gelu epilogue,
- * then fp32 partials in the workspace), ring_reduce_scatter of the partials
- * in place, and the owner's block rounded once to bf16; the results are the
- * same.
+ * unfused, in separate launches: ring_all_gather; every rank's first product
+ * (gelu epilogue); every rank's second product in fp32 into the workspace,
+ * its K split into up to 8 ranges so the few output tiles still fill the
+ * GPU; and the fp32 ring reduce-scatter of each rank's sum of its ranges
+ * (summed in order as the ring reads them where its low-latency rounds run,
+ * else by a kernel first), the owner's block rounded once to bf16.  That
+ * arithmetic differs from the fused path's only in the order of the second
+ * product's sums over K (the ranges), within the same error bound;
+ * integer-valued operands give the same bits.
  */
 int tp_mlp_layer(const void *const *x_shard, const void *const *W1, const void *const *W2,
                  void *const *x_full, void *const *h, void *const *out_shard, int P, int M, int D,
