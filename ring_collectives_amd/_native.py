@@ -87,9 +87,11 @@ def strerror(code: int) -> str:
 
 
 def ptr_array(ptrs):
-    """Host array of device pointers (void* const*)."""
+    """Host array of device pointers (void* const*).  ctypes passes the
+    array itself for a pointer argument; it is returned twice so callers keep
+    it alive while the call runs."""
     arr = (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
-    return ctypes.cast(arr, _pp), arr   # keep `arr` alive while the call runs
+    return arr, arr
 
 
 def check(code: int, where: str) -> None:

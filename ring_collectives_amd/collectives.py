@@ -23,8 +23,12 @@ def _dtype(t: torch.Tensor) -> int:
 
 
 def _stream(stream) -> int:
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    # torch's current stream on the current device, as a raw handle (the
+    # same value as torch.cuda.current_stream().cuda_stream, without
+    # building a Stream object on every call)
+    return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
 
 
 def _ranks(ts: Sequence[torch.Tensor], what: str, numel: int | None = None, dtype=None):

@@ -7,6 +7,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 namespace ringc {
 
 int elem_bytes(int dtype) {
@@ -175,6 +177,23 @@ static int overlap_kind(const void* const* src, size_t src_bytes, void* const* d
 
 static hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
+// The occupancy of a ring kernel, queried once per (dtype, tile width,
+// kind) and kept: the query costs host time on every call otherwise, which
+// small calls feel.  The library targets one architecture, so the answer
+// is the same on every device.
+static int cached_blocks_per_cu(int dtype, int tile_vecs, int kind) {
+    static std::atomic<int> cache[32][17][4];   // dtype codes < 32, tile_vecs <= 16, 4 kinds
+    if (dtype < 0 || dtype >= 32 || tile_vecs < 0 || tile_vecs > 16 || kind < 0 || kind > 3)
+        return ring_blocks_per_cu(dtype, tile_vecs, kind);
+    std::atomic<int>& c = cache[dtype][tile_vecs][kind];
+    int v = c.load(std::memory_order_relaxed);
+    if (v <= 0) {
+        v = ring_blocks_per_cu(dtype, tile_vecs, kind);
+        if (v > 0) c.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 // Launch the chunk-step kernel over global rounds [k_begin, k_end) (the
 // bidirectional kernel over its rounds 0 .. P-1 when bidir is set).
 static int run_ring(const void* const* src, void* const* dst, int P, size_t n, int dtype,
@@ -241,7 +260,7 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
 
     // Grid: every wave must be resident at once (waves wait on each other).
     // Stay within half the occupancy limit: margin for anything else resident.
-    int occ = ring_blocks_per_cu(dtype, tu.tile_vecs, ll ? 3 : bidir);
+    int occ = cached_blocks_per_cu(dtype, tu.tile_vecs, ll ? 3 : bidir);
     if (occ < 1) return RING_EHIP;
     int bpc = (tu.waves_per_cu + kWavesPerBlock - 1) / kWavesPerBlock;
     if (bpc > occ / 2) bpc = occ / 2 > 0 ? occ / 2 : 1;
@@ -319,7 +338,7 @@ static int run_psum(const void* const* src, void* const* dst, int P, size_t n, i
     prm.psum = 1;
     prm.drop_round = tu.drop_round;
     // every wave of a tile position's ring must be resident: as run_ring
-    int occ = ring_blocks_per_cu(dtype, tu.tile_vecs, 2);
+    int occ = cached_blocks_per_cu(dtype, tu.tile_vecs, 2);
     if (occ < 1) return RING_EHIP;
     int bpc = (tu.waves_per_cu + kWavesPerBlock - 1) / kWavesPerBlock;
     if (bpc > occ / 2) bpc = occ / 2 > 0 ? occ / 2 : 1;
