@@ -62,3 +62,28 @@ def test_every_workload_names_a_profiled_kernel_source():
         for f in files:
             assert os.path.exists(os.path.join(ROOT, "ring_collectives_amd", "csrc", f)), (k, f)
     assert len(bench._sha_source("tp_mlp_layer")) == 64
+
+
+def test_kernel_name_follows_the_low_latency_limit():
+    """The bench names ring_ll_kernel exactly for the one-way collectives
+    whose chunks take the low-latency rounds (at most 256 KiB, words within
+    64 MiB, the tuning knob not lower), and the library's workspace size
+    agrees on which shapes hold the words."""
+    from ring_collectives_amd import _native as N
+    old = N.get_tuning()
+    try:
+        assert bench._ring_kernel("all_reduce", 4, 4096, "f32") == "ring_ll_kernel"
+        assert bench._ring_kernel("reduce_scatter", 8, 8192, "i32") == "ring_ll_kernel"
+        assert bench._ring_kernel("all_gather", 4, 4 * (128 << 10), "bf16") == "ring_ll_kernel"
+        assert bench._ring_kernel("all_reduce", 4, 4 * ((64 << 10) + 4), "f32") == "ring_step_kernel"
+        assert bench._ring_kernel("all_reduce", 8, 64 << 20, "f32") == "ring_step_kernel"
+        assert bench._ring_kernel("reduce_scatter_bidir", 4, 4096, "f32") == "ring_bidir_kernel"
+        assert bench._ring_kernel("ppermute", 2, 4096, "f32") == "copy_kernel_tab"
+        N.set_tuning(ll_max_chunk_bytes=0)
+        assert bench._ring_kernel("all_reduce", 4, 4096, "f32") == "ring_step_kernel"
+    finally:
+        N.set_tuning(**old)
+    L = N.lib()
+    with_words = L.ring_workspace_bytes(N.OP_ALL_REDUCE, 4, 4 * (64 << 10), N.RING_F32)
+    without = L.ring_workspace_bytes(N.OP_ALL_REDUCE, 4, 4 * ((64 << 10) + 4), N.RING_F32)
+    assert with_words > without
