@@ -36,12 +36,13 @@
 static int left_of(int r, int P) { return (r - 1 + P) % P; }
 
 /*
- * Reduce-scatter chunk for rank r at round s (s = 0 .. P-2).  The page's loop
- * uses step = s + 1 and
- *     recv_add_idx  = (my - step - 1 + P) % P
- *     left_send_idx = (left - step + P) % P
- * and the two name the same chunk because left = my - 1 (mod P).  Written
- * here as (r - s - 2) mod P with 2P added so the dividend stays >= 0.
+ * Reduce-scatter chunk for rank r at round s (s = 0 .. P-2).  On the ring
+ * page ("全归约 3：Ring——每步大小恒定", Walkthrough) the chunk a rank adds
+ * its own data into and the chunk its left neighbour sent are, at round s,
+ * both the one numbered (r - s - 2) mod P: counting the step from 1, the
+ * receiver's index is its rank minus the step minus one, and the sender's is
+ * the sender's rank (one less) minus the step.  2P is added so the dividend
+ * stays >= 0.
  */
 static int rs_chunk(int r, int s, int P) { return (r - s - 2 + 2 * P) % P; }
 
