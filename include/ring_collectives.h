@@ -23,15 +23,22 @@
  *              round-to-nearest-even in the ring's fixed order; int32 adds
  *              wrap modulo 2^32; bf16 is added in fp32 (see below).
  *   - ws       device workspace of at least ring_workspace_bytes(...) bytes,
- *              owned by the caller.  It must be zero-filled once before its
- *              first use (ring_workspace_init, or any zero fill); every call
- *              that completes normally leaves its flag table zero again, so
- *              back-to-back calls on one stream need no re-initialisation.
- *              The one exception: a bf16 reduce-scatter or all-reduce that
- *              runs its flag rounds leaves its fp32 partial sums in the
- *              workspace, so a call of another shape or dtype, whose flags
- *              or words may lie there, needs the workspace zero-filled
- *              again first.  Calls that share a workspace must be ordered
+ *              256-byte aligned, owned by the caller.  It must be
+ *              zero-filled once before its first use (ring_workspace_init,
+ *              or any zero fill); every call that completes normally leaves
+ *              its flags and low-latency words zero again, so back-to-back
+ *              calls on one stream need no re-initialisation.  Some calls
+ *              also leave data in the workspace: the fp32 partial sums of a
+ *              bf16 reduce-scatter or all-reduce in the flag rounds, the
+ *              receive slots of the circulating psum, the partial tiles of
+ *              the fused GEMMs and the MLP layer.  The workspace's first 256
+ *              bytes keep a record of where such data lies; a later call
+ *              whose flags or words would lie there (another shape or
+ *              operation on the same workspace) stops at once and reports
+ *              RING_EWORKSPACE through ring_last_error, with its outputs
+ *              undefined, instead of reading that data as flags.  A zero
+ *              fill clears the record.  Calls of one shape and operation
+ *              never trip it.  Calls that share a workspace must be ordered
  *              (same stream).
  *   - stream   a hipStream_t passed as void* (NULL = the default stream).
  *              Every call is asynchronous on that stream; nothing is
@@ -44,8 +51,10 @@
  * RING_EUNSUPPORTED, RING_EWORKSPACE); a failed HIP launch returns RING_EHIP.
  * A rank that waits for its neighbour longer than the watchdog limit
  * (default 5 s) stops, records RING_ETIMEOUT in the workspace and makes the
- * other ranks stop too; ring_last_error() reports it.  After a timeout the
- * output is undefined and the workspace must be re-initialised.
+ * other ranks stop too; ring_last_error() reports it.  Asynchronous errors
+ * (RING_ETIMEOUT, RING_EWORKSPACE from the record above, RING_EPROTOCOL
+ * from the debug check_flags knob) leave the outputs undefined; the
+ * workspace must then be re-initialised.
  */
 #ifndef RING_COLLECTIVES_H
 #define RING_COLLECTIVES_H
@@ -77,7 +86,8 @@ enum {
     RING_EUNSUPPORTED = -2, /* bad dtype or a shape this version rejects    */
     RING_EWORKSPACE = -3,   /* workspace missing or too small               */
     RING_EHIP = -4,         /* a HIP runtime call failed                    */
-    RING_ETIMEOUT = -5      /* a rank waited past the watchdog limit        */
+    RING_ETIMEOUT = -5,     /* a rank waited past the watchdog limit        */
+    RING_EPROTOCOL = -6     /* debug check: a flag was set a second time    */
 };
 
 /*
@@ -284,8 +294,10 @@ size_t tp_mlp_workspace_bytes(int P, int M, int D, int F);
 
 /*
  * Synchronises `stream` and returns the error word a kernel left in `ws`
- * (RING_OK if none).  If info is not NULL it receives the stuck rank, round
- * and tile packed as rank | round << 8 | tile << 16 (tile saturates).
+ * (RING_OK if none).  If info is not NULL it receives where the error
+ * happened, rank | round << 8 | tile << 16 (tile saturates): the stuck
+ * wait for RING_ETIMEOUT, the flag set twice for RING_EPROTOCOL, 0 for
+ * RING_EWORKSPACE.  ws_bytes is the workspace's size (at least 256).
  */
 int ring_last_error(const void *ws, size_t ws_bytes, void *stream, int *info);
 
@@ -330,6 +342,15 @@ const char *ring_strerror(int code);
  *                  (default).  Same chunks, same additions, same results;
  *                  a round costs about half the latency.  Not in stepwise
  *                  mode.
+ *   check_flags    debug: 1 makes every flag set (ring rounds, psum,
+ *                  GEMM tiles, all-gather slices) an atomic add that
+ *                  returns the flag's old value, which must be 0 -- each
+ *                  flag of a launch is set exactly once and cleared by its
+ *                  reader ("全归约 3：Ring——每步大小恒定", Walkthrough: a
+ *                  Ge(1) wait on a row notified once) -- and every
+ *                  low-latency word be empty before it is written.  A
+ *                  violation is recorded as RING_EPROTOCOL with its (rank,
+ *                  round, tile).  Results are unchanged; 0 (default) off.
  */
 typedef struct {
     int tile_vecs;
@@ -340,6 +361,7 @@ typedef struct {
     int drop_round;
     int gemm_tile_n;
     int ll_max_chunk_bytes;
+    int check_flags;
 } ring_tuning_t;
 
 void ring_get_tuning(ring_tuning_t *t);

@@ -16,8 +16,8 @@ LIB_PATH = os.path.join(HERE, "libring_collectives.so")
 RING_F32, RING_BF16, RING_I32 = 0, 1, 2
 (OP_PPERMUTE, OP_REDUCE_SCATTER, OP_ALL_GATHER, OP_ALL_REDUCE, OP_GEMM_REDUCE_SCATTER,
  OP_REDUCE_SCATTER_BIDIR, OP_ALL_GATHER_GEMM, OP_PSUM_CIRCULATING) = range(8)
-RING_OK, RING_EINVAL, RING_EUNSUPPORTED, RING_EWORKSPACE, RING_EHIP, RING_ETIMEOUT = (
-    0, -1, -2, -3, -4, -5)
+RING_OK, RING_EINVAL, RING_EUNSUPPORTED, RING_EWORKSPACE, RING_EHIP, RING_ETIMEOUT, RING_EPROTOCOL = (
+    0, -1, -2, -3, -4, -5, -6)
 MAX_RANKS = 64
 
 _vp = ctypes.c_void_p
@@ -47,7 +47,8 @@ class Tuning(ctypes.Structure):
     _fields_ = [("tile_vecs", ctypes.c_int), ("waves_per_cu", ctypes.c_int),
                 ("map_mode", ctypes.c_int), ("timeout_s", ctypes.c_double),
                 ("stepwise", ctypes.c_int), ("drop_round", ctypes.c_int),
-                ("gemm_tile_n", ctypes.c_int), ("ll_max_chunk_bytes", ctypes.c_int)]
+                ("gemm_tile_n", ctypes.c_int), ("ll_max_chunk_bytes", ctypes.c_int),
+                ("check_flags", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -57,9 +57,13 @@ def workspace(op: int, P: int, n: int, dtype: torch.dtype, device=None) -> torch
 
 def _ordered(ws: torch.Tensor, stream) -> torch.Tensor:
     """A workspace just zero-filled on torch's current stream, made ready for
-    a call on `stream`: that stream waits for the fill."""
+    a call on `stream`: that stream waits for the fill, and the allocator is
+    told the block is in use on `stream`, so it is not handed out again
+    before the call's kernels there have finished, even if the caller drops
+    the returned workspace at once."""
     if stream is not None and stream != torch.cuda.current_stream(ws.device):
         stream.wait_stream(torch.cuda.current_stream(ws.device))
+        ws.record_stream(stream)
     return ws
 
 

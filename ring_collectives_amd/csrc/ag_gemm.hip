@@ -58,9 +58,9 @@ struct AgGemmParams {
     int nflags;                                 // flags in the table
     int drop_round;                             // test hook: rank 0 never flags this phase (0 = off)
     int gelu_bf16;                              // C is bf16(gelu(bf16(product))), else fp32
+    WsSpan ws_zero, ws_data;                    // flags that must start zero; data left behind
+    int check_flags;                            // debug: each flag must be 0 when it is set
 };
-
-constexpr size_t kDoneOffset = 64;   // the finish counter, inside the status block
 
 __device__ __forceinline__ int* ag_flag(const AgGemmParams& p, int f, int q, int pos) {
     return p.flags + (((size_t)f * p.P + q) * p.tpc + pos) * kFlagStride;
@@ -98,11 +98,20 @@ __device__ __forceinline__ bool wg_wait(const AgGemmParams& p, int* f, int wave,
     return __hip_atomic_load(&p.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
 }
 
-// All waves' stores are complete, then the flag is set once.
-__device__ __forceinline__ void wg_signal(int* f, int tid) {
+// All waves' stores are complete, then the flag is set once (with the
+// check_flags debug knob: and its old value must be 0, else RING_EPROTOCOL
+// at (q, g, pos)).
+__device__ __forceinline__ void wg_signal(const AgGemmParams& p, int* f, int tid, int q, int g, int pos) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (tid == 0) __hip_atomic_fetch_add(f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        if (p.check_flags) {
+            if (__hip_atomic_fetch_add(f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+                report_error(p.status, RING_EPROTOCOL, q, g, pos);
+        } else {
+            __hip_atomic_fetch_add(f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 template <class G>
@@ -118,6 +127,10 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
     const int grp = blockIdx.x / P;
     const int left = (q - 1 + P) % P;
     const int Mc = p.M / P;
+    // the workspace's record of data earlier calls left: none may lie under
+    // the slice flags (every wave sees the same answer and leaves)
+    if (blockIdx.x == 0 && tid == 0) ws_add_data(p.status, p.ws_data);
+    if (!ws_ok(p.status, ws_record(p.status), p.ws_zero, lane)) return;
 
     // place the local block (nobody waits for it in A_full)
     for (int pos = grp; pos < p.tpc; pos += p.groups) {
@@ -144,7 +157,7 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
                 else
                     copy_rows<POL_DEV>(p.Af[left] + ((size_t)cg * Mc + r0) * p.K, dst, r1 - r0, p.K, tid,
                                        nthreads);
-                if (!(q == 0 && p.drop_round > 0 && g == p.drop_round)) wg_signal(ag_flag(p, g, q, pos), tid);
+                if (!(q == 0 && p.drop_round > 0 && g == p.drop_round)) wg_signal(p, ag_flag(p, g, q, pos), tid, q, g, pos);
             }
         }
         // GEMM tiles of chunk c
@@ -240,7 +253,8 @@ static bool ag_overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 int ag_gemm_run(const void* const* A_shard, const void* const* B, void* const* A_full, void* const* C,
-                int P, int M, int N, int K, void* ws, size_t ws_bytes, void* stream, int gelu_bf16) {
+                int P, int M, int N, int K, void* ws, size_t ws_bytes, void* stream, int gelu_bf16,
+                WsSpan extra) {
     if (P < 1 || P > RING_MAX_RANKS || M < 0 || N < 0 || K < 0) return RING_EINVAL;
     if (!A_shard || !B || !A_full || !C) return RING_EINVAL;
     if (M == 0 || N == 0) return RING_OK;
@@ -273,8 +287,11 @@ int ag_gemm_run(const void* const* A_shard, const void* const* B, void* const* A
     prm.done = (int*)((char*)ws + kDoneOffset);
     prm.flags = (int*)((char*)ws + lay.flags_off);
     prm.nflags = lay.nflags;
+    prm.ws_zero = WsSpan{kStatusBytes, lay.flags_off + lay.flags_bytes};
+    prm.ws_data = extra;   // the all-gather + GEMM itself leaves no data in the workspace
     const DevInfo di = dev_info();
     const ring_tuning_t tu = tuning();
+    prm.check_flags = tu.check_flags;
     prm.spin_limit = (long long)(tu.timeout_s * (double)di.wall_khz * 1000.0);
     prm.drop_round = tu.drop_round;
     prm.P = P;
@@ -298,5 +315,5 @@ int ag_gemm_run(const void* const* A_shard, const void* const* B, void* const* A
 extern "C" int all_gather_gemm(const void* const* A_shard, const void* const* B, void* const* A_full,
                                void* const* C, int P, int M, int N, int K, void* ws, size_t ws_bytes,
                                void* stream) {
-    return ringc::ag_gemm_run(A_shard, B, A_full, C, P, M, N, K, ws, ws_bytes, stream, 0);
+    return ringc::ag_gemm_run(A_shard, B, A_full, C, P, M, N, K, ws, ws_bytes, stream, 0, ringc::WsSpan{0, 0});
 }

@@ -67,6 +67,8 @@ struct GemmParams {
     float* split;                              //   range's fp32 product at split[(s P + q) M N ..]
     int epi;                                   // what out holds: EPI_F32, EPI_BF16 (the fp32 sum
                                                // rounded once) or EPI_GELU_BF16
+    WsSpan ws_zero, ws_data;                   // flags that must start zero; data left behind
+    int check_flags;                           // debug: each flag must be 0 when it is set
 };
 
 template <class G>
@@ -95,6 +97,10 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
     // ksplit ranges whose products go to split (summed by the caller)
     const int S = p.batched ? p.ksplit : 1;
     const int items = p.batched ? P * p.tpc * S : P * P * p.tpc;
+    // the workspace's record of data earlier calls left: none may lie under
+    // this launch's flags (every wave sees the same answer and leaves)
+    if (blockIdx.x == 0 && tid == 0) ws_add_data(p.status, p.ws_data);
+    if (!ws_ok(p.status, ws_record(p.status), p.ws_zero, lane)) return;
 
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int phase = p.batched ? 0 : it / (P * p.tpc);
@@ -159,7 +165,7 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void gemm_rs_kernel(GemmP
                         }
                     }
                 }
-                signal_flag(gflag<G>(p, phase, q, pos, wave), lane);
+                signal_flag(gflag<G>(p, phase, q, pos, wave), lane, p.check_flags, p.status, q, phase + 1, pos);
             } else {
                 // Final sum of chunk q, row-major into out[q]: fp32, rounded
                 // once to bf16, or bf16(gelu(bf16(sum))).
@@ -238,7 +244,7 @@ static int launch_gemm_rs(GemmParams& prm, const DevInfo& di, hipStream_t stream
 // behind the all-gather's flags).
 int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, int P, int M, int N, int K,
                 void* ws, size_t ws_bytes, void* stream, int epi, size_t region_off, int batched, int ksplit,
-                float* split) {
+                float* split, WsSpan extra) {
     if (P < 1 || P > RING_MAX_RANKS || M < 0 || N < 0 || K < 0) return RING_EINVAL;
     if (!A || !B || !out) return RING_EINVAL;
     if (M == 0 || N == 0) return RING_OK;
@@ -267,8 +273,18 @@ int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, in
     prm.work = (float*)((char*)ws + lay.work_off);
     prm.flags = (int*)((char*)ws + lay.flags_off);
     prm.status = (Status*)ws;
+    // batched products use no flags; the reduce-scatter's partial tiles stay
+    // in the workspace
+    prm.ws_zero = batched ? WsSpan{0, 0} : WsSpan{kStatusBytes, lay.flags_off + lay.flags_bytes};
+    WsSpan data = lay.work_bytes && !batched ? WsSpan{lay.work_off, lay.work_off + lay.work_bytes} : WsSpan{0, 0};
+    if (extra.hi > extra.lo) {
+        if (data.hi <= data.lo) data = extra;
+        else data = WsSpan{data.lo < extra.lo ? data.lo : extra.lo, data.hi > extra.hi ? data.hi : extra.hi};
+    }
+    prm.ws_data = data;
     const DevInfo di = dev_info();
     const ring_tuning_t tu = tuning();
+    prm.check_flags = tu.check_flags;
     prm.spin_limit = (long long)(tu.timeout_s * (double)di.wall_khz * 1000.0);
     prm.P = P;
     prm.M = M;
@@ -304,5 +320,6 @@ int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, in
 extern "C" int gemm_reduce_scatter(const void* const* A, const void* const* B, void* const* out,
                                    int P, int M, int N, int K, void* ws, size_t ws_bytes,
                                    void* stream) {
-    return ringc::gemm_rs_run(A, B, out, P, M, N, K, ws, ws_bytes, stream, ringc::EPI_F32, 0, 0, 1, nullptr);
+    return ringc::gemm_rs_run(A, B, out, P, M, N, K, ws, ws_bytes, stream, ringc::EPI_F32, 0, 0, 1, nullptr,
+                              ringc::WsSpan{0, 0});
 }

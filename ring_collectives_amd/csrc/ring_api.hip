@@ -39,10 +39,10 @@ static bool ll_fits(int P, size_t n, int dtype) {
            2 * (size_t)(P - 1) * n * sizeof(unsigned long long) <= kLlMaxBytes;
 }
 
-RingWs ring_ws_layout(int P, size_t n, int dtype, bool with_ll) {
+RingWs ring_ws_layout(int P, size_t n, int dtype, bool with_ll, size_t tile_elems) {
     RingWs w;
     const size_t C = n / (size_t)P;
-    const size_t tile_min = (size_t)kWave * kMinTileVecs * elems_per_vec(dtype);
+    const size_t tile_min = tile_elems ? tile_elems : (size_t)kWave * kMinTileVecs * elems_per_vec(dtype);
     // + 1: the bidirectional reduce-scatter tiles each half of a chunk
     // separately, which can take one tile more than the whole chunk
     const size_t T = (C + tile_min - 1) / tile_min + 1;
@@ -82,7 +82,8 @@ static bool tuning_valid(const ring_tuning_t& x) {
            x.waves_per_cu <= 16 && (x.map_mode == 0 || x.map_mode == 2) && x.timeout_s > 0 &&
            x.timeout_s < 3600 && (x.stepwise == 0 || x.stepwise == 1) && x.drop_round >= 0 &&
            (x.gemm_tile_n == 0 || x.gemm_tile_n == 64 || x.gemm_tile_n == 128 || x.gemm_tile_n == 256) &&
-           x.ll_max_chunk_bytes >= 0 && (size_t)x.ll_max_chunk_bytes <= kLlMaxChunkBytes;
+           x.ll_max_chunk_bytes >= 0 && (size_t)x.ll_max_chunk_bytes <= kLlMaxChunkBytes &&
+           (x.check_flags == 0 || x.check_flags == 1);
 }
 
 static ring_tuning_t& tuning_ref() {
@@ -100,6 +101,7 @@ static ring_tuning_t& tuning_ref() {
         d.drop_round = 0;
         d.gemm_tile_n = 0;
         d.ll_max_chunk_bytes = (int)kLlMaxChunkBytes;
+        d.check_flags = 0;
         ring_tuning_t x = d;
         x.tile_vecs = env_int("RING_TILE_VECS", d.tile_vecs);
         x.waves_per_cu = env_int("RING_WAVES_PER_CU", d.waves_per_cu);
@@ -109,6 +111,7 @@ static ring_tuning_t& tuning_ref() {
         x.stepwise = env_int("RING_STEPWISE", 0);
         x.gemm_tile_n = env_int("RING_GEMM_TILE_N", d.gemm_tile_n);
         x.ll_max_chunk_bytes = env_int("RING_LL_MAX_CHUNK_BYTES", d.ll_max_chunk_bytes);
+        x.check_flags = env_int("RING_CHECK_FLAGS", 0);
         return tuning_valid(x) ? x : d;
     }();
     return t;
@@ -194,12 +197,19 @@ static int cached_blocks_per_cu(int dtype, int tile_vecs, int kind) {
     return v;
 }
 
+static WsSpan span_hull(WsSpan a, WsSpan b) {
+    if (b.hi <= b.lo) return a;
+    if (a.hi <= a.lo) return b;
+    return WsSpan{a.lo < b.lo ? a.lo : b.lo, a.hi > b.hi ? a.hi : b.hi};
+}
+
 // Launch the chunk-step kernel over global rounds [k_begin, k_end) (the
 // bidirectional kernel over its rounds 0 .. P-1 when bidir is set).
+// extra: a further span of ws the caller's other launches leave data in.
 static int run_ring(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream, int k_begin, int k_end,
                     int compact_src, int bidir = 0, void* const* out16 = nullptr,
-                    const float* ranges = nullptr, int nranges = 0) {
+                    const float* ranges = nullptr, int nranges = 0, WsSpan extra = WsSpan{0, 0}) {
     // reduce-scatter rounds of bf16 data carry fp32 partial sums
     const bool need_carry = dtype == RING_BF16 && (bidir || k_begin < P - 1);
     auto need = [&](const RingWs& l) { return need_carry ? l.total : l.total - l.carry_bytes; };
@@ -208,15 +218,20 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
     const DevInfo di = dev_info();
     const int esz = elem_bytes(dtype);
     const long long C = (long long)(n / (size_t)P);
-    // Low-latency rounds for small one-way calls (not in stepwise mode,
-    // whose rounds are separate launches ordered by the stream), when the
-    // workspace holds their words: the size ring_workspace_bytes gives for
-    // this call does; one sized for a larger call may only cover the flags.
+    // The layout follows from the shape and the workspace's size alone: a
+    // workspace that holds this shape's low-latency words (the size
+    // ring_workspace_bytes gives does; one sized for a larger call may hold
+    // only the flags) keeps them, and the bf16 carry after them, whether or
+    // not this call runs those rounds.  So a call in the flag rounds never
+    // leaves its carry where the same shape's words lie.
     const RingWs with_ll = ring_ws_layout(P, n, dtype, true);
-    const bool ll = !bidir && !tu.stepwise && with_ll.ll_bytes && ws_bytes >= need(with_ll) &&
-                    (size_t)C * (size_t)esz <= (size_t)tu.ll_max_chunk_bytes;
-    const RingWs lay = ll ? with_ll : ring_ws_layout(P, n, dtype, false);
+    const bool has_ll = with_ll.ll_bytes && ws_bytes >= need(with_ll);
+    const RingWs lay = has_ll ? with_ll : ring_ws_layout(P, n, dtype, false);
     if (ws_bytes < need(lay)) return RING_EWORKSPACE;
+    // Low-latency rounds for small one-way calls where the workspace holds
+    // their words (not in stepwise mode, whose rounds are separate launches
+    // ordered by the stream).
+    const bool ll = has_ll && !bidir && !tu.stepwise && (size_t)C * (size_t)esz <= (size_t)tu.ll_max_chunk_bytes;
     if (nranges > 0 && !ll) return RING_EUNSUPPORTED;   // ranges are summed in those rounds only
     const int tile = ll ? kWave * kLlVec : kWave * tu.tile_vecs * elems_per_vec(dtype);
     const long long h = C - C / 2;   // top half of a chunk (bidirectional)
@@ -257,6 +272,13 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
     prm.bidir = bidir;
     prm.T_top = T_top;
     prm.h = h;
+    // the flag rounds need their flags zero, the low-latency rounds their
+    // words; the bf16 carry of the flag rounds is data left behind.  The
+    // span checked runs from the end of the status block (see ws_add_data).
+    prm.ws_zero = WsSpan{kStatusBytes, ll ? lay.ll_off + lay.ll_bytes : lay.flags_off + lay.flags_bytes};
+    prm.ws_data = span_hull(prm.carry ? WsSpan{lay.carry_off, lay.carry_off + lay.carry_bytes} : WsSpan{0, 0},
+                            extra);
+    prm.check_flags = tu.check_flags;
 
     // Grid: every wave must be resident at once (waves wait on each other).
     // Stay within half the occupancy limit: margin for anything else resident.
@@ -337,6 +359,9 @@ static int run_psum(const void* const* src, void* const* dst, int P, size_t n, i
     prm.vec_ok = vec_ok;
     prm.psum = 1;
     prm.drop_round = tu.drop_round;
+    prm.ws_zero = WsSpan{kStatusBytes, lay.slots_off};
+    prm.ws_data = WsSpan{lay.slots_off, lay.total};
+    prm.check_flags = tu.check_flags;
     // every wave of a tile position's ring must be resident: as run_ring
     int occ = cached_blocks_per_cu(dtype, tu.tile_vecs, 2);
     if (occ < 1) return RING_EHIP;
@@ -355,17 +380,17 @@ static int run_psum(const void* const* src, void* const* dst, int P, size_t n, i
 
 // ------------------------------------------------------------------ C ABI
 int ringc::ring_reduce_scatter_bf16_out(const void* const* src, void* const* dst, void* const* out16, int P,
-                                        size_t n, void* ws, size_t ws_bytes, void* stream) {
+                                        size_t n, void* ws, size_t ws_bytes, void* stream, WsSpan extra) {
     if (P < 2 || P > RING_MAX_RANKS || !src || !dst || !out16) return RING_EINVAL;
     if (n == 0) return RING_OK;
     if (n % (size_t)P) return RING_EINVAL;
     for (int q = 0; q < P; ++q)
         if (!src[q] || !dst[q] || !out16[q]) return RING_EINVAL;
-    return run_ring(src, dst, P, n, kDtF32Bf16Out, ws, ws_bytes, stream, 0, P - 1, 0, 0, out16);
+    return run_ring(src, dst, P, n, kDtF32Bf16Out, ws, ws_bytes, stream, 0, P - 1, 0, 0, out16, nullptr, 0, extra);
 }
 
 int ringc::ring_reduce_scatter_ranges_bf16_out(const float* ranges, int S, void* const* out16, int P, size_t n,
-                                               void* ws, size_t ws_bytes, void* stream) {
+                                               void* ws, size_t ws_bytes, void* stream, WsSpan extra) {
     if (P < 2 || P > RING_MAX_RANKS || !ranges || !out16 || S < 1 || S > kLlMaxRanges) return RING_EINVAL;
     if (n == 0) return RING_OK;
     if (n % (size_t)P || ((uintptr_t)ranges & 3)) return RING_EINVAL;
@@ -374,7 +399,8 @@ int ringc::ring_reduce_scatter_ranges_bf16_out(const float* ranges, int S, void*
         if (!out16[q]) return RING_EINVAL;
         dst[q] = (void*)(ranges + (size_t)q * n);
     }
-    return run_ring(nullptr, dst, P, n, kDtF32Bf16Out, ws, ws_bytes, stream, 0, P - 1, 0, 0, out16, ranges, S);
+    return run_ring(nullptr, dst, P, n, kDtF32Bf16Out, ws, ws_bytes, stream, 0, P - 1, 0, 0, out16, ranges, S,
+                    extra);
 }
 
 extern "C" {
@@ -441,8 +467,7 @@ static int rs_or_ar(const void* const* src, void* const* dst, int P, size_t n, i
     }
     if (kind == KIND_RS_BIDIR)   // P steps: P-1 that add, one that takes the complete halves
         return run_ring(src, dst, P, n, dtype, ws, ws_bytes, stream, 0, P, 0, 1);
-    return run_ring(src, dst, P, n, dtype, ws, ws_bytes, stream, 0,
-                    kind == KIND_AR ? 2 * (P - 1) : P - 1, 0);
+    return run_ring(src, dst, P, n, dtype, ws, ws_bytes, stream, 0, kind == KIND_AR ? 2 * (P - 1) : P - 1, 0);
 }
 
 int ring_reduce_scatter(const void* const* src, void* const* dst, int P, size_t n, int dtype,
@@ -471,8 +496,10 @@ int ring_psum_circulating(const void* const* src, void* const* dst, int P, size_
     return run_psum(src, dst, P, n, dtype, ws, ws_bytes, stream);
 }
 
-int ring_all_gather(const void* const* src_or_null, void* const* dst, int P, size_t n, int dtype,
-                    void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+int ringc::ring_all_gather_rec(const void* const* src_or_null, void* const* dst, int P, size_t n, int dtype,
+                               void* ws, size_t ws_bytes, void* stream, WsSpan extra) {
     int rc = check_common(dst, P, n, dtype, true);
     if (rc) return rc;
     const size_t esz = (size_t)elem_bytes(dtype);
@@ -491,11 +518,18 @@ int ring_all_gather(const void* const* src_or_null, void* const* dst, int P, siz
     }
     // the all-gather rounds are global rounds P-1 .. 2P-3 of the all-reduce
     return run_ring(src_or_null, dst, P, n, dtype, ws, ws_bytes, stream, P - 1, 2 * (P - 1),
-                    src_or_null ? 1 : 0);
+                    src_or_null ? 1 : 0, 0, nullptr, nullptr, 0, extra);
+}
+
+extern "C" {
+
+int ring_all_gather(const void* const* src_or_null, void* const* dst, int P, size_t n, int dtype,
+                    void* ws, size_t ws_bytes, void* stream) {
+    return ring_all_gather_rec(src_or_null, dst, P, n, dtype, ws, ws_bytes, stream, WsSpan{0, 0});
 }
 
 int ring_last_error(const void* ws, size_t ws_bytes, void* stream, int* info) {
-    if (!ws || ws_bytes < sizeof(Status)) return RING_EINVAL;
+    if (!ws || ws_bytes < kStatusBytes) return RING_EINVAL;
     if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return RING_EHIP;
     Status st;
     if (hipMemcpy(&st, ws, sizeof st, hipMemcpyDeviceToHost) != hipSuccess) return RING_EHIP;
@@ -518,9 +552,12 @@ const char* ring_strerror(int code) {
         case RING_OK: return "ok";
         case RING_EINVAL: return "invalid argument (rank count, size, pointer, alignment or overlap)";
         case RING_EUNSUPPORTED: return "unsupported dtype or shape";
-        case RING_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case RING_EWORKSPACE:
+            return "workspace missing, misaligned or too small, or its flags lie over data an earlier call "
+                   "left there (re-initialise it)";
         case RING_EHIP: return "HIP runtime call failed";
         case RING_ETIMEOUT: return "a rank waited for its neighbour past the watchdog limit";
+        case RING_EPROTOCOL: return "a flag was set twice or a word overwritten before it was read (check_flags)";
         default: return "unknown error";
     }
 }

@@ -75,14 +75,57 @@ template <int POL> __device__ __forceinline__ void st2(unsigned short x, rsrc_t 
 // from 0 to 1 when its producer has finished a tile, and back to 0 when its
 // single consumer has seen it (so a finished launch leaves the table zeroed).
 
-__device__ inline void report_timeout(Status* st, int r, int k, int j) {
+// Record the first asynchronous error of a launch and where it happened
+// (later errors keep the first one).
+__device__ inline void report_error(Status* st, int code, int r, int k, int j) {
     int expected = 0;
-    if (__hip_atomic_compare_exchange_strong(&st->code, &expected, (int)RING_ETIMEOUT,
-                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+    if (__hip_atomic_compare_exchange_strong(&st->code, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT)) {
         int info = (r & 0xFF) | ((k & 0xFF) << 8) | ((j < 32767 ? j : 32767) << 16);
         __hip_atomic_store(&st->info, info, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+__device__ inline void report_timeout(Status* st, int r, int k, int j) { report_error(st, RING_ETIMEOUT, r, k, j); }
+
+// ---------------------------------------------------------------- workspace record
+// A launch reads the record of data earlier calls left in the workspace
+// (Status::data_lo_inv, data_hi) as it starts; the loads are issued at once
+// and their result is needed only by ws_ok, by when the wave's first data
+// loads have usually returned too.
+struct WsRecord {
+    unsigned long long lo_inv, hi;
+};
+__device__ __forceinline__ WsRecord ws_record(Status* st) {
+    WsRecord r;
+    r.lo_inv = __hip_atomic_load(&st->data_lo_inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    r.hi = __hip_atomic_load(&st->data_hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return r;
+}
+// The launch's own data span joins the record (one lane of one wave per
+// launch).  The record only grows, to the smallest range holding every span
+// added since the last zero fill.  Every span lies past the status block;
+// the span a launch checks (its flags or words and everything below them)
+// starts right at the end of the status block, and its own data lies above
+// it.  So a record that clears the checked span lies wholly above it, and
+// still does once the launch's own data has joined: every wave of a launch
+// gets the same answer, whether it reads the record before or after the
+// launch's own addition.
+__device__ __forceinline__ void ws_add_data(Status* st, WsSpan data) {
+    if (data.hi > data.lo) {
+        __hip_atomic_fetch_max(&st->data_lo_inv, ~data.lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max(&st->data_hi, data.hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+// False if data an earlier call left may lie where this launch needs zeros
+// (its flags or words): RING_EWORKSPACE is recorded and the wave must stop
+// before it signals anything.
+__device__ __forceinline__ bool ws_ok(Status* st, const WsRecord& rec, WsSpan zero, int lane) {
+    const unsigned long long lo = ~rec.lo_inv;
+    if (lo < zero.hi && zero.lo < rec.hi) {
+        if (lane == 0) report_error(st, RING_EWORKSPACE, 0, 0, 0);
+        return false;
+    }
+    return true;
 }
 
 // First look at a flag; callers issue their independent loads before they
@@ -124,10 +167,21 @@ __device__ inline bool wait_flag(int* f, Status* st, long long spin_limit, int r
 
 // Publish: wait until all of this wave's memory operations are complete (its
 // device-scope stores are at the coherence point, its loads of the
-// neighbour's data have returned), then set flag f.
-__device__ __forceinline__ void signal_flag(int* f, int lane) {
+// neighbour's data have returned), then set flag f.  With `check` (a debug
+// knob) the add returns the flag's old value, which must be 0: each flag is
+// set exactly once per launch and cleared by its reader, so anything else
+// means two producers or a missed clear, recorded as RING_EPROTOCOL at
+// (r, k, j).
+__device__ __forceinline__ void signal_flag(int* f, int lane, int check, Status* st, int r, int k, int j) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (lane == 0) __hip_atomic_fetch_add(f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) {
+        if (check) {
+            const int old = __hip_atomic_fetch_add(f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old != 0) report_error(st, RING_EPROTOCOL, r, k, j);
+        } else {
+            __hip_atomic_fetch_add(f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 }  // namespace ringc

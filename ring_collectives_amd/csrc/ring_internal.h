@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <cstddef>
+
 #include "ring_collectives.h"
 
 namespace ringc {
@@ -28,10 +30,34 @@ constexpr size_t kLlMaxBytes = 64 << 20;
 constexpr int kLlVec = 4;            // words per lane per tile position
 constexpr int kLlMaxRanges = 8;      // K ranges a low-latency reduce-scatter can sum as it reads
 
-// The error header every workspace starts with.
+// The status block every workspace starts with (kStatusBytes; a zero fill
+// initialises it).
+//   code, info      the error word: RING_OK, or the first asynchronous error
+//                   (RING_ETIMEOUT, RING_EWORKSPACE, RING_EPROTOCOL) and where
+//                   it happened, rank | round << 8 | min(tile, 32767) << 16.
+//   at 64           the fused all-gather + GEMM's finish counter.
+//   data_lo_inv,    the record of data calls have left in the workspace: the
+//   data_hi         byte range [~data_lo_inv, data_hi) holds every byte some
+//                   call since the last zero fill may have left non-zero
+//                   (bf16 partial sums, psum slots, partial GEMM tiles).  Zero
+//                   fill: ~0 and 0, an empty range.  A launch whose flags or
+//                   words would lie in that range stops with RING_EWORKSPACE
+//                   instead of reading stale data as set flags.
 struct Status {
-    int code;   // RING_OK or RING_ETIMEOUT
-    int info;   // rank | round << 8 | min(tile, 32767) << 16
+    int code;
+    int info;
+    int reserved[30];
+    unsigned long long data_lo_inv;
+    unsigned long long data_hi;
+};
+static_assert(offsetof(Status, data_lo_inv) == 128 && offsetof(Status, data_hi) == 136,
+              "status block layout");
+static_assert(sizeof(Status) <= kStatusBytes, "status block size");
+constexpr size_t kDoneOffset = 64;   // the all-gather + GEMM finish counter
+
+// A byte range of a workspace, as offsets from its start (hi == lo: none).
+struct WsSpan {
+    unsigned long long lo, hi;
 };
 
 // Parameters of one launch of the persistent chunk-step kernel.
@@ -69,6 +95,10 @@ struct RingParams {
     // ranges[(s P + q) n ..] (0: the input is src)
     const float* ranges;
     int nranges;
+    // what this launch needs zero in the workspace at its start (its flags or
+    // words) and where it leaves data (see Status)
+    WsSpan ws_zero, ws_data;
+    int check_flags;                  // debug: every flag must be 0 when it is set
 };
 
 // Internal element type of the ring launchers: an fp32 reduce-scatter whose
@@ -85,7 +115,9 @@ struct RingWs {
 
 int elem_bytes(int dtype);
 int elems_per_vec(int dtype);
-RingWs ring_ws_layout(int P, size_t n, int dtype, bool with_ll = true);
+// tile_elems: the tile the flag table is sized for (0: the smallest tile any
+// tuning uses, so one workspace serves every tuning).
+RingWs ring_ws_layout(int P, size_t n, int dtype, bool with_ll = true, size_t tile_elems = 0);
 
 // Tuning knobs: defaults, overridable by RING_* environment variables at
 // first use and by ring_set_tuning().
@@ -103,14 +135,19 @@ int ring_blocks_per_cu(int dtype, int tile_vecs, int kind);   // occupancy: 0 ri
 // may be src), with the owner's chunk of the sum rounded once to bf16 into
 // out16[q] (n / P elements) instead of stored in dst.  P >= 2.  The MLP
 // layer's unfused path.
+// extra: a further span of ws that the caller's other launches leave data
+// in, added to the workspace's record by this launch.
 int ring_reduce_scatter_bf16_out(const void* const* src, void* const* dst, void* const* out16, int P, size_t n,
-                                 void* ws, size_t ws_bytes, void* stream);
+                                 void* ws, size_t ws_bytes, void* stream, WsSpan extra);
 // The same reduce-scatter of inputs that are each the in-order sum of S
 // ranges (rank q's: ranges[(s P + q) n ..], s < S <= kLlMaxRanges), summed
 // as the rounds read them.  Only in the low-latency rounds: RING_EUNSUPPORTED,
 // with nothing launched, when the call does not take them.
 int ring_reduce_scatter_ranges_bf16_out(const float* ranges, int S, void* const* out16, int P, size_t n,
-                                        void* ws, size_t ws_bytes, void* stream);
+                                        void* ws, size_t ws_bytes, void* stream, WsSpan extra);
+// ring_all_gather with a further data span recorded (as above).
+int ring_all_gather_rec(const void* const* src_or_null, void* const* dst, int P, size_t n, int dtype,
+                        void* ws, size_t ws_bytes, void* stream, WsSpan extra);
 
 // GEMM + reduce-scatter workspace size (n = M * N per rank).
 size_t gemm_rs_workspace_bytes(int P, size_t n);
@@ -124,11 +161,14 @@ size_t ag_gemm_workspace_bytes(int P, size_t n);
 // and ksplit > 1 then splits K into that many ranges whose fp32 products go
 // to split[(s P + q) M N ..] instead (epi must be EPI_F32; out unused).  ag_gemm_run: gelu_bf16 stores
 // bf16(gelu(bf16(product))) instead of the fp32 product.
+// Both record `extra` (a span of ws other launches of the caller leave data
+// in) in the workspace's record, as well as their own data.
 int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, int P, int M, int N, int K,
                 void* ws, size_t ws_bytes, void* stream, int epi, size_t region_off, int batched = 0,
-                int ksplit = 1, float* split = nullptr);
+                int ksplit = 1, float* split = nullptr, WsSpan extra = WsSpan{0, 0});
 int ag_gemm_run(const void* const* A_shard, const void* const* B, void* const* A_full, void* const* C,
-                int P, int M, int N, int K, void* ws, size_t ws_bytes, void* stream, int gelu_bf16);
+                int P, int M, int N, int K, void* ws, size_t ws_bytes, void* stream, int gelu_bf16,
+                WsSpan extra = WsSpan{0, 0});
 
 // Device properties cached per device.
 struct DevInfo {

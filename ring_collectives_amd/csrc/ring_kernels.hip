@@ -106,7 +106,17 @@ __device__ __forceinline__ bool wait_flag(const RingParams& p, int k, int left, 
 }
 // Set flag (k, r, j): this rank finished tile j of round k-1.
 __device__ __forceinline__ void signal_flag(const RingParams& p, int k, int r, int j, int lane) {
-    signal_flag(flag_at(p, k, r, j), lane);
+    signal_flag(flag_at(p, k, r, j), lane, p.check_flags, p.status, r, k, j);
+}
+
+// Start of every ring launch: the first lane of the grid adds the launch's
+// data span to the workspace's record, and every wave issues the loads of
+// the record it checks (ws_ok) before it first signals a flag or passes a
+// word on -- which precedes its first wait, so no wave reads a flag or word
+// of a table that holds another call's data.
+__device__ __forceinline__ WsRecord ring_launch_begin(const RingParams& p) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) ws_add_data(p.status, p.ws_data);
+    return ws_record(p.status);
 }
 
 // ---------------------------------------------------------------- tile bodies
@@ -436,11 +446,13 @@ __device__ __forceinline__ bool map_wave(const RingParams& p, int& r, int& w) {
 
 template <int DT, int U>
 __global__ __launch_bounds__(kBlock) void ring_step_kernel(RingParams p) {
+    const WsRecord rec = ring_launch_begin(p);
     int r, w;
     if (!map_wave(p, r, w)) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int left = left_of(r, p.P);
     const int rs_end = p.P - 1;
+    bool checked = false;
     for (int j = w; j < p.T; j += p.waves_per_rank) {
         for (int k = p.k_begin; k < p.k_end; ++k) {
             const bool wait = (k > p.k_begin);
@@ -453,8 +465,13 @@ __global__ __launch_bounds__(kBlock) void ring_step_kernel(RingParams p) {
                 else ok = ag_tile<DT, U>(p, r, left, k, j, lane, wait);
             }
             if (!ok) return;
-            if (k + 1 < p.k_end && !(r == 0 && k + 1 == p.drop_round))
-                signal_flag(p, k + 1, r, j, lane);
+            if (k + 1 < p.k_end) {
+                if (!checked) {
+                    if (!ws_ok(p.status, rec, p.ws_zero, lane)) return;
+                    checked = true;
+                }
+                if (!(r == 0 && k + 1 == p.drop_round)) signal_flag(p, k + 1, r, j, lane);
+            }
         }
     }
 }
@@ -545,9 +562,11 @@ __device__ bool bidir_final_tile(const RingParams& p, int r, int from, int k, in
 
 template <int DT, int U>
 __global__ __launch_bounds__(kBlock) void ring_bidir_kernel(RingParams p) {
+    const WsRecord rec = ring_launch_begin(p);
     int r, w;
     if (!map_wave(p, r, w)) return;
     const int lane = threadIdx.x & (kWave - 1);
+    if (!ws_ok(p.status, rec, p.ws_zero, lane)) return;
     for (int j = w; j < p.T; j += p.waves_per_rank) {
         for (int k = p.k_begin; k < p.k_end; ++k) {
             const bool wait = (k > p.k_begin);
@@ -562,8 +581,7 @@ __global__ __launch_bounds__(kBlock) void ring_bidir_kernel(RingParams p) {
                 ok = bidir_final_tile<DT, U>(p, r, b.from, k, j, b.t, lane, wait);
             }
             if (!ok) return;
-            if (k + 1 < p.k_end && !(r == 0 && k + 1 == p.drop_round))
-                signal_flag(p, k + 1, r, j, lane);
+            if (k + 1 < p.k_end && !(r == 0 && k + 1 == p.drop_round)) signal_flag(p, k + 1, r, j, lane);
         }
     }
 }
@@ -610,7 +628,7 @@ __device__ bool psum_tile(const RingParams& p, int d, int j, int lane) {
     const rsrc_t out = tile_view((char*)p.dst[d] + e0 * ESZ, nb);
     const bool drop = (d == 0 && p.drop_round > 0);   // test hook (0 = off)
     auto sig = [&](int* f, int row) {
-        if (!(drop && row == p.drop_round)) signal_flag(f, lane);
+        if (!(drop && row == p.drop_round)) signal_flag(f, lane, p.check_flags, p.status, d, row, j);
     };
     auto wait = [&](int* f, int s) {
         return wait_flag(f, p.status, p.spin_limit, d, s, j, lane, peek_flag(f));
@@ -733,9 +751,11 @@ __device__ bool psum_tile(const RingParams& p, int d, int j, int lane) {
 
 template <int DT, int U>
 __global__ __launch_bounds__(kBlock) void ring_psum_kernel(RingParams p) {
+    const WsRecord rec = ring_launch_begin(p);
     int r, w;
     if (!map_wave(p, r, w)) return;
     const int lane = threadIdx.x & (kWave - 1);
+    if (!ws_ok(p.status, rec, p.ws_zero, lane)) return;
     for (int j = w; j < p.T; j += p.waves_per_rank)
         if (!psum_tile<DT, U>(p, r, j, lane)) return;
 }
@@ -749,7 +769,10 @@ __global__ __launch_bounds__(kBlock) void ring_psum_kernel(RingParams p) {
 // polls that word until the mark is set and then clears it (it is the word's
 // only reader), so a finished launch leaves every word zero.  An aligned
 // 8-byte access is single-copy atomic, so a word never shows the mark with a
-// stale value.  With flags a round costs four trips to the device coherence
+// stale value: LLVM's AMDGPU backend (AMDGPUUsage, the GFX942 memory model,
+// which gfx950 follows) implements a monotonic atomic load or store of up to
+// 64 bits as one plain load or store instruction, which is sound only
+// because a naturally aligned access of that size is single-copy atomic.  With flags a round costs four trips to the device coherence
 // point one after the other (the data store and its acknowledgement, the
 // flag add, the poll that sees it, the data load); here two (the store, the
 // poll that returns the data).  fp32 partial sums of bf16 data travel as
@@ -854,10 +877,19 @@ __device__ bool ll_recv(const RingParams& p, int k, int from, long long o0, unsi
     return true;
 }
 
-// Pass this lane's values of round k on to the right neighbour.
+// Pass this lane's values of round k on to the right neighbour.  With the
+// check_flags debug knob every word must still be empty (each word is
+// written once per launch and cleared by its one reader): a mark already
+// set is recorded as RING_EPROTOCOL at (r, k + 1, j).
 __device__ __forceinline__ void ll_send(const RingParams& p, int k, int r, long long o0,
-                                        const unsigned (&v)[kLlVec]) {
+                                        const unsigned (&v)[kLlVec], int j, int lane) {
     const rsrc_t w = ll_words(p, k, r);
+    if (p.check_flags) {
+        bool busy = false;
+#pragma unroll
+        for (int i = 0; i < kLlVec; ++i) busy |= ld8<POL_DEV>(w, (unsigned)(o0 + i * kWave) * 8u)[1] != 0u;
+        if (__any(busy) && lane == 0) report_error(p.status, RING_EPROTOCOL, r, k + 1, j);
+    }
 #pragma unroll
     for (int i = 0; i < kLlVec; ++i) {
         const u32x2 x = {v[i], 1u};
@@ -867,12 +899,14 @@ __device__ __forceinline__ void ll_send(const RingParams& p, int k, int r, long 
 
 template <int DT>
 __global__ __launch_bounds__(kBlock) void ring_ll_kernel(RingParams p) {
+    const WsRecord rec = ring_launch_begin(p);
     int r, w;
     if (!map_wave(p, r, w)) return;
     const int lane = threadIdx.x & (kWave - 1);
     const int P = p.P;
     const int left = left_of(r, P);
     const long long C = p.C;
+    bool checked = false;
     for (int j = w; j < p.T; j += p.waves_per_rank) {
         const long long o0 = (long long)j * kLlTile + lane;
         for (int k = p.k_begin; k < p.k_end; ++k) {
@@ -962,7 +996,11 @@ __global__ __launch_bounds__(kBlock) void ring_ll_kernel(RingParams p) {
 #pragma unroll
                 for (int i = 0; i < kLlVec; ++i) ll_st<DT>(out, o0 + i * kWave, v[i]);
             }
-            if (send) ll_send(p, k, r, o0, v);
+            if (k + 1 < p.k_end && !checked) {
+                if (!ws_ok(p.status, rec, p.ws_zero, lane)) return;
+                checked = true;
+            }
+            if (send) ll_send(p, k, r, o0, v, j, lane);
         }
     }
 }

@@ -147,25 +147,28 @@ int mlp_unfused(const void* const* x_shard, const void* const* W1, const void* c
                 void* ws, size_t ws_bytes, const MlpWs& lay, void* stream) {
     const int Fr = F / P;
     const size_t nd = (size_t)M * D;
-    int rc = ring_all_gather(x_shard, x_full, P, nd, RING_BF16, ws, lay.gemm_off, stream);
+    // the partial sums and range products stay in the workspace: every
+    // launch adds that span to the workspace's record
+    const WsSpan data{lay.part_off, lay.total};
+    int rc = ring_all_gather_rec(x_shard, x_full, P, nd, RING_BF16, ws, lay.gemm_off, stream, data);
     if (rc != RING_OK) return rc;
     void* part[RING_MAX_RANKS];
     for (int q = 0; q < P; ++q) part[q] = (char*)ws + lay.part_off + (size_t)q * nd * sizeof(float);
     const size_t goff = lay.gemm_off - kStatusBytes;   // the GEMMs' flags after the ring's
     // every rank's product in one launch each (the batched mode of the fused kernel)
     rc = gemm_rs_run((const void* const*)x_full, W1, h, P, M, Fr, D, ws, lay.part_off, stream, EPI_GELU_BF16,
-                     goff, 1);
+                     goff, 1, 1, nullptr, data);
     if (rc != RING_OK) return rc;
     const int S = mlp_split(P, M, D, F);
     float* split = (float*)((char*)ws + lay.split_off);
     rc = gemm_rs_run((const void* const*)h, W2, part, P, M, D, Fr, ws, lay.part_off, stream, EPI_F32, goff, 1,
-                     S, S > 1 ? split : nullptr);
+                     S, S > 1 ? split : nullptr, data);
     if (rc != RING_OK) return rc;
     if (S > 1) {
         // Where the reduce-scatter takes its low-latency rounds it sums the
         // ranges itself as it reads them, in the same order; otherwise a
         // kernel sums them into the partials first.
-        rc = ring_reduce_scatter_ranges_bf16_out(split, S, out_shard, P, nd, ws, lay.gemm_off, stream);
+        rc = ring_reduce_scatter_ranges_bf16_out(split, S, out_shard, P, nd, ws, lay.gemm_off, stream, data);
         if (rc != RING_EUNSUPPORTED) return rc;
         PartTab pt;
         for (int q = 0; q < P; ++q) pt.p[q] = (float*)part[q];
@@ -178,7 +181,7 @@ int mlp_unfused(const void* const* x_shard, const void* const* W1, const void* c
     // in place: a rank's chunk is rewritten only in a round after the ones
     // that read it as input
     return ring_reduce_scatter_bf16_out((const void* const*)part, part, out_shard, P, nd, ws, lay.gemm_off,
-                                        stream);
+                                        stream, data);
 }
 
 }  // namespace

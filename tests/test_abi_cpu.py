@@ -50,8 +50,8 @@ def test_binding_covers_the_header():
 
 def test_strerror():
     for code in (N.RING_OK, N.RING_EINVAL, N.RING_EUNSUPPORTED, N.RING_EWORKSPACE,
-                 N.RING_EHIP, N.RING_ETIMEOUT):
-        assert N.strerror(code)
+                 N.RING_EHIP, N.RING_ETIMEOUT, N.RING_EPROTOCOL):
+        assert N.strerror(code) != "unknown error"
     assert N.strerror(12345) == "unknown error"
 
 
@@ -197,13 +197,18 @@ def test_tuning_roundtrip_and_validation():
         assert N.get_tuning()["tile_vecs"] == 16
         N.set_tuning(gemm_tile_n=256)
         assert N.get_tuning()["gemm_tile_n"] == 256
+        assert old["check_flags"] == 0
+        N.set_tuning(check_flags=1)
+        assert N.get_tuning()["check_flags"] == 1
         for bad in ({"tile_vecs": 5}, {"waves_per_cu": 1}, {"waves_per_cu": 32}, {"map_mode": 1},
                     {"map_mode": 7},
                     {"timeout_s": 0.0}, {"stepwise": 2}, {"drop_round": -1},
                     {"gemm_tile_n": 32}, {"gemm_tile_n": 192},
-                    {"ll_max_chunk_bytes": -1}, {"ll_max_chunk_bytes": (256 << 10) + 1}):
+                    {"ll_max_chunk_bytes": -1}, {"ll_max_chunk_bytes": (256 << 10) + 1},
+                    {"check_flags": 2}, {"check_flags": -1}):
             with pytest.raises(N.RingError):
                 N.set_tuning(**bad)
     finally:
         t = N.Tuning(**old)
         assert N.lib().ring_set_tuning(ctypes.byref(t)) == N.RING_OK
+
