@@ -353,6 +353,15 @@ def all_gather_gemm(A_shards: np.ndarray, B: np.ndarray):
     return full, gemm_products_f32(full, B)
 
 
+def all_gather_gemm_f64(A_shards: np.ndarray, B: np.ndarray, q: int) -> tuple:
+    """Every element of rank q's product: A_full @ B[q] in fp64 and the
+    magnitude |A_full| @ |B[q]|, with A_full the concatenation of the row
+    blocks.  Returns two (M, N) arrays."""
+    A_shards = _ranks(A_shards, np.uint16)
+    P, Mc, _ = A_shards.shape
+    return all_gather_gemm_rows_f64(A_shards, B, q, np.arange(P * Mc))
+
+
 def all_gather_gemm_rows_f64(A_shards: np.ndarray, B: np.ndarray, q: int, rows) -> tuple:
     """Sampled reference for all_gather_gemm: rows `rows` of A_full @ B[q] in
     fp64 and the magnitude denominator |A_full[rows]| @ |B[q]|, with A_full
@@ -363,6 +372,15 @@ def all_gather_gemm_rows_f64(A_shards: np.ndarray, B: np.ndarray, q: int, rows) 
     a = bf16_to_f32(A_shards.reshape(P * Mc, K)[rows]).astype(np.float64)
     b = bf16_to_f32(_ranks(B, np.uint16)[q]).astype(np.float64)
     return a @ b, np.abs(a) @ np.abs(b)
+
+
+def gemm_reduce_scatter_f64(A: np.ndarray, B: np.ndarray, r: int) -> tuple:
+    """Every element of output rank r: rows [r M/P, (r+1) M/P) of
+    sum_q A_q @ B_q in fp64, and the magnitude sum_q |A_q| @ |B_q| of those
+    rows (each exact product counted once).  Returns two (M/P, N) arrays."""
+    A = _ranks(A, np.uint16)
+    P, M, _ = A.shape
+    return gemm_reduce_scatter_rows_f64(A, B, r, np.arange(M // P))
 
 
 def gemm_reduce_scatter_rows_f64(A: np.ndarray, B: np.ndarray, r: int, rows) -> tuple:
@@ -464,34 +482,61 @@ def _exact_in_fp32(a: np.ndarray, b: np.ndarray) -> bool:
     """True if every partial sum of every dot product of a @ b is exact in
     fp32 whatever the order: all products are multiples of a common power of
     two g (the coarsest grid both operands sit on) and sum |a b| < 2^24 g."""
-    def grid_bits(v):
+    def lsb_exp(v):
+        # the exponent of the lowest set bit of every nonzero value (each v is
+        # m 2^e with 0.5 <= |m| < 1 and at most 53 significant bits), min over v
         v = v[v != 0]
-        for k in range(-160, 161):
-            s = np.ldexp(v, k)
-            if np.all(s == np.rint(s)):
-                return k
-        return None
-    ka, kb = grid_bits(a), grid_bits(b)
-    if ka is None or kb is None:
-        return False
-    g = np.ldexp(1.0, -(ka + kb))
+        if v.size == 0:
+            return None
+        m, e = np.frexp(v)
+        mi = np.abs(m * 2.0 ** 53).astype(np.int64)          # exact: 53-bit integers
+        tz = np.zeros(mi.shape, dtype=np.int64)
+        for sh in (32, 16, 8, 4, 2, 1):                      # count trailing zero bits
+            low = (mi & ((1 << sh) - 1)) == 0
+            tz += np.where(low, sh, 0)
+            mi = np.where(low, mi >> sh, mi)
+        return int((e - 53 + tz).min())
+    la, lb = lsb_exp(a), lsb_exp(b)
+    if la is None or lb is None:
+        return True                                          # a zero operand: every sum is 0
+    g = np.ldexp(1.0, la + lb)
     return float((np.abs(a) @ np.abs(b)).max(initial=0.0)) < 2.0 ** 24 * g
 
 
 _GELU_ARGMIN = -0.7517916     # gelu's only minimum lies in [-0.7518, -0.7517]
 
 
-def gelu_fp32_rel_error(x: np.ndarray) -> np.ndarray:
-    """Relative error allowed for gelu(x) evaluated in fp32 as x sigmoid(t),
-    t = 2 sqrt(2/pi) (x + 0.044715 x^3), with the exponential exp(-|t|)
-    accurate to 2 units in the last place: the constants and the cube and
-    sums before t carry at most 7 roundings, an absolute error of 7 u |t| in
-    t and so a relative 7 u |t| in the exponential; sigmoid, 1 + e, the
-    division and the last product add a few units more (u = 2^-24).  The
-    bound used is twice (8 + 7 |t|) u."""
+def gelu_fp32_error(x: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """Absolute error allowed for gelu(x) = g evaluated in fp32 (the kernel
+    evaluates x sigmoid(t), t = 2 sqrt(2/pi) (x + 0.044715 x^3), through an
+    exponential e = exp(-|t|) <= 1):
+      * t: the constants, the cube and the sum (no cancellation: x and
+        0.044715 x^3 have the same sign) carry at most 7 roundings, an
+        absolute error of 7 u |t|, so e has a relative error of 7 u |t| plus
+        2 units of its own (u = 2^-24);
+      * x >= 0: gelu = x / (1 + e), and e's relative error reaches the result
+        damped by e / (1 + e) (once e is below u it does not reach it at
+        all); x < 0: gelu = x e / (1 + e) carries it undamped;
+      * 1 + e, the division and the product add a few units more: 8 in all;
+      * the bound used is twice that, relative to |g|;
+      * near fp32's underflow (x down to about -10.5, where e is subnormal)
+        an absolute |x| 2^-147 covers the spacing of fp32's subnormals, 2^-149
+        (below -16 the result is 0 in any evaluation; the floor stays 2^-143,
+        which rounds to 0 in bf16).
+    The exponential's error grows with |t|; the page's form through tanh
+    would instead lose all relative accuracy where 1 + tanh cancels (x below
+    about -3.5), which is why an implementation evaluates the logistic."""
     x = np.asarray(x, dtype=np.float64)
-    t = 2.0 * _GELU_C * (x + 0.044715 * x * x * x)
-    return 2.0 * (8.0 + 7.0 * np.abs(t)) * 2.0 ** -24
+    g = np.asarray(g, dtype=np.float64)
+    t = np.abs(2.0 * _GELU_C * (x + 0.044715 * x * x * x))
+    with np.errstate(over="ignore", invalid="ignore"):
+        e = np.exp(-t)
+        damp = np.where(x >= 0, np.where(e > 0, e / (1.0 + e), 0.0), 1.0)
+        tw = np.where(damp > 0, t * damp, 0.0)
+        rel = 2.0 * (8.0 + 7.0 * tw) * 2.0 ** -24
+        rel_part = np.where(g != 0, rel * np.abs(g), 0.0)
+    floor = np.ldexp(np.minimum(np.abs(x), 16.0), -147)
+    return rel_part + floor
 
 
 def tp_mlp_bounds(x_shards: np.ndarray, W1: np.ndarray, W2: np.ndarray, r: int, rows):
@@ -505,7 +550,7 @@ def tp_mlp_bounds(x_shards: np.ndarray, W1: np.ndarray, W2: np.ndarray, r: int, 
         implementation may produce (the first product within the
         recursive-summation bound D 2^-24 sum|x w|, or exact when the
         operands' grid makes it so, rounded to bf16; gelu of that within
-        gelu_fp32_rel_error, rounded to bf16);
+        gelu_fp32_error, rounded to bf16);
       s (R, D) fp64: sum_q h_ref[q] @ W2[q] at those rows;
       t (R, D) fp64: how far an implementation's fp32 out may lie from s:
         sum_q |h - h_ref| @ |W2[q]| over the h intervals plus
@@ -534,9 +579,12 @@ def tp_mlp_bounds(x_shards: np.ndarray, W1: np.ndarray, W2: np.ndarray, r: int, 
         g_lo = np.minimum(gelu_tanh(b_lo), gelu_tanh(b_hi))
         g_lo = np.where((b_lo < _GELU_ARGMIN) & (b_hi > _GELU_ARGMIN), gelu_tanh(_GELU_ARGMIN), g_lo)
         g_hi = np.maximum(gelu_tanh(b_lo), gelu_tanh(b_hi))
-        rel = np.maximum(gelu_fp32_rel_error(b_lo), gelu_fp32_rel_error(b_hi))
-        h_lo[q] = bf16_nearest(g_lo - rel * np.abs(g_lo))
-        h_hi[q] = bf16_nearest(g_hi + rel * np.abs(g_hi))
+        # gelu's evaluation error at the ends of the range (and at gelu's
+        # minimum, where g_lo may sit); each end's own bound
+        err_lo = np.maximum(gelu_fp32_error(b_lo, g_lo), gelu_fp32_error(b_hi, g_lo))
+        err_hi = np.maximum(gelu_fp32_error(b_lo, g_hi), gelu_fp32_error(b_hi, g_hi))
+        h_lo[q] = bf16_nearest(g_lo - err_lo)
+        h_hi[q] = bf16_nearest(g_hi + err_hi)
         hr = _f64(h_ref[q])
         w2 = np.abs(_f64(W2[q]))
         s = s + hr @ _f64(W2[q])

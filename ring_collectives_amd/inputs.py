@@ -25,7 +25,9 @@ here, so only shape, type and distribution follow them):
   * GEMM + reduce-scatter: P = 4, A_q and B_q bf16 4096 x 4096,
     normal(0, 1/64), seed 4 (all-gather + GEMM: the same shapes, seed 5);
   * tensor-parallel MLP layer: P = 4, x [M, 1024], W1 [1024, 16384],
-    W2 [16384, 1024], seed 6 (see mlp_operands).
+    W2 [16384, 1024], seed 6: plain normal bf16 operands (mlp_operands_normal)
+    and operands on fixed-point grids whose first product is exact
+    (mlp_operands).
 
 Two-dimensional per-rank arrays of shape (R, w * P) are stored chunk-major:
 chunk c (a flat, contiguous run of R * w elements) is column block c of the
@@ -187,6 +189,29 @@ def mlp_operands(P: int = 4, M: int = 8192, D: int = 1024, F: int = 16384, seed:
         w1[q] = bf16_bits((b / 1024.0).astype(np.float32))
         c = g.standard_normal((Fr, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(F))
         w2[q] = bf16_bits(c)
+
+    with ThreadPoolExecutor(_threads(P)) as ex:
+        list(ex.map(draw, range(P)))
+    return x, w1, w2
+
+
+def mlp_operands_normal(P: int = 4, M: int = 8192, D: int = 1024, F: int = 16384, seed: int = SEED_MLP):
+    """Tensor-parallel MLP layer operands as bf16 bit patterns, shaped as in
+    mlp_operands, with plain normal values rounded to bf16 (nearest even):
+    x normal(0, 1), W1 normal(0, 1/D), W2 normal(0, 1/F) -- the scale of an
+    initialised layer.  Rank q draws x_q, W1_q and W2_q, in that order, from
+    its own child stream."""
+    Mq, Fr = M // P, F // P
+    x = np.empty((P, Mq, D), dtype=np.uint16)
+    w1 = np.empty((P, D, Fr), dtype=np.uint16)
+    w2 = np.empty((P, Fr, D), dtype=np.uint16)
+    gens = rank_streams(seed, P)
+
+    def draw(q):
+        g = gens[q]
+        x[q] = bf16_bits(g.standard_normal((Mq, D), dtype=np.float32))
+        w1[q] = bf16_bits(g.standard_normal((D, Fr), dtype=np.float32) * np.float32(1.0 / np.sqrt(D)))
+        w2[q] = bf16_bits(g.standard_normal((Fr, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(F)))
 
     with ThreadPoolExecutor(_threads(P)) as ex:
         list(ex.map(draw, range(P)))

@@ -113,22 +113,27 @@ def test_full_occupancy_integer_exact(P, tile_n):
         assert bad == 0, "call %d: %d elements differ" % (call, bad)
 
 
-def test_full_size_sampled_rows():
+def test_full_size_every_element():
     """P = 4, A 4096 x 4096 in row blocks of 1024, B_q 4096 x 4096,
-    normal(0, 1/64): the gathered A everywhere, sampled output rows of every
-    rank against the fp64 product."""
+    normal(0, 1/64), seed 5 (the all-gather + GEMM workload), in the default
+    launch configuration: the gathered A bit for bit, and every element of
+    every rank's C within K 2^-24 |A_full| |B_q| of the fp64 product (full
+    host products, no sampling)."""
     P, M, Nn, K = 4, 4096, 4096, 4096
     note("ag_gemm full size generate")
-    As, B = inputs.gemm_operands(P, M // P, Nn, K, seed=104)
+    As, B = inputs.gemm_operands(P, M // P, Nn, K, seed=5)
     note("ag_gemm full size run")
     gf, gc, _ = _run(As, B)
     np.testing.assert_array_equal(gf, np.stack([As.reshape(M, K)] * P))
-    rows = np.unique(np.concatenate([[0, 255, 256, 1023, 1024, 4095],
-                                     np.random.default_rng(6).integers(0, M, size=10)]))
+    assert np.all(np.isfinite(gc))
+    worst = 0.0
     for q in range(P):
-        ref, mag = oracle.all_gather_gemm_rows_f64(As, B, q, rows)
-        err = np.abs(gc[q][rows].astype(np.float64) - ref) / mag
-        assert err.max() <= K * 2.0 ** -24, (q, err.max())
+        note("ag_gemm full size check rank %d" % q)
+        ref, mag = oracle.all_gather_gemm_f64(As, B, q)
+        err = np.abs(gc[q].astype(np.float64) - ref) / mag
+        worst = max(worst, float(err.max()))
+    assert worst <= K * 2.0 ** -24, worst
+    print("max normalised error %.3e (bound %.3e)" % (worst, K * 2.0 ** -24))
 
 
 def test_errors():

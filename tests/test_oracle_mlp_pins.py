@@ -215,3 +215,99 @@ def test_page_cost_figures():
     assert f["flop"] == 4 * 2 * 2147483648
     assert f["shard_bytes"] == 131072
     assert f["ring_bytes_per_direction"] == 3 * 131072
+
+
+# ---------------------------------------------------------------- gelu's fp32 allowance
+def _every_finite_bf16():
+    u = np.arange(65536, dtype=np.uint32)
+    return u[((u >> 7) & 0xFF) != 255].astype(np.uint16)
+
+
+@pytest.fixture(scope="module")
+def gelu_intervals():
+    """The oracle's interval for h = bf16(gelu(b)) at every finite bf16 b, as
+    tp_mlp_bounds gives it for a layer whose first product is exactly b
+    (x rows are unit vectors, W1 holds the values)."""
+    vals = _every_finite_bf16()
+    D = F = 256
+    w1 = np.concatenate([vals, vals[:D * F - len(vals)]]).reshape(1, D, F)
+    x = np.zeros((1, 256, D), dtype=np.float32)
+    x[0, np.arange(256), np.arange(256)] = 1.0
+    _, lo, hi, _, _ = oracle.tp_mlp_bounds(inputs.bf16_bits(x), w1, np.zeros((1, F, D), np.uint16), 0,
+                                           np.arange(256))
+    n = len(vals)
+    b = (vals.astype(np.uint32) << 16).view(np.float32)
+    return b, lo[0].reshape(-1)[:n], hi[0].reshape(-1)[:n]
+
+
+def _bf16_of(g32: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 (torch's conversion, nearest-even) as fp64 values."""
+    return torch.from_numpy(np.ascontiguousarray(g32, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _gelu_f32_tanh(b, c=np.sqrt(2.0 / np.pi), k=0.044715):
+    """The page's formula, 0.5 x (1 + tanh(c (x + k x^3))), in NumPy float32."""
+    c, k = np.float32(c), np.float32(k)
+    with np.errstate(over="ignore", invalid="ignore"):
+        z = c * (b + k * b * b * b)
+        return np.float32(0.5) * b * (np.float32(1.0) + np.tanh(z)), np.float32(1.0) + np.tanh(z)
+
+
+def _gelu_f32_logistic(b, c=np.sqrt(2.0 / np.pi), k=0.044715, split=True):
+    """x sigmoid(2z) in NumPy float32 through e = exp(-|2z|) <= 1:
+    x / (1 + e) for x >= 0, x e / (1 + e) for x < 0 (split=False: the first
+    form everywhere)."""
+    c, k = np.float32(c), np.float32(k)
+    with np.errstate(over="ignore", invalid="ignore"):
+        t = np.float32(2.0) * c * (b + k * b * b * b)
+        e = np.exp(-np.abs(t))
+        pos = b / (np.float32(1.0) + e)
+        neg = b * e / (np.float32(1.0) + e)
+        return np.where(b >= 0, pos, neg) if split else b / (np.float32(1.0) + np.exp(-t))
+
+
+def _inside(h, lo, hi):
+    return (lo <= h) & (h <= hi)
+
+
+def test_gelu_intervals_are_tight(gelu_intervals):
+    """One admissible h on at least 99% of all finite bf16 inputs (what is
+    left is mostly subnormal inputs whose gelu, x/2 to within 1e-40 relative,
+    sits on a bf16 rounding tie)."""
+    _, lo, hi = gelu_intervals
+    assert np.mean(lo == hi) >= 0.99, np.mean(lo == hi)
+
+
+def test_independent_fp32_gelu_lands_inside(gelu_intervals):
+    """Plain fp32 evaluations written apart from the oracle and the kernel
+    land inside the intervals: the logistic form everywhere; the page's tanh
+    form, in NumPy float32 and as torch's float32 gelu, wherever 1 + tanh z
+    holds at least 1/16 (further left it cancels and loses the relative
+    accuracy the bound is about: the reason an implementation evaluates the
+    logistic)."""
+    b, lo, hi = gelu_intervals
+    assert _inside(_bf16_of(_gelu_f32_logistic(b)), lo, hi).all()
+    g_tanh, one_plus = _gelu_f32_tanh(b)
+    ok = one_plus >= np.float32(1.0 / 16)
+    assert ok[b >= -1.8].all() and ok.sum() > 0.7 * len(b)  # all x >= -1.8 (3/4 of the bf16 values)
+    assert _inside(_bf16_of(g_tanh), lo, hi)[ok].all()
+    g_torch = torch.nn.functional.gelu(torch.from_numpy(b), approximate="tanh").numpy()
+    assert _inside(_bf16_of(g_torch), lo, hi)[ok].all()
+
+
+@pytest.mark.parametrize("mistake", ["k=0.04472", "c=sqrt(1/pi)", "no cube", "one branch", "tanh unguarded"])
+def test_plausible_gelu_mistakes_fall_outside(gelu_intervals, mistake):
+    """Each plausible slip in an fp32 gelu puts results outside the
+    intervals on some inputs: the intervals are tight enough to catch it."""
+    b, lo, hi = gelu_intervals
+    if mistake == "k=0.04472":
+        g = _gelu_f32_logistic(b, k=0.04472)
+    elif mistake == "c=sqrt(1/pi)":
+        g = _gelu_f32_logistic(b, c=np.sqrt(1.0 / np.pi))
+    elif mistake == "no cube":
+        g = _gelu_f32_logistic(b, k=0.0)
+    elif mistake == "one branch":                             # x / (1 + exp(-t)) overflows for x < -10
+        g = _gelu_f32_logistic(b, split=False)
+    else:                                                   # the tanh form where it cancels
+        g = _gelu_f32_tanh(b)[0]
+    assert (~_inside(_bf16_of(g), lo, hi)).sum() >= 5
