@@ -367,6 +367,34 @@ typedef struct {
 void ring_get_tuning(ring_tuning_t *t);
 int ring_set_tuning(const ring_tuning_t *t);   /* RING_EINVAL on bad values */
 
+/*
+ * ring_all_reduce for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it): the same
+ * call without a workspace argument.  Its flags, low-latency words and bf16
+ * partial sums live in a static device array of RING_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends;
+ * the call allocates nothing and calls no allocating routine.  Results are
+ * the same bits as ring_all_reduce's.
+ *
+ * Each call first clears the part of that array it needs zero (a fill
+ * kernel on `stream`, no memset), so no call depends on what an earlier one
+ * left there.  Every call on one device shares the one array: calls that
+ * overlap in time on one device (different streams, or host threads) race
+ * and give undefined results; order them.
+ *
+ * The flag table is sized for the tile the call actually uses (16 KiB tiles
+ * by default), plus, for bf16, P n fp32 partial sums; a call that needs more
+ * than RING_NOALLOC_SCRATCH_BYTES returns RING_EWORKSPACE synchronously and
+ * launches nothing (at the default tuning: fp32 and int32 up to about 73 Mi
+ * elements per rank at P = 8, bf16 up to about 0.5 Mi).  Other argument
+ * errors as ring_all_reduce.  A watchdog timeout leaves the outputs
+ * undefined and is not reported (there is no workspace to read it from);
+ * the next call starts from a cleared array.
+ */
+#define RING_NOALLOC_SCRATCH_BYTES (16u << 20)
+int ring_all_reduce_noalloc(const void *const *src, void *const *dst, int P, size_t n,
+                            int dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ RING_F32, RING_BF16, RING_I32 = 0, 1, 2
 RING_OK, RING_EINVAL, RING_EUNSUPPORTED, RING_EWORKSPACE, RING_EHIP, RING_ETIMEOUT, RING_EPROTOCOL = (
     0, -1, -2, -3, -4, -5, -6)
 MAX_RANKS = 64
+NOALLOC_SCRATCH_BYTES = 16 << 20   # RING_NOALLOC_SCRATCH_BYTES
 
 _vp = ctypes.c_void_p
 _pp = ctypes.POINTER(ctypes.c_void_p)
@@ -34,6 +35,7 @@ SIGNATURES = {
     "ring_psum_circulating": (_i, [_pp, _pp, _i, _sz, _i, _vp, _sz, _vp]),
     "ring_all_gather": (_i, [_pp, _pp, _i, _sz, _i, _vp, _sz, _vp]),
     "ring_all_reduce": (_i, [_pp, _pp, _i, _sz, _i, _vp, _sz, _vp]),
+    "ring_all_reduce_noalloc": (_i, [_pp, _pp, _i, _sz, _i, _vp]),
     "gemm_reduce_scatter": (_i, [_pp, _pp, _pp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "all_gather_gemm": (_i, [_pp, _pp, _pp, _pp, _i, _i, _i, _i, _vp, _sz, _vp]),
     "tp_mlp_layer": (_i, [_pp, _pp, _pp, _pp, _pp, _pp, _i, _i, _i, _i, _vp, _sz, _vp]),

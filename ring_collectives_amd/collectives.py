@@ -126,6 +126,22 @@ def all_reduce(src, dst, ws=None, stream=None):
                   src, dst, ws, stream)
 
 
+def all_reduce_noalloc(src, dst, stream=None) -> None:
+    """ring_all_reduce without a workspace argument: the library's static
+    device array serves as the workspace, so the call allocates nothing.
+    Calls that overlap in time on one device race (one shared array)."""
+    n = src[0].numel()
+    P = len(src)
+    ps = _ranks(src, "ring_all_reduce_noalloc", n, src[0].dtype)
+    pd = _ranks(dst, "ring_all_reduce_noalloc", n, src[0].dtype)
+    if len(pd) != P:
+        raise ValueError("ring_all_reduce_noalloc: src and dst rank counts differ")
+    a, ka = N.ptr_array(ps)
+    b, kb = N.ptr_array(pd)
+    N.check(N.lib().ring_all_reduce_noalloc(a, b, P, n, _dtype(src[0]), _stream(stream)),
+            "ring_all_reduce_noalloc")
+
+
 def all_gather(dst, src=None, ws=None, stream=None):
     """Ring all-gather.  src=None: chunk r of dst[r] already holds rank r's
     piece; otherwise src[r] is rank r's compact piece (numel = n / P)."""

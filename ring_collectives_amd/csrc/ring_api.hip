@@ -206,10 +206,14 @@ static WsSpan span_hull(WsSpan a, WsSpan b) {
 // Launch the chunk-step kernel over global rounds [k_begin, k_end) (the
 // bidirectional kernel over its rounds 0 .. P-1 when bidir is set).
 // extra: a further span of ws the caller's other launches leave data in.
+// scratch: ws is the no-alloc entry point's static array -- its flag table
+// is sized for the tile this call uses, and the part the call needs zero
+// is cleared (a fill kernel) before the launch.
 static int run_ring(const void* const* src, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream, int k_begin, int k_end,
                     int compact_src, int bidir = 0, void* const* out16 = nullptr,
-                    const float* ranges = nullptr, int nranges = 0, WsSpan extra = WsSpan{0, 0}) {
+                    const float* ranges = nullptr, int nranges = 0, WsSpan extra = WsSpan{0, 0},
+                    bool scratch = false) {
     // reduce-scatter rounds of bf16 data carry fp32 partial sums
     const bool need_carry = dtype == RING_BF16 && (bidir || k_begin < P - 1);
     auto need = [&](const RingWs& l) { return need_carry ? l.total : l.total - l.carry_bytes; };
@@ -224,9 +228,10 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
     // only the flags) keeps them, and the bf16 carry after them, whether or
     // not this call runs those rounds.  So a call in the flag rounds never
     // leaves its carry where the same shape's words lie.
-    const RingWs with_ll = ring_ws_layout(P, n, dtype, true);
+    const size_t lay_tile = scratch ? (size_t)kWave * tu.tile_vecs * elems_per_vec(dtype) : 0;
+    const RingWs with_ll = ring_ws_layout(P, n, dtype, true, lay_tile);
     const bool has_ll = with_ll.ll_bytes && ws_bytes >= need(with_ll);
-    const RingWs lay = has_ll ? with_ll : ring_ws_layout(P, n, dtype, false);
+    const RingWs lay = has_ll ? with_ll : ring_ws_layout(P, n, dtype, false, lay_tile);
     if (ws_bytes < need(lay)) return RING_EWORKSPACE;
     // Low-latency rounds for small one-way calls where the workspace holds
     // their words (not in stepwise mode, whose rounds are separate launches
@@ -313,6 +318,7 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
     prm.waves_per_rank = W;
     prm.map_mode = map_mode;
     prm.drop_round = tu.drop_round;
+    if (scratch && launch_fill_zero(ws, prm.ws_zero.hi, as_stream(stream)) != hipSuccess) return RING_EHIP;
     if (tu.stepwise) {
         // One launch per round: stream order replaces the flags (no waits,
         // no signals inside a launch of a single round).
@@ -453,7 +459,7 @@ int ring_ppermute(const void* const* src, void* const* dst, int P, size_t n, int
 enum { KIND_RS, KIND_AR, KIND_RS_BIDIR };
 
 static int rs_or_ar(const void* const* src, void* const* dst, int P, size_t n, int dtype,
-                    void* ws, size_t ws_bytes, void* stream, int kind) {
+                    void* ws, size_t ws_bytes, void* stream, int kind, bool scratch = false) {
     int rc = check_common(src, P, n, dtype, true);
     if (rc) return rc;
     if ((rc = check_common(dst, P, n, dtype, true))) return rc;
@@ -467,7 +473,9 @@ static int rs_or_ar(const void* const* src, void* const* dst, int P, size_t n, i
     }
     if (kind == KIND_RS_BIDIR)   // P steps: P-1 that add, one that takes the complete halves
         return run_ring(src, dst, P, n, dtype, ws, ws_bytes, stream, 0, P, 0, 1);
-    return run_ring(src, dst, P, n, dtype, ws, ws_bytes, stream, 0, kind == KIND_AR ? 2 * (P - 1) : P - 1, 0);
+    if (scratch && !ws) return RING_EHIP;   // the static array's address was not available
+    return run_ring(src, dst, P, n, dtype, ws, ws_bytes, stream, 0,
+                    kind == KIND_AR ? 2 * (P - 1) : P - 1, 0, 0, nullptr, nullptr, 0, WsSpan{0, 0}, scratch);
 }
 
 int ring_reduce_scatter(const void* const* src, void* const* dst, int P, size_t n, int dtype,
@@ -526,6 +534,43 @@ extern "C" {
 int ring_all_gather(const void* const* src_or_null, void* const* dst, int P, size_t n, int dtype,
                     void* ws, size_t ws_bytes, void* stream) {
     return ring_all_gather_rec(src_or_null, dst, P, n, dtype, ws, ws_bytes, stream, WsSpan{0, 0});
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ no-alloc entry point
+// The static array behind ring_all_reduce_noalloc.  In host code `scratch`
+// names a host-side stand-in, not device memory: only the address
+// hipGetSymbolAddress returns for the current device may reach a kernel or
+// a fill.
+static __device__ __align__(256) unsigned char scratch[RING_NOALLOC_SCRATCH_BYTES];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; null if the lookup fails.
+static void* scratch_ptr() {
+    static std::atomic<void*> ptrs[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    void* p = ptrs[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        ptrs[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+extern "C" {
+
+int ring_all_reduce_noalloc(const void* const* src, void* const* dst, int P, size_t n, int dtype, void* stream) {
+    int rc = check_common(src, P, n, dtype, true);
+    if (rc) return rc;
+    if ((rc = check_common(dst, P, n, dtype, true))) return rc;
+    const size_t bytes = n * (size_t)elem_bytes(dtype);
+    if (overlap_kind(src, bytes, dst, bytes, P, true) < 0) return RING_EINVAL;
+    if (n == 0) return RING_OK;
+    // P = 1 is a copy and needs no scratch; rs_or_ar takes that path first
+    return rs_or_ar(src, dst, P, n, dtype, P > 1 ? scratch_ptr() : nullptr, RING_NOALLOC_SCRATCH_BYTES, stream,
+                    KIND_AR, true);
 }
 
 int ring_last_error(const void* ws, size_t ws_bytes, void* stream, int* info) {

@@ -212,3 +212,16 @@ def test_tuning_roundtrip_and_validation():
         t = N.Tuning(**old)
         assert N.lib().ring_set_tuning(ctypes.byref(t)) == N.RING_OK
 
+
+def test_noalloc_rejects_bad_arguments_before_the_device():
+    """ring_all_reduce_noalloc's argument checks run on the host: a null
+    pointer array, a bad rank count or dtype, n not divisible by P."""
+    L = N.lib()
+    fake = [0x10000 * (i + 1) for i in range(4)]
+    a, _ = N.ptr_array(fake)
+    b, _ = N.ptr_array([p + 0x100000 for p in fake])
+    assert L.ring_all_reduce_noalloc(None, b, 4, 4096, N.RING_F32, None) == N.RING_EINVAL
+    assert L.ring_all_reduce_noalloc(a, b, 0, 4096, N.RING_F32, None) == N.RING_EINVAL
+    assert L.ring_all_reduce_noalloc(a, b, 4, 4097, N.RING_F32, None) == N.RING_EINVAL
+    assert L.ring_all_reduce_noalloc(a, b, 4, 4096, 7, None) == N.RING_EUNSUPPORTED
+    assert L.ring_all_reduce_noalloc(a, b, 4, 0, N.RING_F32, None) == N.RING_OK
