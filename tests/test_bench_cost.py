@@ -11,6 +11,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -87,3 +89,22 @@ def test_kernel_name_follows_the_low_latency_limit():
     with_words = L.ring_workspace_bytes(N.OP_ALL_REDUCE, 4, 4 * (64 << 10), N.RING_F32)
     without = L.ring_workspace_bytes(N.OP_ALL_REDUCE, 4, 4 * ((64 << 10) + 4), N.RING_F32)
     assert with_words > without
+
+
+@pytest.mark.parametrize("P,n", [(8, 8 * 4096 * 3), (16, 16 * 2048), (3, 3 * 1000)])
+def test_multi_thread_oracle_leg_keeps_the_bits(P, n):
+    """The bench's multi-thread oracle leg runs the unchanged oracle on
+    sub-problems made of one slice of every chunk: chunk c of a sub-problem
+    holds only elements of chunk c, so the ring's order, and every bit, is
+    the single call's (fp32, bf16, int32; all-reduce and reduce-scatter)."""
+    import numpy as np
+    import oracle
+    from ring_collectives_amd import inputs
+    T = bench._slice_threads(n // P, 8)
+    assert (n // P) % T == 0 and T >= 1
+    x = inputs.normal_f32(P, n, seed=2)
+    xb = inputs.normal_bf16(P, n, seed=3)
+    xi = np.random.default_rng(1).integers(-1000, 1000, size=(P, n), dtype=np.int32)
+    for fn, a in ((oracle.all_reduce, x), (oracle.reduce_scatter, x), (oracle.all_reduce_bf16, xb),
+                  (oracle.all_reduce, xi)):
+        np.testing.assert_array_equal(bench._oracle_sliced(fn, a, P, T).view(np.uint8), fn(a).view(np.uint8))
