@@ -265,7 +265,12 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
     };
 
     const int KT = kl / G::BKB;                // steps
-    __syncthreads();   // the previous tile's epilogue may still be reading LDS
+    // The previous tile's epilogue may still be reading LDS: an LDS barrier.
+    // Not __syncthreads(), whose wait for every outstanding memory operation
+    // would first drain the previous tile's output stores; each path's first
+    // wait below counts its own loads, which return in issue order, so the
+    // stores drain while the first stage loads.
+    lds_barrier();
     if constexpr (G::NS == 2) {
         // Two buffers, in steps of BKB of K: A stage p serves steps R p .. R p
         // + R - 1.  At the start of step t (after the barrier, so every wave
