@@ -85,16 +85,36 @@ __device__ __forceinline__ void copy_rows(const unsigned short* src, unsigned sh
         st16<POL_DEV>(ld16<LOAD_POL>(s, (unsigned)(i * 16)), d, (unsigned)(i * 16));
 }
 
-// One wave waits for flag f; the workgroup follows it.  Returns false (for
-// every wave) if the launch is being abandoned: a wave that gives up has
-// recorded the timeout in the error word before the barrier.
-__device__ __forceinline__ bool wg_wait(const AgGemmParams& p, int* f, int wave, int lane, int q, int phase,
-                                        int pos) {
+// Wave 0 waits until flags f0, f0 + kFlagStride, ... (n of them) are all set,
+// one lane per flag, 64 at a time, so a panel's flags cost one round trip
+// to the coherence point rather than one each; the workgroup follows it
+// through an LDS-only barrier, which leaves this wave's earlier output stores
+// in flight (nothing in the launch reads them).  The other waves' loads of
+// the flagged rows are device-scope and issued after the barrier.  Returns
+// false (for every wave) if the launch is being abandoned: a wave that gives
+// up has recorded the timeout in the error word before the barrier.
+__device__ __forceinline__ bool wg_wait(const AgGemmParams& p, const int* f0, int n, int wave, int lane, int q,
+                                        int phase, int pos) {
     if (wave == 0) {
-        const int seen = peek_flag(f);
-        wait_flag(f, p.status, p.spin_limit, q, phase, pos, lane, seen, false);
+        for (int b = 0; b < n; b += 64) {
+            const bool mine = b + lane < n;
+            const int* f = f0 + (size_t)(mine ? b + lane : b) * kFlagStride;
+            const long long t0 = wall_clock64();
+            unsigned spins = 0;
+            while (__ballot(mine && __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < 1) != 0) {
+                __builtin_amdgcn_s_sleep(2);
+                if ((++spins & 31u) == 0) {
+                    if (__hip_atomic_load(&p.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+                    if (wall_clock64() - t0 > p.spin_limit) {
+                        if (lane == 0) report_timeout(p.status, q, phase, pos);
+                        break;
+                    }
+                }
+            }
+        }
+        asm volatile("" ::: "memory");
     }
-    __syncthreads();
+    lds_barrier();
     return __hip_atomic_load(&p.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
 }
 
@@ -114,8 +134,11 @@ __device__ __forceinline__ void wg_signal(const AgGemmParams& p, int* f, int tid
     }
 }
 
-template <class G>
+// The gelu output of the 256-wide tile is stored during the next tile's K
+// loop (DeferredGeluStore); the other widths store each tile as it finishes.
+template <class G, bool GELU>
 __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
+    constexpr bool kDefer = GELU && G::BN == 256;
     constexpr int BN = G::BN;
     const int tid = threadIdx.x;
     const int nthreads = 64 * G::NW;
@@ -139,6 +162,8 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
         copy_rows<POL_PLAIN>(p.As[q] + (size_t)r0 * p.K, p.Af[q] + ((size_t)q * Mc + r0) * p.K, r1 - r0, p.K,
                              tid, nthreads);
     }
+    DeferredGeluStore<G> dg;
+    if constexpr (kDefer) dg.init(lds, lane, wave);
     for (int f = 0; f < P; ++f) {
         const int c = (q - f + P) % P;
         // forward this workgroup's slices of phase g = f + 1 before the tiles
@@ -151,7 +176,7 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
                 int r0, r1;
                 slice_rows(p, pos, r0, r1);
                 unsigned short* dst = p.Af[q] + ((size_t)cg * Mc + r0) * p.K;
-                if (g >= 2 && !wg_wait(p, ag_flag(p, g - 1, left, pos), wave, lane, q, g, pos)) return;
+                if (g >= 2 && !wg_wait(p, ag_flag(p, g - 1, left, pos), 1, wave, lane, q, g, pos)) return;
                 if (g == 1)   // the left rank's own block, straight from its input
                     copy_rows<POL_PLAIN>(p.As[left] + (size_t)r0 * p.K, dst, r1 - r0, p.K, tid, nthreads);
                 else
@@ -165,28 +190,43 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
             const int pr = pos / p.tn, tc = pos % p.tn;
             f32x16 acc[kMI][G::NI];
             if (f == 0) {
-                gemm_tile<G, POL_PLAIN>(p.K, p.N, p.As[q], p.B[q], pr, tc, acc, lds, lane, wave, wr, wc);
+                if constexpr (kDefer)
+                    gemm_tile_h<G, POL_PLAIN, true>(p.K, p.N, p.As[q], p.B[q], pr, tc, acc, lds, lane, wave, wr,
+                                                    wc, dg);
+                else
+                    gemm_tile<G, POL_PLAIN>(p.K, p.N, p.As[q], p.B[q], pr, tc, acc, lds, lane, wave, wr, wc);
             } else {
-                for (int t = 0; t < p.tn; ++t)
-                    if (!wg_wait(p, ag_flag(p, f, q, pr * p.tn + t), wave, lane, q, f, pos)) return;
-                gemm_tile<G, POL_DEV>(p.K, p.N, p.Af[q], p.B[q], c * p.tm_chunk + pr, tc, acc, lds, lane,
-                                      wave, wr, wc);
+                // the panel's tn slices, flagged at consecutive positions
+                if (!wg_wait(p, ag_flag(p, f, q, pr * p.tn), p.tn, wave, lane, q, f, pos)) return;
+                if constexpr (kDefer)
+                    gemm_tile_h<G, POL_DEV, true>(p.K, p.N, p.Af[q], p.B[q], c * p.tm_chunk + pr, tc, acc, lds,
+                                                  lane, wave, wr, wc, dg);
+                else
+                    gemm_tile<G, POL_DEV>(p.K, p.N, p.Af[q], p.B[q], c * p.tm_chunk + pr, tc, acc, lds, lane,
+                                          wave, wr, wc);
             }
             const size_t at = ((size_t)c * Mc + pr * kBM + wr * kWM) * p.N + tc * BN + wc * G::WN;
-            if (p.gelu_bf16)
+            if constexpr (kDefer) {
+                dg.flush();   // what the K loop had no steps left for
+                dg.fill(acc, (char*)p.C[q] + at * 2, p.N, lane);
+            } else if constexpr (GELU) {
                 store_part_rowmajor<G, false, EPI_GELU_BF16>(acc, tile_view(nullptr, 0), (char*)p.C[q] + at * 2,
                                                              p.N, lds, lane, wave);
-            else
+            } else {
                 store_part_rowmajor<G, false, EPI_F32>(acc, tile_view(nullptr, 0), (char*)p.C[q] + at * 4, p.N,
                                                        lds, lane, wave);
+            }
         }
     }
+    if constexpr (kDefer) dg.flush();
 }
 
-template <class G>
+template <class G, bool GELU>
 __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void ag_gemm_kernel(AgGemmParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned short lds[G::kLds / 2];
-    ag_gemm_body<G>(p, lds);
+    // the deferred gelu store's slices follow the K loop's stages
+    constexpr int kExtra = GELU && G::BN == 256 ? DeferredGeluStore<G>::kLds : 0;
+    __shared__ __attribute__((aligned(16))) unsigned short lds[(G::kLds + kExtra) / 2];
+    ag_gemm_body<G, GELU>(p, lds);
     // The last workgroup to finish clears the slice flags for the next call
     // (every reader is done by then; an abandoned launch gets here too).
     // Wave 0 counts the workgroup out and, if it was the last, clears.
@@ -229,21 +269,21 @@ size_t ag_gemm_workspace_bytes(int P, size_t n) {
     return ag_ws_layout(P, n).total;
 }
 
-template <class G>
+template <class G, bool GELU>
 static int launch_ag_gemm(AgGemmParams& prm, const DevInfo& di, hipStream_t stream) {
     prm.tn = prm.N / G::BN;
     prm.tpc = prm.tm_chunk * prm.tn;
     // every workgroup must be resident (the panel's workgroups wait for each
     // other's slices)
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ag_gemm_kernel<G>, 64 * G::NW, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ag_gemm_kernel<G, GELU>, 64 * G::NW, 0) != hipSuccess ||
         occ < G::kWGsPerCU)
         return RING_EHIP;
     long long groups = (long long)di.cus * G::kWGsPerCU / prm.P;
     if (groups > prm.tpc) groups = prm.tpc;
     if (groups < 1) return RING_EUNSUPPORTED;
     prm.groups = (int)groups;
-    hipLaunchKernelGGL(ag_gemm_kernel<G>, dim3((unsigned)(groups * prm.P)), dim3(64 * G::NW), 0, stream, prm);
+    ag_gemm_kernel<G, GELU><<<dim3((unsigned)(groups * prm.P)), dim3(64 * G::NW), 0, stream>>>(prm);
     return hipGetLastError() == hipSuccess ? RING_OK : RING_EHIP;
 }
 
@@ -307,7 +347,9 @@ int ag_gemm_run(const void* const* A_shard, const void* const* B, void* const* A
     if (bn == 256 && N % 256) return RING_EUNSUPPORTED;
     prm.gelu_bf16 = gelu_bf16 ? 1 : 0;
     const hipStream_t st = (hipStream_t)stream;
-    return bn == 256 ? launch_ag_gemm<Geo<256, 8>>(prm, di, st) : launch_ag_gemm<Geo<128, 4>>(prm, di, st);
+    if (prm.gelu_bf16)
+        return bn == 256 ? launch_ag_gemm<Geo<256, 8>, true>(prm, di, st) : launch_ag_gemm<Geo<128, 4>, true>(prm, di, st);
+    return bn == 256 ? launch_ag_gemm<Geo<256, 8>, false>(prm, di, st) : launch_ag_gemm<Geo<128, 4>, false>(prm, di, st);
 }
 
 }  // namespace ringc

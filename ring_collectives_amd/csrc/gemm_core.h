@@ -115,7 +115,10 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait until at most `n` of this wave's vector memory operations are in flight.
+// Wait until at most `n` of this wave's vector memory operations are in
+// flight (n rounded down to a count listed here).  The counter retires loads
+// and stores together, in issue order, so this waits for every operation but
+// the n issued last.
 __device__ __forceinline__ void wait_vm(int n) {
     if (n >= 20) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
     else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -124,8 +127,23 @@ __device__ __forceinline__ void wait_vm(int n) {
     else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else if (n >= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if (n >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if (n >= 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
+
+// Work a caller slips into the K loop of a tile.  At step t, right after the
+// step's stage loads, issue(t) runs if issues(t) (wave-uniform) and then
+// issues exactly kOps vector memory operations; the next step's wait lets
+// those stay in flight, since they come after the loads it waits for.
+// begin() and end(steps) bracket the loop.
+struct NoHook {
+    static constexpr int kOps = 0;
+    __device__ __forceinline__ void begin() {}
+    __device__ __forceinline__ bool issues(int) const { return false; }
+    __device__ __forceinline__ void issue(int) {}
+    __device__ __forceinline__ void end(int) {}
+};
 
 // C tile (tr, tc) of A B into acc (the wave's part): rows 256 tr .. of A
 // (M x K row-major), columns BN tc .. of B (K x N row-major), over the K
@@ -140,11 +158,20 @@ __device__ __forceinline__ void wait_vm(int n) {
 // each group of 16 lanes, when lane j points at row kb + j / 4, columns
 // cb + 4 (j % 4) .. +3, lane i receives rows kb .. kb+3 of column cb + i, so
 // two such reads give a lane its 8 consecutive k of one column.
-template <class G, int APOL = POL_PLAIN>
-__device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __restrict__ A,
-                                          const unsigned short* __restrict__ B, int tr, int tc,
-                                          f32x16 (&acc)[kMI][G::NI], unsigned short* lds,
-                                          int lane, int wave, int wr, int wc, int kbeg = 0, int kl = -1) {
+//
+// With SWAP the MFMAs take the B fragment as their first operand and so
+// compute the transposed block: lane l then holds row m = l % 32 of each
+// block, at columns 8 (v / 4) + 4 (l / 32) + v % 4 for accumulator v, that is
+// runs of 4 consecutive columns of one row.  (The same products, summed the
+// same way.)  Without it lane l holds column l % 32, rows 8 (v / 4) + 4 (l /
+// 32) + v % 4.
+template <class G, int APOL, bool SWAP, class Hook>
+__device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* __restrict__ A,
+                                            const unsigned short* __restrict__ B, int tr, int tc,
+                                            f32x16 (&acc)[kMI][G::NI], unsigned short* lds,
+                                            int lane, int wave, int wr, int wc, Hook& hook,
+                                            int kbeg = 0, int kl = -1) {
+    static_assert(Hook::kOps == 0 || (G::NS == 2 && G::R == 1), "K-loop work needs one stage per step");
     constexpr int BN = G::BN;
     if (kl < 0) kl = K;
 #pragma unroll
@@ -251,8 +278,10 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
             for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < G::NI; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        af[kk & 1][mi], bf[kk & 1][ni], acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                             bf[kk & 1][ni], af[kk & 1][mi], acc[mi][ni], 0, 0, 0)
+                                       : __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                             af[kk & 1][mi], bf[kk & 1][ni], acc[mi][ni], 0, 0, 0);
             if (kk + 1 < G::KK) {
 #pragma unroll
                 for (int g = 0; g < kMI * G::NI; ++g) {
@@ -281,22 +310,34 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
         // the A loads of the stage after in flight (R = 2, odd steps).  Past
         // the end of K the issues re-read the last stage into the free buffer
         // (never read again).
+        // The hook's operations of step t go after the loads of stage t +
+        // 1, so the wait at step t + 1 leaves exactly those in flight.
         const int KA = kl / G::BKA;            // A stages
+        hook.begin();
         issue_b(0, 0);
         issue_a(0, 0);
         for (int p = 0; p < KA; ++p) {
 #pragma unroll
             for (int r = 0; r < G::R; ++r) {
                 const int t = p * G::R + r;
-                if (r == 0) wait_vm(0);            // B stage t and A stage p have landed
-                else wait_vm(G::kLoadsA);          // B stage t has; A stage p + 1 may be in flight
+                if (r == 0) {                      // B stage t and A stage p have landed
+                    if (Hook::kOps > 0 && t > 0 && hook.issues(t - 1)) wait_vm(Hook::kOps);
+                    else wait_vm(0);
+                } else {
+                    wait_vm(G::kLoadsA);           // B stage t has; A stage p + 1 may be in flight
+                }
                 lds_barrier();                     // everyone's has; buffers of step t - 1 are free
                 issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
                 if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
+                if (Hook::kOps > 0 && hook.issues(t)) {
+                    __builtin_amdgcn_sched_barrier(0);   // not ahead of the stage loads
+                    hook.issue(t);
+                }
                 step((unsigned)((p & 1) * G::kStageA), r * G::KK,
                      (unsigned)(G::kBBase + (t & 1) * G::kStageB));
             }
         }
+        hook.end(KT);
     } else {
         // NS buffers, A and B staged together (R = 1): stages 0 .. NS - 2 are
         // issued up front; at the start of step t (after the barrier, so every
@@ -333,6 +374,15 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
     __syncthreads();   // all waves are done with the stages before the epilogue uses LDS
 }
 
+template <class G, int APOL = POL_PLAIN>
+__device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __restrict__ A,
+                                          const unsigned short* __restrict__ B, int tr, int tc,
+                                          f32x16 (&acc)[kMI][G::NI], unsigned short* lds,
+                                          int lane, int wave, int wr, int wc, int kbeg = 0, int kl = -1) {
+    NoHook none;
+    gemm_tile_h<G, APOL, false>(K, N, A, B, tr, tc, acc, lds, lane, wave, wr, wc, none, kbeg, kl);
+}
+
 
 // GELU in its tanh form, 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))),
 // the default of jax.nn.gelu, which the tensor-parallel MLP of "TPU 与分布式
@@ -367,23 +417,140 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
 // product to bf16 before the activation and the activation to bf16 after.
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_GELU_BF16 = 2 };
 
+// Four bf16 (two dwords) -> bf16(gelu) of each.
+__device__ __forceinline__ u32x2 gelu_bf16x4(const u32x2 b) {
+    u32x2 h;
+    h[0] = pack_bf16x2(gelu_tanh(__uint_as_float(b[0] << 16)), gelu_tanh(__uint_as_float(b[0] & 0xFFFF0000u)));
+    h[1] = pack_bf16x2(gelu_tanh(__uint_as_float(b[1] << 16)), gelu_tanh(__uint_as_float(b[1] & 0xFFFF0000u)));
+    return h;
+}
+
 // Four fp32 values (bits) -> four bf16 in two dwords, with the epilogue EPI.
 template <int EPI>
 __device__ __forceinline__ u32x2 epi_bf16x4(const u32x4 o) {
-    float f0 = __uint_as_float(o[0]), f1 = __uint_as_float(o[1]);
-    float f2 = __uint_as_float(o[2]), f3 = __uint_as_float(o[3]);
-    if constexpr (EPI == EPI_GELU_BF16) {
-        const unsigned p01 = pack_bf16x2(f0, f1), p23 = pack_bf16x2(f2, f3);
-        f0 = gelu_tanh(__uint_as_float(p01 << 16));
-        f1 = gelu_tanh(__uint_as_float(p01 & 0xFFFF0000u));
-        f2 = gelu_tanh(__uint_as_float(p23 << 16));
-        f3 = gelu_tanh(__uint_as_float(p23 & 0xFFFF0000u));
-    }
-    u32x2 h;
-    h[0] = pack_bf16x2(f0, f1);
-    h[1] = pack_bf16x2(f2, f3);
-    return h;
+    u32x2 b;
+    b[0] = pack_bf16x2(__uint_as_float(o[0]), __uint_as_float(o[1]));
+    b[1] = pack_bf16x2(__uint_as_float(o[2]), __uint_as_float(o[3]));
+    if constexpr (EPI == EPI_GELU_BF16) b = gelu_bf16x4(b);
+    return b;
 }
+
+// The MLP's first-layer output of a finished 256-wide tile (computed with
+// SWAP, so lane l holds runs of 4 columns of row l % 32 of each 32 x 32
+// block), stored row-major as bf16(gelu(bf16(product))).  The wave's part is
+// 4 rows of blocks, 32 rows x 64 columns (128 bytes a row) each.  A row of
+// blocks goes out through the wave's own 4 KiB slice of LDS (kSlice bytes
+// past the K loop's stages): 8 writes of 8 bytes a lane, then reads of 16
+// bytes a lane, 8 lanes a row, so each store writes 8 whole 128-byte rows.
+// fill() stores the first kMI - D - 1 rows of blocks at once, leaves the
+// next one staged in the slice and keeps the last D as bf16(product) in
+// registers.  The staged row and then the held ones go out during the next
+// tile's K loop, one store a step (a held row is staged with its first
+// store), so most of every tile's output trickles out behind the next
+// tile's operand loads instead of all workgroups storing it together
+// between tiles while the matrix cores wait (the K loop's registers leave
+// room for D = 2).  Nothing in the launch reads the stored values.  fill()
+// takes a tile once the previous one is flushed; flush() stores what the K
+// loop has not.
+//   Slice layout: row r at r 128 bytes, its 16-byte chunk j (columns 8 j ..)
+//   at chunk j ^ (r & 7), so neither the writes (32 rows, one chunk) nor the
+//   reads (8 rows, all chunks) pile onto a few banks.
+template <class G, int D = 2>
+struct DeferredGeluStore {
+    static_assert(G::WN == 64, "rows of 128 bytes");
+    static constexpr int kSlice = 4096;               // bytes of LDS per wave
+    static constexpr int kLds = G::NW * kSlice;       // LDS the kernel adds past its stages
+    static constexpr int kM0 = kMI - D - 1;           // the row of blocks left staged
+    static constexpr int kPend = D * G::NI * 4;       // register pairs held: (mi, ni, 4-column group)
+    static constexpr int kOps = 1;                    // stores per K step
+    static constexpr int kChunks = (D + 1) * 4;       // a chunk: 8 rows
+    u32x2 pend[kPend];
+    rsrc_t ov;           // the wave's part of the output tile
+    unsigned out_lane;   // byte offset of the lane's 16 bytes in row 0 of it
+    unsigned row8;       // bytes of 8 output rows
+    unsigned wr_base;    // the lane's write address in the slice (before the chunk XOR)
+    unsigned rd_base;    // its read address for rows 0 .. 7
+    unsigned short* lds_;
+    int first, next;     // chunk stored at step 0 of the current K loop; next chunk due
+
+    __device__ __forceinline__ void init(unsigned short* lds, int lane, int wave) {
+        const unsigned slice = (unsigned)(G::kLds + wave * kSlice);
+        // write: row lane % 32, 8-byte half lane / 32 of a chunk
+        wr_base = slice + (unsigned)((lane & 31) * 128 + 8 * (lane >> 5) + 16 * (lane & 7));
+        // read: row lane / 8 (+ 8 i), logical chunk lane % 8
+        rd_base = slice + (unsigned)((lane >> 3) * 128 + 16 * ((lane & 7) ^ (lane >> 3)));
+        first = next = kChunks;
+        lds_ = lds;
+    }
+    __device__ __forceinline__ void begin() { first = next; }
+    __device__ __forceinline__ bool issues(int t) const { return first + t < kChunks; }
+    __device__ __forceinline__ void end(int steps) { next = first + steps < kChunks ? first + steps : kChunks; }
+
+    // One row of blocks (bf16(product), in (ni, group) order) into the slice,
+    // through gelu.
+    __device__ __forceinline__ void stage(unsigned short* lds, u32x2 (&b)[G::NI * 4]) {
+#pragma unroll
+        for (int k = 0; k < G::NI * 4; ++k) {   // k = 4 ni + group = logical chunk
+            const u32x2 h = gelu_bf16x4(b[k]);
+            *(u32x2*)((char*)lds + (wr_base ^ (unsigned)(16 * k))) = h;
+        }
+    }
+    // Rows 8 i .. 8 i + 7 of row of blocks mi, from the slice to memory.
+    __device__ __forceinline__ void emit(unsigned short* lds, int mi, int i) {
+        const u32x4 v = *(const u32x4*)((const char*)lds + rd_base + (unsigned)(i * 1024));
+        st16<POL_NT>(v, ov, out_lane + (unsigned)(4 * mi + i) * row8);
+    }
+    // Chunk c (wave-uniform): rows 8 (c % 4) .. of row of blocks kM0 + c / 4.
+    // Row kM0 is staged already; a later one is pend[0 ..] when c % 4 == 0,
+    // staged then, and the remaining registers move up.
+    __device__ __forceinline__ void chunk(unsigned short* lds, int c) {
+        if (c >= 4 && (c & 3) == 0) {
+            u32x2 b[G::NI * 4];
+#pragma unroll
+            for (int k = 0; k < G::NI * 4; ++k) b[k] = pend[k];
+            stage(lds, b);
+#pragma unroll
+            for (int k = 0; k + G::NI * 4 < kPend; ++k) pend[k] = pend[k + G::NI * 4];
+        }
+        emit(lds, kM0 + (c >> 2), c & 3);
+    }
+    __device__ __forceinline__ void issue(int t) { chunk(lds_, first + t); }
+    __device__ __forceinline__ void flush() {
+        for (int c = next; c < kChunks; ++c) chunk(lds_, c);
+        next = kChunks;
+    }
+    // The wave's part of a finished tile: element (0, 0) of the part at
+    // `part` (bf16, row stride ld elements).
+    __device__ __forceinline__ void fill(const f32x16 (&acc)[kMI][G::NI], void* part, int ld, int lane) {
+        ov = tile_view(part, ((long long)(kWM - 1) * ld + G::WN) * 2);
+        unsigned lo = (unsigned)(((lane >> 3) * ld + 8 * (lane & 7)) * 2);
+        asm volatile("" : "+v"(lo));
+        out_lane = lo;
+        row8 = (unsigned)(8 * ld * 2);
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi) {
+            u32x2 b[G::NI * 4];
+#pragma unroll
+            for (int ni = 0; ni < G::NI; ++ni)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    b[ni * 4 + g][0] = pack_bf16x2(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1]);
+                    b[ni * 4 + g][1] = pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+                }
+            if (mi <= kM0) {
+                stage(lds_, b);
+                if (mi < kM0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) emit(lds_, mi, i);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < G::NI * 4; ++k) pend[(mi - kM0 - 1) * G::NI * 4 + k] = b[k];
+            }
+        }
+        next = 0;
+    }
+};
 
 // Store a wave's part of a finished tile row-major: element (i, j) of the
 // part goes to ob[i * ld + j], fp32 for EPI_F32 and bf16 otherwise.  With
