@@ -267,9 +267,12 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
     // for the reads it consumes.  The scheduling fences and groups hold that
     // order; left alone, the compiler pairs each read with its use through
     // one register set and exposes the LDS latency once per block.
-    auto step = [&](unsigned abase, int ka0, unsigned bbase) {
+    auto step = [&](unsigned abase, int ka0, unsigned bbase, const bf16x8 (&af0)[kMI], const bf16x8 (&bf0)[G::NI]) {
         bf16x8 af[2][kMI], bf[2][G::NI];
-        read_frags(abase, ka0, bbase, 0, af[0], bf[0]);
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi) af[0][mi] = af0[mi];
+#pragma unroll
+        for (int ni = 0; ni < G::NI; ++ni) bf[0][ni] = bf0[ni];
 #pragma unroll
         for (int kk = 0; kk < G::KK; ++kk) {
             if (kk + 1 < G::KK)
@@ -327,14 +330,21 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
                     wait_vm(G::kLoadsA);           // B stage t has; A stage p + 1 may be in flight
                 }
                 lds_barrier();                     // everyone's has; buffers of step t - 1 are free
+                // the first k-step's fragments are read before the loads are
+                // issued, so their latency hides behind the issue
+                bf16x8 af0[kMI], bf0[G::NI];
+                read_frags((unsigned)((p & 1) * G::kStageA), r * G::KK, (unsigned)(G::kBBase + (t & 1) * G::kStageB),
+                           0, af0, bf0);
+                __builtin_amdgcn_sched_barrier(0);
                 issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
                 if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
                 if (Hook::kOps > 0 && hook.issues(t)) {
                     __builtin_amdgcn_sched_barrier(0);   // not ahead of the stage loads
                     hook.issue(t);
                 }
+                __builtin_amdgcn_sched_barrier(0);
                 step((unsigned)((p & 1) * G::kStageA), r * G::KK,
-                     (unsigned)(G::kBBase + (t & 1) * G::kStageB));
+                     (unsigned)(G::kBBase + (t & 1) * G::kStageB), af0, bf0);
             }
         }
         hook.end(KT);
@@ -366,7 +376,9 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
                 issue_b(nx, ns);
                 issue_a(nx, ns);
             }
-            step((unsigned)(slot * G::kStageA), 0, (unsigned)(G::kBBase + slot * G::kStageB));
+            bf16x8 af0[kMI], bf0[G::NI];
+            read_frags((unsigned)(slot * G::kStageA), 0, (unsigned)(G::kBBase + slot * G::kStageB), 0, af0, bf0);
+            step((unsigned)(slot * G::kStageA), 0, (unsigned)(G::kBBase + slot * G::kStageB), af0, bf0);
             slot = slot + 1 == G::NS ? 0 : slot + 1;
         }
     }
