@@ -73,15 +73,25 @@ __device__ __forceinline__ void slice_rows(const AgGemmParams& p, int pos, int& 
     r1 = pr * kBM + ((t + 1) * kBM) / p.tn;
 }
 
-// Copy rows [r0, r1) of a chunk (K bf16 each) with the whole workgroup.
-template <int LOAD_POL>
+// Copy rows [r0, r1) of a chunk (K bf16 each) with the whole workgroup, U
+// 16-byte loads in flight per thread before their stores (one at a time,
+// each copy waited out a whole device-scope round trip).
+template <int LOAD_POL, int U>
 __device__ __forceinline__ void copy_rows(const unsigned short* src, unsigned short* dst, int rows, int K,
                                           int tid, int nthreads) {
     const long long bytes = (long long)rows * K * 2;
     const rsrc_t s = tile_view(src, bytes);
     const rsrc_t d = tile_view(dst, bytes);
     const long long nvec = bytes / 16;
-    for (long long i = tid; i < nvec; i += nthreads)
+    long long i = tid;
+    for (; i + (long long)(U - 1) * nthreads < nvec; i += (long long)U * nthreads) {
+        u32x4 v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) v[j] = ld16<LOAD_POL>(s, (unsigned)((i + (long long)j * nthreads) * 16));
+#pragma unroll
+        for (int j = 0; j < U; ++j) st16<POL_DEV>(v[j], d, (unsigned)((i + (long long)j * nthreads) * 16));
+    }
+    for (; i < nvec; i += nthreads)
         st16<POL_DEV>(ld16<LOAD_POL>(s, (unsigned)(i * 16)), d, (unsigned)(i * 16));
 }
 
@@ -139,6 +149,7 @@ __device__ __forceinline__ void wg_signal(const AgGemmParams& p, int* f, int tid
 template <class G, bool GELU>
 __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
     constexpr bool kDefer = GELU && G::BN == 256;
+    constexpr int kCopyU = kDefer ? 4 : 8;   // copies in flight; the deferred store holds registers
     constexpr int BN = G::BN;
     const int tid = threadIdx.x;
     const int nthreads = 64 * G::NW;
@@ -159,7 +170,7 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
     for (int pos = grp; pos < p.tpc; pos += p.groups) {
         int r0, r1;
         slice_rows(p, pos, r0, r1);
-        copy_rows<POL_PLAIN>(p.As[q] + (size_t)r0 * p.K, p.Af[q] + ((size_t)q * Mc + r0) * p.K, r1 - r0, p.K,
+        copy_rows<POL_PLAIN, kCopyU>(p.As[q] + (size_t)r0 * p.K, p.Af[q] + ((size_t)q * Mc + r0) * p.K, r1 - r0, p.K,
                              tid, nthreads);
     }
     DeferredGeluStore<G> dg;
@@ -178,9 +189,9 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
                 unsigned short* dst = p.Af[q] + ((size_t)cg * Mc + r0) * p.K;
                 if (g >= 2 && !wg_wait(p, ag_flag(p, g - 1, left, pos), 1, wave, lane, q, g, pos)) return;
                 if (g == 1)   // the left rank's own block, straight from its input
-                    copy_rows<POL_PLAIN>(p.As[left] + (size_t)r0 * p.K, dst, r1 - r0, p.K, tid, nthreads);
+                    copy_rows<POL_PLAIN, kCopyU>(p.As[left] + (size_t)r0 * p.K, dst, r1 - r0, p.K, tid, nthreads);
                 else
-                    copy_rows<POL_DEV>(p.Af[left] + ((size_t)cg * Mc + r0) * p.K, dst, r1 - r0, p.K, tid,
+                    copy_rows<POL_DEV, kCopyU>(p.Af[left] + ((size_t)cg * Mc + r0) * p.K, dst, r1 - r0, p.K, tid,
                                        nthreads);
                 if (!(q == 0 && p.drop_round > 0 && g == p.drop_round)) wg_signal(p, ag_flag(p, g, q, pos), tid, q, g, pos);
             }

@@ -330,21 +330,32 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
                     wait_vm(G::kLoadsA);           // B stage t has; A stage p + 1 may be in flight
                 }
                 lds_barrier();                     // everyone's has; buffers of step t - 1 are free
-                // the first k-step's fragments are read before the loads are
-                // issued, so their latency hides behind the issue
-                bf16x8 af0[kMI], bf0[G::NI];
-                read_frags((unsigned)((p & 1) * G::kStageA), r * G::KK, (unsigned)(G::kBBase + (t & 1) * G::kStageB),
-                           0, af0, bf0);
-                __builtin_amdgcn_sched_barrier(0);
-                issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
-                if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
-                if (Hook::kOps > 0 && hook.issues(t)) {
-                    __builtin_amdgcn_sched_barrier(0);   // not ahead of the stage loads
-                    hook.issue(t);
+                // The first k-step's fragments are read before the loads
+                // are issued, so their latency hides behind the issue --
+                // except where a hook works between the loads and the
+                // MFMAs (its registers and the fragments' do not fit
+                // together).
+                const unsigned abuf = (unsigned)((p & 1) * G::kStageA);
+                const unsigned bbuf = (unsigned)(G::kBBase + (t & 1) * G::kStageB);
+                if constexpr (Hook::kOps == 0) {
+                    bf16x8 af0[kMI], bf0[G::NI];
+                    read_frags(abuf, r * G::KK, bbuf, 0, af0, bf0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
+                    if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    step(abuf, r * G::KK, bbuf, af0, bf0);
+                } else {
+                    issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
+                    if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
+                    if (hook.issues(t)) {
+                        __builtin_amdgcn_sched_barrier(0);   // not ahead of the stage loads
+                        hook.issue(t);
+                    }
+                    bf16x8 af0[kMI], bf0[G::NI];
+                    read_frags(abuf, r * G::KK, bbuf, 0, af0, bf0);
+                    step(abuf, r * G::KK, bbuf, af0, bf0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                step((unsigned)((p & 1) * G::kStageA), r * G::KK,
-                     (unsigned)(G::kBBase + (t & 1) * G::kStageB), af0, bf0);
             }
         }
         hook.end(KT);
