@@ -12,28 +12,24 @@
 //
 // Schedule.  Phase f = 0 .. P-1 handles chunk c = (q - f) mod P, the order in
 // which the ring delivers the blocks (round t of the ring all-gather brings
-// chunk (q - t - 1) mod P from the left neighbour), local block first:
-//   forwarding of phase f >= 1: rank q copies chunk c from its left
-//     neighbour (from A_shard[left] at f = 1, the left rank's own block; from
-//     A_full[left] after) into A_full[q], slice by slice, each slice once the
-//     left neighbour has flagged it, and flags it in turn.  A workgroup
-//     forwards its slices of phase f + 1 just before its tiles of phase f,
-//     so forwarding runs a phase ahead of the tiles that need it.  The local
-//     block is placed first.
-//   GEMM: the tiles of chunk c, each once every slice of its row panel is
-//     flagged (phase 0 reads the local block straight from A_shard[q]).
-// A slice is the part of a 256-row panel that one tile position forwards:
-// rows 256 t / tn .. 256 (t + 1) / tn of the panel for column tile t, all K
-// columns, so the tn workgroups of a panel forward it together.
+// chunk (q - t - 1) mod P from the left neighbour), local block first.  The
+// tiles of chunk c read its rows from where they already are: phase 0 from
+// A_shard[q], phase 1 from A_shard[left] (the left rank's own block), phase
+// f >= 2 from A_full[left], which the left rank's phase f - 1 tiles wrote.
+// Forwarding rides on those reads: the tile at column position tc of a
+// 256-row panel copies the K range [tc K / tn, (tc + 1) K / tn) of the
+// panel's rows (tn column tiles) from the LDS stages its K loop brings in
+// anyway into A_full[q], and flags that when its K loop is done, so the tn
+// tiles of a panel forward the whole panel once, with no loads of their own.
+// A tile of phase f >= 2 starts once the left rank's tn phase f - 1 tiles of
+// its panel have flagged.
 //
-// Progress.  In its iteration f a workgroup forwards phase f + 1, which waits
-// only for the left rank's forwarding of phase f (its iteration f - 1), and
-// computes tiles of phase f, which wait only for slices forwarded in
-// iteration f - 1; so by induction on f every workgroup finishes every
-// iteration, provided all workgroups are resident (the grid is sized so).
-// The slice flags have several readers (the panel's GEMM tiles and the right
-// neighbour), so readers leave them set and the last workgroup to finish
-// clears the table for the next call.
+// Progress.  A phase-f tile waits only for phase f - 1 tiles of the left
+// rank, and every workgroup finishes its tiles of phase f - 1 before it
+// starts phase f; so by induction on f every tile finishes, provided all
+// workgroups are resident (the grid is sized so).  A flag has the tn tiles
+// of the right rank's panel for readers, so readers leave it set and the last
+// workgroup to finish clears the table for the next call.
 #include "gemm_core.h"
 
 #include <hip/hip_runtime.h>
@@ -66,34 +62,72 @@ __device__ __forceinline__ int* ag_flag(const AgGemmParams& p, int f, int q, int
     return p.flags + (((size_t)f * p.P + q) * p.tpc + pos) * kFlagStride;
 }
 
-// Rows [r0, r1) of chunk c's panel slice for tile position pos.
-__device__ __forceinline__ void slice_rows(const AgGemmParams& p, int pos, int& r0, int& r1) {
-    const int pr = pos / p.tn, t = pos % p.tn;
-    r0 = pr * kBM + (t * kBM) / p.tn;
-    r1 = pr * kBM + ((t + 1) * kBM) / p.tn;
+// K range [k0, k1) of the panel that column tile tc forwards (multiples of
+// 8 elements, so whole 16-byte pieces; the tn ranges tile [0, K)).
+__device__ __forceinline__ void forward_range(const AgGemmParams& p, int tc, int& k0, int& k1) {
+    const int k8 = p.K / 8;
+    k0 = (int)(((long long)tc * k8) / p.tn) * 8;
+    k1 = (int)(((long long)(tc + 1) * k8) / p.tn) * 8;
 }
 
-// Copy rows [r0, r1) of a chunk (K bf16 each) with the whole workgroup, U
-// 16-byte loads in flight per thread before their stores (one at a time,
-// each copy waited out a whole device-scope round trip).
-template <int LOAD_POL, int U>
-__device__ __forceinline__ void copy_rows(const unsigned short* src, unsigned short* dst, int rows, int K,
-                                          int tid, int nthreads) {
-    const long long bytes = (long long)rows * K * 2;
-    const rsrc_t s = tile_view(src, bytes);
-    const rsrc_t d = tile_view(dst, bytes);
-    const long long nvec = bytes / 16;
-    long long i = tid;
-    for (; i + (long long)(U - 1) * nthreads < nvec; i += (long long)U * nthreads) {
-        u32x4 v[U];
-#pragma unroll
-        for (int j = 0; j < U; ++j) v[j] = ld16<LOAD_POL>(s, (unsigned)((i + (long long)j * nthreads) * 16));
-#pragma unroll
-        for (int j = 0; j < U; ++j) st16<POL_DEV>(v[j], d, (unsigned)((i + (long long)j * nthreads) * 16));
+// The K-loop hook that forwards: at the first step of each A stage that
+// overlaps [k0, k1), the wave copies its kRows rows of the stage (64 columns,
+// 128 bytes a row, read back from the swizzled LDS buffer) into the panel's
+// rows of A_full[q], 8 rows per 16-byte-per-lane store; columns outside the
+// range get an offset past the end of the view, which drops them.
+template <class G>
+struct ForwardHook {
+    static constexpr bool kActive = true;
+    static constexpr int kRows = kBM / G::NW;     // rows of a stage this wave copies
+    static constexpr int kStores = kRows / 8;     // 16-byte stores per lane and stage
+    const unsigned short* lds;
+    rsrc_t dv;            // the panel's rows of A_full[q], all K columns
+    unsigned dst_lane;    // byte offset of the lane's piece, row 0 of its rows, column 0
+    unsigned row8;        // bytes of 8 rows
+    unsigned lds_row;     // LDS byte offset of the lane's row within an A buffer
+    int chunk;            // the lane's 16-byte piece of a row (columns 8 chunk ..)
+    int swz0;             // (row >> 1) & 7 of the lane's first row
+    int k0, k1;
+    __device__ __forceinline__ void begin() {}
+    __device__ __forceinline__ void end(int) {}
+    __device__ __forceinline__ int ops(int t) const {
+        if (t % G::R) return 0;
+        const int kb = (t / G::R) * G::BKA;
+        return kb < k1 && kb + G::BKA > k0 ? kStores : 0;
     }
-    for (; i < nvec; i += nthreads)
-        st16<POL_DEV>(ld16<LOAD_POL>(s, (unsigned)(i * 16)), d, (unsigned)(i * 16));
-}
+    __device__ __forceinline__ void issue(int t) {
+        const int st = t / G::R;
+        const int kb = st * G::BKA;
+        const int k = kb + 8 * chunk;
+        const bool in = k >= k0 && k < k1;
+        const unsigned abuf = (unsigned)((st & 1) * G::kStageA);
+#pragma unroll
+        for (int i = 0; i < kStores; ++i) {
+            // row kRows wave + 8 i + lane / 8: its swizzle is swz0 + 4 i (mod 8)
+            const int sw = (swz0 + 4 * i) & 7;
+            const u32x4 v = *(const u32x4*)((const char*)lds + abuf + lds_row + (unsigned)(i * 8 * G::kARowBytes) +
+                                            (unsigned)((chunk ^ sw) * 16));
+            const unsigned off = in ? dst_lane + (unsigned)i * row8 + (unsigned)(kb * 2) : 0x80000000u;
+            st16<POL_DEV>(v, dv, off);
+        }
+    }
+    __device__ __forceinline__ void init(const unsigned short* l, int lane, int wave) {
+        lds = l;
+        const int row = kRows * wave + lane / 8;
+        lds_row = (unsigned)(row * G::kARowBytes);
+        chunk = lane & 7;
+        swz0 = (row >> 1) & 7;
+    }
+    // the panel: rows (element (0, 0) at `panel`, row stride K) and this
+    // tile's range
+    __device__ __forceinline__ void at(unsigned short* panel, int K, int lane, int wave, int a, int b) {
+        dv = tile_view(panel, (long long)kBM * K * 2);
+        dst_lane = (unsigned)(((kRows * wave + lane / 8) * K + 8 * (lane & 7)) * 2);
+        row8 = (unsigned)(8 * K * 2);
+        k0 = a;
+        k1 = b;
+    }
+};
 
 // Wave 0 waits until flags f0, f0 + kFlagStride, ... (n of them) are all set,
 // one lane per flag, 64 at a time, so a panel's flags cost one round trip
@@ -128,12 +162,10 @@ __device__ __forceinline__ bool wg_wait(const AgGemmParams& p, const int* f0, in
     return __hip_atomic_load(&p.status->code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
 }
 
-// All waves' stores are complete, then the flag is set once (with the
-// check_flags debug knob: and its old value must be 0, else RING_EPROTOCOL
-// at (q, g, pos)).
+// Set flag f once, after every wave's stores are complete (the caller's K
+// loop ends with a full wait and a workgroup barrier); with the check_flags
+// debug knob its old value must be 0, else RING_EPROTOCOL at (q, g, pos).
 __device__ __forceinline__ void wg_signal(const AgGemmParams& p, int* f, int tid, int q, int g, int pos) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
     if (tid == 0) {
         if (p.check_flags) {
             if (__hip_atomic_fetch_add(f, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
@@ -149,10 +181,8 @@ __device__ __forceinline__ void wg_signal(const AgGemmParams& p, int* f, int tid
 template <class G, bool GELU>
 __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
     constexpr bool kDefer = GELU && G::BN == 256;
-    constexpr int kCopyU = kDefer ? 4 : 8;   // copies in flight; the deferred store holds registers
     constexpr int BN = G::BN;
     const int tid = threadIdx.x;
-    const int nthreads = 64 * G::NW;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave / G::WC, wc = wave % G::WC;
@@ -162,60 +192,50 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
     const int left = (q - 1 + P) % P;
     const int Mc = p.M / P;
     // the workspace's record of data earlier calls left: none may lie under
-    // the slice flags (every wave sees the same answer and leaves)
+    // the panel flags (every wave sees the same answer and leaves)
     if (blockIdx.x == 0 && tid == 0) ws_add_data(p.status, p.ws_data);
     if (!ws_ok(p.status, ws_record(p.status), p.ws_zero, lane)) return;
 
-    // place the local block (nobody waits for it in A_full)
-    for (int pos = grp; pos < p.tpc; pos += p.groups) {
-        int r0, r1;
-        slice_rows(p, pos, r0, r1);
-        copy_rows<POL_PLAIN, kCopyU>(p.As[q] + (size_t)r0 * p.K, p.Af[q] + ((size_t)q * Mc + r0) * p.K, r1 - r0, p.K,
-                             tid, nthreads);
-    }
     DeferredGeluStore<G> dg;
     if constexpr (kDefer) dg.init(lds, lane, wave);
+    ForwardHook<G> fw;
+    fw.init(lds, lane, wave);
     for (int f = 0; f < P; ++f) {
         const int c = (q - f + P) % P;
-        // forward this workgroup's slices of phase g = f + 1 before the tiles
-        // of phase f, so the tiles of phase g find their panel forwarded a
-        // whole phase earlier
-        const int g = f + 1;
-        if (g < P) {
-            const int cg = (q - g + P) % P;
-            for (int pos = grp; pos < p.tpc; pos += p.groups) {
-                int r0, r1;
-                slice_rows(p, pos, r0, r1);
-                unsigned short* dst = p.Af[q] + ((size_t)cg * Mc + r0) * p.K;
-                if (g >= 2 && !wg_wait(p, ag_flag(p, g - 1, left, pos), 1, wave, lane, q, g, pos)) return;
-                if (g == 1)   // the left rank's own block, straight from its input
-                    copy_rows<POL_PLAIN, kCopyU>(p.As[left] + (size_t)r0 * p.K, dst, r1 - r0, p.K, tid, nthreads);
-                else
-                    copy_rows<POL_DEV, kCopyU>(p.Af[left] + ((size_t)cg * Mc + r0) * p.K, dst, r1 - r0, p.K, tid,
-                                       nthreads);
-                if (!(q == 0 && p.drop_round > 0 && g == p.drop_round)) wg_signal(p, ag_flag(p, g, q, pos), tid, q, g, pos);
-            }
-        }
-        // GEMM tiles of chunk c
         for (int pos = grp; pos < p.tpc; pos += p.groups) {
             const int pr = pos / p.tn, tc = pos % p.tn;
+            int k0, k1;
+            forward_range(p, tc, k0, k1);
+            fw.at(p.Af[q] + ((size_t)c * Mc + (size_t)pr * kBM) * p.K, p.K, lane, wave, k0, k1);
             f32x16 acc[kMI][G::NI];
-            if (f == 0) {
-                if constexpr (kDefer)
-                    gemm_tile_h<G, POL_PLAIN, true>(p.K, p.N, p.As[q], p.B[q], pr, tc, acc, lds, lane, wave, wr,
-                                                    wc, dg);
-                else
-                    gemm_tile<G, POL_PLAIN>(p.K, p.N, p.As[q], p.B[q], pr, tc, acc, lds, lane, wave, wr, wc);
+            if (f < 2) {
+                // the local block, then the left rank's, straight from the inputs
+                const unsigned short* src = p.As[f == 0 ? q : left];
+                if constexpr (kDefer) {
+                    HookPair<ForwardHook<G>, DeferredGeluStore<G>> hk{fw, dg};
+                    gemm_tile_h<G, POL_PLAIN, true>(p.K, p.N, src, p.B[q], pr, tc, acc, lds, lane, wave, wr, wc,
+                                                    hk);
+                } else {
+                    gemm_tile_with<G, POL_PLAIN>(p.K, p.N, src, p.B[q], pr, tc, acc, lds, lane, wave, wr, wc,
+                                                     fw);
+                }
             } else {
-                // the panel's tn slices, flagged at consecutive positions
-                if (!wg_wait(p, ag_flag(p, f, q, pr * p.tn), p.tn, wave, lane, q, f, pos)) return;
-                if constexpr (kDefer)
-                    gemm_tile_h<G, POL_DEV, true>(p.K, p.N, p.Af[q], p.B[q], c * p.tm_chunk + pr, tc, acc, lds,
-                                                  lane, wave, wr, wc, dg);
-                else
-                    gemm_tile<G, POL_DEV>(p.K, p.N, p.Af[q], p.B[q], c * p.tm_chunk + pr, tc, acc, lds, lane,
-                                          wave, wr, wc);
+                // the left rank's phase f - 1 tiles of this panel, flagged at
+                // consecutive positions
+                if (!wg_wait(p, ag_flag(p, f - 1, left, pr * p.tn), p.tn, wave, lane, q, f, pos)) return;
+                if constexpr (kDefer) {
+                    HookPair<ForwardHook<G>, DeferredGeluStore<G>> hk{fw, dg};
+                    gemm_tile_h<G, POL_DEV, true>(p.K, p.N, p.Af[left], p.B[q], c * p.tm_chunk + pr, tc, acc, lds,
+                                                  lane, wave, wr, wc, hk);
+                } else {
+                    gemm_tile_with<G, POL_DEV>(p.K, p.N, p.Af[left], p.B[q], c * p.tm_chunk + pr, tc, acc,
+                                                   lds, lane, wave, wr, wc, fw);
+                }
             }
+            // this tile's share of the panel is in A_full[q]: flag it for the
+            // right rank's next phase (the last phase has no reader)
+            if (f >= 1 && f + 1 < P && !(q == 0 && p.drop_round > 0 && f == p.drop_round))
+                wg_signal(p, ag_flag(p, f, q, pos), tid, q, f, pos);
             const size_t at = ((size_t)c * Mc + pr * kBM + wr * kWM) * p.N + tc * BN + wc * G::WN;
             if constexpr (kDefer) {
                 dg.flush();   // what the K loop had no steps left for
@@ -238,7 +258,7 @@ __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void ag_gemm_kernel(AgGem
     constexpr int kExtra = GELU && G::BN == 256 ? DeferredGeluStore<G>::kLds : 0;
     __shared__ __attribute__((aligned(16))) unsigned short lds[(G::kLds + kExtra) / 2];
     ag_gemm_body<G, GELU>(p, lds);
-    // The last workgroup to finish clears the slice flags for the next call
+    // The last workgroup to finish clears the panel flags for the next call
     // (every reader is done by then; an abandoned launch gets here too).
     // Wave 0 counts the workgroup out and, if it was the last, clears.
     __syncthreads();
@@ -284,8 +304,8 @@ template <class G, bool GELU>
 static int launch_ag_gemm(AgGemmParams& prm, const DevInfo& di, hipStream_t stream) {
     prm.tn = prm.N / G::BN;
     prm.tpc = prm.tm_chunk * prm.tn;
-    // every workgroup must be resident (the panel's workgroups wait for each
-    // other's slices)
+    // every workgroup must be resident (tiles wait for the left rank's tiles
+    // of the previous phase)
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ag_gemm_kernel<G, GELU>, 64 * G::NW, 0) != hipSuccess ||
         occ < G::kWGsPerCU)

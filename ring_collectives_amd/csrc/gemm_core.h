@@ -124,25 +124,44 @@ __device__ __forceinline__ void wait_vm(int n) {
     else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     else if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     else if (n >= 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else if (n >= 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (n >= 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
     else if (n >= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if (n >= 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if (n >= 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
     else if (n >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
     else if (n >= 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Work a caller slips into the K loop of a tile.  At step t, right after the
-// step's stage loads, issue(t) runs if issues(t) (wave-uniform) and then
-// issues exactly kOps vector memory operations; the next step's wait lets
-// those stay in flight, since they come after the loads it waits for.
+// Work a caller slips into the K loop of a tile (two-buffer pipeline only).
+// At step t, right after the step's stage loads, issue(t) issues exactly
+// ops(t) vector memory operations (both wave-uniform); the next step's wait
+// lets those stay in flight, since they come after the loads it waits for.
 // begin() and end(steps) bracket the loop.
 struct NoHook {
-    static constexpr int kOps = 0;
+    static constexpr bool kActive = false;
     __device__ __forceinline__ void begin() {}
-    __device__ __forceinline__ bool issues(int) const { return false; }
+    __device__ __forceinline__ int ops(int) const { return 0; }
     __device__ __forceinline__ void issue(int) {}
     __device__ __forceinline__ void end(int) {}
+};
+
+// Two hooks in one K loop: a's operations, then b's.
+template <class H1, class H2>
+struct HookPair {
+    static constexpr bool kActive = true;
+    H1& a;
+    H2& b;
+    __device__ __forceinline__ void begin() { a.begin(); b.begin(); }
+    __device__ __forceinline__ int ops(int t) const { return a.ops(t) + b.ops(t); }
+    __device__ __forceinline__ void issue(int t) {
+        if (a.ops(t) > 0) a.issue(t);
+        if (b.ops(t) > 0) b.issue(t);
+    }
+    __device__ __forceinline__ void end(int steps) { a.end(steps); b.end(steps); }
 };
 
 // C tile (tr, tc) of A B into acc (the wave's part): rows 256 tr .. of A
@@ -171,7 +190,7 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
                                             f32x16 (&acc)[kMI][G::NI], unsigned short* lds,
                                             int lane, int wave, int wr, int wc, Hook& hook,
                                             int kbeg = 0, int kl = -1) {
-    static_assert(Hook::kOps == 0 || (G::NS == 2 && G::R == 1), "K-loop work needs one stage per step");
+    static_assert(!Hook::kActive || G::NS == 2, "K-loop work needs the two-buffer pipeline");
     constexpr int BN = G::BN;
     if (kl < 0) kl = K;
 #pragma unroll
@@ -323,12 +342,11 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
 #pragma unroll
             for (int r = 0; r < G::R; ++r) {
                 const int t = p * G::R + r;
-                if (r == 0) {                      // B stage t and A stage p have landed
-                    if (Hook::kOps > 0 && t > 0 && hook.issues(t - 1)) wait_vm(Hook::kOps);
-                    else wait_vm(0);
-                } else {
-                    wait_vm(G::kLoadsA);           // B stage t has; A stage p + 1 may be in flight
-                }
+                // what step t - 1 issued after B stage t: its hook work (and,
+                // on the second step of an A stage, A stage p + 1 before it)
+                const int later = Hook::kActive && t > 0 ? hook.ops(t - 1) : 0;
+                if (r == 0) wait_vm(later);        // B stage t and A stage p have landed
+                else wait_vm(G::kLoadsA + later);  // B stage t has; A stage p + 1 may be in flight
                 lds_barrier();                     // everyone's has; buffers of step t - 1 are free
                 // The first k-step's fragments are read before the loads
                 // are issued, so their latency hides behind the issue --
@@ -337,7 +355,7 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
                 // together).
                 const unsigned abuf = (unsigned)((p & 1) * G::kStageA);
                 const unsigned bbuf = (unsigned)(G::kBBase + (t & 1) * G::kStageB);
-                if constexpr (Hook::kOps == 0) {
+                if constexpr (!Hook::kActive) {
                     bf16x8 af0[kMI], bf0[G::NI];
                     read_frags(abuf, r * G::KK, bbuf, 0, af0, bf0);
                     __builtin_amdgcn_sched_barrier(0);
@@ -348,7 +366,7 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
                 } else {
                     issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
                     if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
-                    if (hook.issues(t)) {
+                    if (hook.ops(t) > 0) {
                         __builtin_amdgcn_sched_barrier(0);   // not ahead of the stage loads
                         hook.issue(t);
                     }
@@ -395,6 +413,18 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
     }
     wait_vm(0);        // the trailing loads have landed
     __syncthreads();   // all waves are done with the stages before the epilogue uses LDS
+}
+
+// gemm_tile_h with the usual (untransposed) blocks.  Callers outside this
+// header go through this wrapper: calling gemm_tile_h directly from their
+// kernels' bodies, the host compilation pass rejects the template for some
+// tile shapes (a substitution failure it gives no reason for).
+template <class G, int APOL, class Hook>
+__device__ __forceinline__ void gemm_tile_with(int K, int N, const unsigned short* __restrict__ A,
+                                               const unsigned short* __restrict__ B, int tr, int tc,
+                                               f32x16 (&acc)[kMI][G::NI], unsigned short* lds, int lane, int wave,
+                                               int wr, int wc, Hook& hook) {
+    gemm_tile_h<G, APOL, false>(K, N, A, B, tr, tc, acc, lds, lane, wave, wr, wc, hook);
 }
 
 template <class G, int APOL = POL_PLAIN>
@@ -485,8 +515,8 @@ struct DeferredGeluStore {
     static constexpr int kLds = G::NW * kSlice;       // LDS the kernel adds past its stages
     static constexpr int kM0 = kMI - D - 1;           // the row of blocks left staged
     static constexpr int kPend = D * G::NI * 4;       // register pairs held: (mi, ni, 4-column group)
-    static constexpr int kOps = 1;                    // stores per K step
-    static constexpr int kChunks = (D + 1) * 4;       // a chunk: 8 rows
+    static constexpr bool kActive = true;
+    static constexpr int kChunks = (D + 1) * 4;       // a chunk: 8 rows, one store
     u32x2 pend[kPend];
     rsrc_t ov;           // the wave's part of the output tile
     unsigned out_lane;   // byte offset of the lane's 16 bytes in row 0 of it
@@ -506,7 +536,7 @@ struct DeferredGeluStore {
         lds_ = lds;
     }
     __device__ __forceinline__ void begin() { first = next; }
-    __device__ __forceinline__ bool issues(int t) const { return first + t < kChunks; }
+    __device__ __forceinline__ int ops(int t) const { return first + t < kChunks ? 1 : 0; }
     __device__ __forceinline__ void end(int steps) { next = first + steps < kChunks ? first + steps : kChunks; }
 
     // One row of blocks (bf16(product), in (ni, group) order) into the slice,

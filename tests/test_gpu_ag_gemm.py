@@ -165,9 +165,9 @@ def test_errors():
 
 
 def test_watchdog_reports_timeout_and_recovers():
-    """Rank 0 never flags its slices of phase 1: its own panels' tiles and
-    its right neighbour's forwarding wait, time out, and every workgroup
-    exits; the same workspace then serves a normal call."""
+    """Rank 0 never flags its tiles of phase 1: its right neighbour's phase-2
+    tiles wait for them, time out, and every workgroup exits; the same
+    workspace then serves a normal call."""
     P, M, Nn, K = 4, 2048, 512, 128
     rng = np.random.default_rng(540)
     As = inputs.small_int_bf16(rng, (P, M // P, K))
