@@ -97,7 +97,7 @@ def test_normal_within_bound(P, M, N, K):
 def test_full_occupancy_integer_exact(P, tile_n):
     """M = N = 4096: every CU busy, panels forwarded by many workgroups while
     others already multiply; every element of every output, three calls on
-    one workspace (the slice flags must be cleared between calls)."""
+    one workspace (the panel flags must be cleared between calls)."""
     M = Nn = 4096
     K = 256
     note("ag_gemm full occupancy P=%d tile_n=%d" % (P, tile_n))

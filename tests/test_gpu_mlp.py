@@ -317,7 +317,7 @@ def test_errors():
 
 
 def test_watchdog_reports_timeout_and_recovers():
-    """Rank 0 never flags its slices of the all-gather's phase 1: the layer
+    """Rank 0 never flags its tiles of the all-gather's phase 1: the layer
     ends in RING_ETIMEOUT; the same workspace, cleared, then serves a normal
     call."""
     P, M, D, F = 4, 1024, 256, 1024

@@ -10,11 +10,13 @@ position of phase f - 1 and adds that item's partial tile to its own product
 (q - s - 2) mod P to what its left neighbour sends).  The model checks that
 every schedule finishes and that every rank ends with the sum of its chunk.
 
-All-gather + GEMM: workgroup (group g, rank q) forwards its slices of phase
-f + 1 (waiting for the left rank's slice of phase f) and then computes its
-tiles of phase f (waiting for every slice of the tile's panel).  The model
-checks that every schedule finishes, that every tile reads its whole panel
-after it was written, and that every gathered buffer ends complete.
+All-gather + GEMM: a tile of phase f reads its panel of chunk (q - f) mod P
+(from an input block in phases 0 and 1, else from the left rank's gathered
+buffer once the left rank's phase-(f - 1) tiles of the panel have flagged)
+and copies its column tile's K range of the panel into rank q's gathered
+buffer.  The model checks that every schedule finishes, that every tile
+reads its whole panel after it was written, and that every gathered buffer
+ends complete.
 
 Each model plants a mistake that the checks must catch.
 """
@@ -111,41 +113,35 @@ def test_gemm_rs_wrong_wait_is_caught():
 
 
 # ------------------------------------------------------------ all-gather + GEMM
-def _ag_gemm_sim(P, tm_chunk, tn, groups, rng, ahead=True, skip_forward_wait=False):
-    """Returns (finished, tiles_ok, gathered_ok).  Slices are the kernel's:
-    tile position pos = pr * tn + t forwards rows 256 t / tn .. of panel pr;
-    here a slice is one token that names (source chunk, panel, slice)."""
+def _ag_gemm_sim(P, tm_chunk, tn, groups, rng, skip_wait=False, flag_first=False):
+    """Returns (finished, tiles_ok, gathered_ok).  Workgroup (group g, rank
+    q) takes tile positions pos = g, g + groups, ... (pos = pr * tn + t: panel
+    pr, column tile t) in every phase f, phases in order.  A tile of phase f
+    reads the whole panel pr of chunk c = (q - f) mod P -- from rank q's own
+    block (f = 0), the left rank's own block (f = 1) or the left rank's
+    gathered buffer (f >= 2), waiting for the left rank's tn phase-(f - 1)
+    tiles of that panel -- and copies K range t of it into its own gathered
+    buffer, then flags (f, q, pos).  A token (c, pr, t) names a piece of the
+    data.  Planted: skip_wait reads without waiting; flag_first sets the flag
+    before the copy lands."""
     tpc = tm_chunk * tn
-    # gathered[q][c][pos] holds the token of chunk c's slice pos, or None
-    gathered = [[[None] * tpc for _ in range(P)] for _ in range(P)]
+    gathered = [[[[None] * tn for _ in range(tm_chunk)] for _ in range(P)] for _ in range(P)]
     flags = set()       # (phase, rank, pos)
     tiles_ok = True
 
-    def token(c, pos):
-        return (c, pos)
-
-    # each workgroup's program as a list of steps; a step is (wait_keys, action)
     def program(q, grp):
         left = (q - 1) % P
-        mine = list(range(grp, tpc, groups))
         steps = []
-        for pos in mine:                                # place the local block
-            steps.append(([], ("place", q, pos)))
-
-        def forward(g_):
-            for pos in mine:
-                waits = [] if (g_ < 2 or skip_forward_wait) else [(g_ - 1, left, pos)]
-                steps.append((waits, ("fwd", q, g_, pos)))
-
         for f in range(P):
-            if ahead and f + 1 < P:
-                forward(f + 1)
-            if not ahead and f >= 1:
-                forward(f)
-            for pos in mine:
+            for pos in range(grp, tpc, groups):
                 pr = pos // tn
-                waits = [] if f == 0 else [(f, q, pr * tn + t) for t in range(tn)]
-                steps.append((waits, ("tile", q, f, pos)))
+                waits = [] if (f < 2 or skip_wait) else [(f - 1, left, pr * tn + t) for t in range(tn)]
+                if flag_first:
+                    steps.append((waits, ("flag", q, f, pos)))
+                    steps.append(([], ("tile", q, f, pos)))
+                else:
+                    steps.append((waits, ("tile", q, f, pos)))
+                    steps.append(([], ("flag", q, f, pos)))
         return steps
 
     progs = {(q, g): program(q, g) for q in range(P) for g in range(groups)}
@@ -158,47 +154,42 @@ def _ag_gemm_sim(P, tm_chunk, tn, groups, rng, ahead=True, skip_forward_wait=Fal
         k = ready[int(rng.integers(len(ready)))]
         _, act = progs[k][pc[k]]
         pc[k] += 1
-        if act[0] == "place":
-            _, q, pos = act
-            gathered[q][q][pos] = token(q, pos)
-        elif act[0] == "fwd":
-            _, q, g_, pos = act
-            left = (q - 1) % P
-            c = (q - g_) % P
-            # phase 1 copies the left rank's own shard; later phases its gathered buffer
-            src = token(c, pos) if g_ == 1 else gathered[left][c][pos]
-            gathered[q][c][pos] = src
-            flags.add((g_, q, pos))
+        _, q, f, pos = act
+        if act[0] == "flag":
+            if 1 <= f <= P - 2:
+                flags.add((f, q, pos))
+            continue
+        left = (q - 1) % P
+        c = (q - f) % P
+        pr, t = pos // tn, pos % tn
+        if f < 2:
+            panel = [(c, pr, u) for u in range(tn)]            # an input block: always whole
         else:
-            _, q, f, pos = act
-            c = (q - f) % P
-            pr = pos // tn
-            if f > 0:
-                panel = [gathered[q][c][pr * tn + t] for t in range(tn)]
-                tiles_ok &= panel == [token(c, pr * tn + t) for t in range(tn)]
+            panel = list(gathered[left][c][pr])
+        tiles_ok &= panel == [(c, pr, u) for u in range(tn)]
+        gathered[q][c][pr][t] = panel[t]
     finished = all(pc[k] == len(progs[k]) for k in progs)
-    gathered_ok = all(gathered[q][c][pos] == token(c, pos) for q in range(P) for c in range(P)
-                      for pos in range(tpc))
+    gathered_ok = all(gathered[q][c][pr][t] == (c, pr, t) for q in range(P) for c in range(P)
+                      for pr in range(tm_chunk) for t in range(tn))
     return finished, tiles_ok, gathered_ok
 
 
 @pytest.mark.parametrize("P,tm_chunk,tn,groups", [(1, 2, 2, 2), (2, 1, 2, 2), (3, 2, 2, 1), (4, 2, 4, 3),
-                                                  (4, 1, 16, 16), (8, 1, 2, 1)])
-@pytest.mark.parametrize("ahead", [True, False])
-def test_ag_gemm_every_schedule_finishes_with_whole_panels(P, tm_chunk, tn, groups, ahead):
+                                                  (4, 1, 16, 16), (8, 1, 2, 1), (5, 2, 3, 4)])
+def test_ag_gemm_every_schedule_finishes_with_whole_panels(P, tm_chunk, tn, groups):
     rng = np.random.default_rng(920 + P + tn + groups)
     for _ in range(15):
-        finished, tiles_ok, gathered_ok = _ag_gemm_sim(P, tm_chunk, tn, groups, rng, ahead=ahead)
-        assert finished and tiles_ok and gathered_ok, (P, tm_chunk, tn, groups, ahead)
+        finished, tiles_ok, gathered_ok = _ag_gemm_sim(P, tm_chunk, tn, groups, rng)
+        assert finished and tiles_ok and gathered_ok, (P, tm_chunk, tn, groups)
 
 
-def test_ag_gemm_forward_without_wait_is_caught():
-    """Forwarding a slice before the left rank has it copies a hole: some
-    schedule gives a tile a panel with a missing slice or leaves a gathered
-    buffer incomplete."""
+@pytest.mark.parametrize("mistake", ["skip_wait", "flag_first"])
+def test_ag_gemm_planted_mistakes_are_caught(mistake):
+    """A tile that reads the left rank's gathered panel without waiting, or a
+    flag set before its tile's copy, lets some schedule read a hole."""
     rng = np.random.default_rng(930)
     caught = 0
     for _ in range(30):
-        finished, tiles_ok, gathered_ok = _ag_gemm_sim(4, 2, 4, 2, rng, skip_forward_wait=True)
+        finished, tiles_ok, gathered_ok = _ag_gemm_sim(4, 2, 4, 2, rng, **{mistake: True})
         caught += not (finished and tiles_ok and gathered_ok)
     assert caught > 0
