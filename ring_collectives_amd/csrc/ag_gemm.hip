@@ -78,6 +78,7 @@ __device__ __forceinline__ void forward_range(const AgGemmParams& p, int tc, int
 template <class G>
 struct ForwardHook {
     static constexpr bool kActive = true;
+    static constexpr bool kHalfLoads = true;
     static constexpr int kRows = kBM / G::NW;     // rows of a stage this wave copies
     static constexpr int kStores = kRows / 8;     // 16-byte stores per lane and stage
     const unsigned short* lds;

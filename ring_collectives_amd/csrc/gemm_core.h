@@ -62,10 +62,8 @@ template <int BN_, int NW_> struct Geo {
     static constexpr int kARowBytes = BKA * 2;           // 128
     static constexpr int kAC = BKA / 8;                  // 16-byte chunks per A row
     static constexpr int kARows = 64 / kAC;              // A rows per 1-KiB load
-    static constexpr int kLoadsA = kBM / kARows / NW;    // per wave per A stage
     static constexpr int kBRowBytes = BN * 2;
     static constexpr int kBRows = 1024 / kBRowBytes;     // B rows per 1-KiB load
-    static constexpr int kLoadsB = BKB / kBRows / NW;    // per wave per B stage
     static constexpr int kPart = kWM * WN;               // floats of a wave's part
     static constexpr int kTile = kBM * BN;
     static constexpr int kEpiStride = WN + 4;            // LDS floats per row of the final transpose
@@ -77,7 +75,6 @@ template <int BN_, int NW_> struct Geo {
     static __device__ __forceinline__ int swz_b(int k) { return BN == 64 ? 4 * ((k >> 1) & 1) : 4 * (k & 3); }
     static_assert(kLds * kWGsPerCU <= 160 * 1024, "LDS");
     static_assert(NW * kEpiWave * 4 <= kLds, "epilogue LDS");
-    static_assert(kBM % (NW * kARows) == 0 && BKB % (NW * kBRows) == 0, "load split");
     static_assert(NS == 2 || R == 1, "a deep pipeline stages A and B together");
 };
 
@@ -143,6 +140,7 @@ __device__ __forceinline__ void wait_vm(int n) {
 // begin() and end(steps) bracket the loop.
 struct NoHook {
     static constexpr bool kActive = false;
+    static constexpr bool kHalfLoads = true;   // see gemm_tile_h
     __device__ __forceinline__ void begin() {}
     __device__ __forceinline__ int ops(int) const { return 0; }
     __device__ __forceinline__ void issue(int) {}
@@ -153,6 +151,7 @@ struct NoHook {
 template <class H1, class H2>
 struct HookPair {
     static constexpr bool kActive = true;
+    static constexpr bool kHalfLoads = H1::kHalfLoads && H2::kHalfLoads;
     H1& a;
     H2& b;
     __device__ __forceinline__ void begin() { a.begin(); b.begin(); }
@@ -192,6 +191,16 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
                                             int kbeg = 0, int kl = -1) {
     static_assert(!Hook::kActive || G::NS == 2, "K-loop work needs the two-buffer pipeline");
     constexpr int BN = G::BN;
+    // Who issues the stage loads.  With the 256-wide tile only waves 0-3 do
+    // (16 each), one per SIMD: all 64 loads of a step queue up at the CU's
+    // address unit, and the waves that issue them stall until it takes
+    // them; this way each SIMD's other wave goes straight on to its MFMAs
+    // meanwhile and keeps the matrix core busy.  (A hook whose work would
+    // fall on the loading waves as well can ask for every wave to load.)
+    constexpr int LW = BN == 256 && Hook::kHalfLoads ? G::NW / 2 : G::NW;
+    constexpr int kLA = kBM / G::kARows / LW;          // this wave's loads per A stage, if it loads
+    constexpr int kLB = G::BKB / G::kBRows / LW;       // ... per B stage
+    static_assert(kBM % (LW * G::kARows) == 0 && G::BKB % (LW * G::kBRows) == 0, "load split");
     if (kl < 0) kl = K;
 #pragma unroll
     for (int mi = 0; mi < kMI; ++mi)
@@ -205,7 +214,7 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
     const rsrc_t Av = tile_view(A + (size_t)tr * kBM * K + kbeg, ((long long)(kBM - 1) * K + kl) * 2);
     const rsrc_t Bv = tile_view(B + (size_t)kbeg * N + (size_t)tc * BN, ((long long)(kl - 1) * N + BN) * 2);
 
-    // Direct loads.  A instruction i of wave w fills rows 8 (kLoadsA w + i)
+    // Direct loads.  A instruction i of loading wave w fills rows 8 (kLA w + i)
     // .. +7 (lane: row + lane / 8, stored chunk lane % 8); B instruction i
     // fills kBRows rows of k (lane: row + lane / (BN / 8), stored chunk
     // lane % (BN / 8)).  Each lane fetches the logical chunk its stored
@@ -224,9 +233,10 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
     }
     auto issue_a = [&](int st, int slot) {                 // A stage st (K 64 st ..)
         const unsigned base = (unsigned)(slot * G::kStageA);
+        if (wave >= LW) return;
 #pragma unroll
-        for (int i = 0; i < G::kLoadsA; ++i) {
-            const int r0 = (wave * G::kLoadsA + i) * G::kARows;
+        for (int i = 0; i < kLA; ++i) {
+            const int r0 = (wave * kLA + i) * G::kARows;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(Av, lds_at(lds, base + r0 * G::kARowBytes), 16,
                                                      a_voff[i & 1],
                                                      (unsigned)((r0 * K + st * G::BKA) * 2), 0, APOL);
@@ -234,9 +244,10 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
     };
     auto issue_b = [&](int st, int slot) {                 // B stage st (K BKB st ..)
         const unsigned base = (unsigned)(G::kBBase + slot * G::kStageB);
+        if (wave >= LW) return;
 #pragma unroll
-        for (int i = 0; i < G::kLoadsB; ++i) {
-            const int k0 = (wave * G::kLoadsB + i) * G::kBRows;
+        for (int i = 0; i < kLB; ++i) {
+            const int k0 = (wave * kLB + i) * G::kBRows;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(Bv, lds_at(lds, base + k0 * G::kBRowBytes), 16,
                                                      b_voff[i & 1],
                                                      (unsigned)((st * G::BKB + k0) * N * 2), 0, POL_PLAIN);
@@ -346,7 +357,7 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
                 // on the second step of an A stage, A stage p + 1 before it)
                 const int later = Hook::kActive && t > 0 ? hook.ops(t - 1) : 0;
                 if (r == 0) wait_vm(later);        // B stage t and A stage p have landed
-                else wait_vm(G::kLoadsA + later);  // B stage t has; A stage p + 1 may be in flight
+                else wait_vm((wave < LW ? kLA : 0) + later);  // B stage t has; A stage p + 1 may be in flight
                 lds_barrier();                     // everyone's has; buffers of step t - 1 are free
                 // The first k-step's fragments are read before the loads
                 // are issued, so their latency hides behind the issue --
@@ -386,7 +397,8 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
         // issue order and nothing else is counted (the previous tile's stores
         // are drained first), so waiting for at most (stages after t) x
         // (loads per stage) to be in flight waits for exactly stage t.
-        constexpr int L = G::kLoadsA + G::kLoadsB;  // this wave's loads per stage
+        static_assert(LW == G::NW, "every wave loads in the deep pipeline");
+        constexpr int L = kLA + kLB;                // this wave's loads per stage
         wait_vm(0);
 #pragma unroll
         for (int s = 0; s < G::NS - 1; ++s)
@@ -516,6 +528,7 @@ struct DeferredGeluStore {
     static constexpr int kM0 = kMI - D - 1;           // the row of blocks left staged
     static constexpr int kPend = D * G::NI * 4;       // register pairs held: (mi, ni, 4-column group)
     static constexpr bool kActive = true;
+    static constexpr bool kHalfLoads = false;         // its staging work would fall on the loading waves
     static constexpr int kChunks = (D + 1) * 4;       // a chunk: 8 rows, one store
     u32x2 pend[kPend];
     rsrc_t ov;           // the wave's part of the output tile
