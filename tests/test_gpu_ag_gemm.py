@@ -187,6 +187,23 @@ def test_watchdog_reports_timeout_and_recovers():
     np.testing.assert_array_equal(gc.view(np.uint32), want_c.view(np.uint32))
 
 
+@pytest.mark.parametrize("P,M,N,K", [(3, 768, 2048, 64), (4, 1024, 4096, 128), (2, 512, 1024, 192)])
+def test_more_column_tiles_than_k_pieces(P, M, N, K, tile_n):
+    """The tiles of a panel forward its K range between them, one share per
+    column tile, in pieces of 8 columns: with more column tiles than pieces
+    some tiles forward nothing, and the gathered buffers must still come out
+    whole (pre-filled with a NaN pattern, so a hole shows), every product
+    exact."""
+    note("ag_gemm share split P=%d M=%d N=%d K=%d tile_n=%d" % (P, M, N, K, tile_n))
+    rng = np.random.default_rng(560 + P + K)
+    As = inputs.small_int_bf16(rng, (P, M // P, K))
+    B = inputs.small_int_bf16(rng, (P, K, N))
+    gf, gc, _ = _run(As, B)
+    want_full, want_c = oracle.all_gather_gemm(As, B)
+    np.testing.assert_array_equal(gf, want_full)
+    np.testing.assert_array_equal(gc.view(np.uint32), want_c.view(np.uint32))
+
+
 def _random_shapes(seed, count):
     """Seeded shapes the kernel accepts: P of 2..8 (5, 6 and 7 included),
     row blocks of one or two 256-row tiles per rank, N a multiple of 128,
