@@ -78,7 +78,6 @@ __device__ __forceinline__ void forward_range(const AgGemmParams& p, int tc, int
 template <class G>
 struct ForwardHook {
     static constexpr bool kActive = true;
-    static constexpr bool kHalfLoads = true;
     static constexpr int kRows = kBM / G::NW;     // rows of a stage this wave copies
     static constexpr int kStores = kRows / 8;     // 16-byte stores per lane and stage
     const unsigned short* lds;
@@ -177,11 +176,8 @@ __device__ __forceinline__ void wg_signal(const AgGemmParams& p, int* f, int tid
     }
 }
 
-// The gelu output of the 256-wide tile is stored during the next tile's K
-// loop (DeferredGeluStore); the other widths store each tile as it finishes.
 template <class G, bool GELU>
 __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
-    constexpr bool kDefer = GELU && G::BN == 256;
     constexpr int BN = G::BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -197,8 +193,6 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
     if (blockIdx.x == 0 && tid == 0) ws_add_data(p.status, p.ws_data);
     if (!ws_ok(p.status, ws_record(p.status), p.ws_zero, lane)) return;
 
-    DeferredGeluStore<G> dg;
-    if constexpr (kDefer) dg.init(lds, lane, wave);
     ForwardHook<G> fw;
     fw.init(lds, lane, wave);
     for (int f = 0; f < P; ++f) {
@@ -212,36 +206,20 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
             if (f < 2) {
                 // the local block, then the left rank's, straight from the inputs
                 const unsigned short* src = p.As[f == 0 ? q : left];
-                if constexpr (kDefer) {
-                    HookPair<ForwardHook<G>, DeferredGeluStore<G>> hk{fw, dg};
-                    gemm_tile_h<G, POL_PLAIN, true>(p.K, p.N, src, p.B[q], pr, tc, acc, lds, lane, wave, wr, wc,
-                                                    hk);
-                } else {
-                    gemm_tile_with<G, POL_PLAIN>(p.K, p.N, src, p.B[q], pr, tc, acc, lds, lane, wave, wr, wc,
-                                                     fw);
-                }
+                gemm_tile_with<G, POL_PLAIN>(p.K, p.N, src, p.B[q], pr, tc, acc, lds, lane, wave, wr, wc, fw);
             } else {
                 // the left rank's phase f - 1 tiles of this panel, flagged at
                 // consecutive positions
                 if (!wg_wait(p, ag_flag(p, f - 1, left, pr * p.tn), p.tn, wave, lane, q, f, pos)) return;
-                if constexpr (kDefer) {
-                    HookPair<ForwardHook<G>, DeferredGeluStore<G>> hk{fw, dg};
-                    gemm_tile_h<G, POL_DEV, true>(p.K, p.N, p.Af[left], p.B[q], c * p.tm_chunk + pr, tc, acc, lds,
-                                                  lane, wave, wr, wc, hk);
-                } else {
-                    gemm_tile_with<G, POL_DEV>(p.K, p.N, p.Af[left], p.B[q], c * p.tm_chunk + pr, tc, acc,
-                                                   lds, lane, wave, wr, wc, fw);
-                }
+                gemm_tile_with<G, POL_DEV>(p.K, p.N, p.Af[left], p.B[q], c * p.tm_chunk + pr, tc, acc, lds, lane,
+                                           wave, wr, wc, fw);
             }
             // this tile's share of the panel is in A_full[q]: flag it for the
             // right rank's next phase (the last phase has no reader)
             if (f >= 1 && f + 1 < P && !(q == 0 && p.drop_round > 0 && f == p.drop_round))
                 wg_signal(p, ag_flag(p, f, q, pos), tid, q, f, pos);
             const size_t at = ((size_t)c * Mc + pr * kBM + wr * kWM) * p.N + tc * BN + wc * G::WN;
-            if constexpr (kDefer) {
-                dg.flush();   // what the K loop had no steps left for
-                dg.fill(acc, (char*)p.C[q] + at * 2, p.N, lane);
-            } else if constexpr (GELU) {
+            if constexpr (GELU) {
                 store_part_rowmajor<G, false, EPI_GELU_BF16>(acc, tile_view(nullptr, 0), (char*)p.C[q] + at * 2,
                                                              p.N, lds, lane, wave);
             } else {
@@ -250,14 +228,11 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
             }
         }
     }
-    if constexpr (kDefer) dg.flush();
 }
 
 template <class G, bool GELU>
 __global__ __launch_bounds__(64 * G::NW, G::kWGsPerCU) void ag_gemm_kernel(AgGemmParams p) {
-    // the deferred gelu store's slices follow the K loop's stages
-    constexpr int kExtra = GELU && G::BN == 256 ? DeferredGeluStore<G>::kLds : 0;
-    __shared__ __attribute__((aligned(16))) unsigned short lds[(G::kLds + kExtra) / 2];
+    __shared__ __attribute__((aligned(16))) unsigned short lds[G::kLds / 2];
     ag_gemm_body<G, GELU>(p, lds);
     // The last workgroup to finish clears the panel flags for the next call
     // (every reader is done by then; an abandoned launch gets here too).

@@ -140,27 +140,10 @@ __device__ __forceinline__ void wait_vm(int n) {
 // begin() and end(steps) bracket the loop.
 struct NoHook {
     static constexpr bool kActive = false;
-    static constexpr bool kHalfLoads = true;   // see gemm_tile_h
     __device__ __forceinline__ void begin() {}
     __device__ __forceinline__ int ops(int) const { return 0; }
     __device__ __forceinline__ void issue(int) {}
     __device__ __forceinline__ void end(int) {}
-};
-
-// Two hooks in one K loop: a's operations, then b's.
-template <class H1, class H2>
-struct HookPair {
-    static constexpr bool kActive = true;
-    static constexpr bool kHalfLoads = H1::kHalfLoads && H2::kHalfLoads;
-    H1& a;
-    H2& b;
-    __device__ __forceinline__ void begin() { a.begin(); b.begin(); }
-    __device__ __forceinline__ int ops(int t) const { return a.ops(t) + b.ops(t); }
-    __device__ __forceinline__ void issue(int t) {
-        if (a.ops(t) > 0) a.issue(t);
-        if (b.ops(t) > 0) b.issue(t);
-    }
-    __device__ __forceinline__ void end(int steps) { a.end(steps); b.end(steps); }
 };
 
 // C tile (tr, tc) of A B into acc (the wave's part): rows 256 tr .. of A
@@ -177,13 +160,9 @@ struct HookPair {
 // cb + 4 (j % 4) .. +3, lane i receives rows kb .. kb+3 of column cb + i, so
 // two such reads give a lane its 8 consecutive k of one column.
 //
-// With SWAP the MFMAs take the B fragment as their first operand and so
-// compute the transposed block: lane l then holds row m = l % 32 of each
-// block, at columns 8 (v / 4) + 4 (l / 32) + v % 4 for accumulator v, that is
-// runs of 4 consecutive columns of one row.  (The same products, summed the
-// same way.)  Without it lane l holds column l % 32, rows 8 (v / 4) + 4 (l /
-// 32) + v % 4.
-template <class G, int APOL, bool SWAP, class Hook>
+// Accumulator v of lane l holds column l % 32, row 8 (v / 4) + 4 (l / 32) +
+// v % 4 of its 32 x 32 block.
+template <class G, int APOL, class Hook>
 __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* __restrict__ A,
                                             const unsigned short* __restrict__ B, int tr, int tc,
                                             f32x16 (&acc)[kMI][G::NI], unsigned short* lds,
@@ -195,9 +174,8 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
     // (16 each), one per SIMD: all 64 loads of a step queue up at the CU's
     // address unit, and the waves that issue them stall until it takes
     // them; this way each SIMD's other wave goes straight on to its MFMAs
-    // meanwhile and keeps the matrix core busy.  (A hook whose work would
-    // fall on the loading waves as well can ask for every wave to load.)
-    constexpr int LW = BN == 256 && Hook::kHalfLoads ? G::NW / 2 : G::NW;
+    // meanwhile and keeps the matrix core busy.
+    constexpr int LW = BN == 256 ? G::NW / 2 : G::NW;
     constexpr int kLA = kBM / G::kARows / LW;          // this wave's loads per A stage, if it loads
     constexpr int kLB = G::BKB / G::kBRows / LW;       // ... per B stage
     static_assert(kBM % (LW * G::kARows) == 0 && G::BKB % (LW * G::kBRows) == 0, "load split");
@@ -311,10 +289,8 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
             for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < G::NI; ++ni)
-                    acc[mi][ni] = SWAP ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                             bf[kk & 1][ni], af[kk & 1][mi], acc[mi][ni], 0, 0, 0)
-                                       : __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                             af[kk & 1][mi], bf[kk & 1][ni], acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        af[kk & 1][mi], bf[kk & 1][ni], acc[mi][ni], 0, 0, 0);
             if (kk + 1 < G::KK) {
 #pragma unroll
                 for (int g = 0; g < kMI * G::NI; ++g) {
@@ -360,31 +336,21 @@ __device__ __forceinline__ void gemm_tile_h(int K, int N, const unsigned short* 
                 else wait_vm((wave < LW ? kLA : 0) + later);  // B stage t has; A stage p + 1 may be in flight
                 lds_barrier();                     // everyone's has; buffers of step t - 1 are free
                 // The first k-step's fragments are read before the loads
-                // are issued, so their latency hides behind the issue --
-                // except where a hook works between the loads and the
-                // MFMAs (its registers and the fragments' do not fit
-                // together).
+                // are issued, so their latency hides behind the issue.  The
+                // hook's work goes after the loads.
                 const unsigned abuf = (unsigned)((p & 1) * G::kStageA);
                 const unsigned bbuf = (unsigned)(G::kBBase + (t & 1) * G::kStageB);
-                if constexpr (!Hook::kActive) {
-                    bf16x8 af0[kMI], bf0[G::NI];
-                    read_frags(abuf, r * G::KK, bbuf, 0, af0, bf0);
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
-                    if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    step(abuf, r * G::KK, bbuf, af0, bf0);
-                } else {
-                    issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
-                    if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
-                    if (hook.ops(t) > 0) {
-                        __builtin_amdgcn_sched_barrier(0);   // not ahead of the stage loads
-                        hook.issue(t);
-                    }
-                    bf16x8 af0[kMI], bf0[G::NI];
-                    read_frags(abuf, r * G::KK, bbuf, 0, af0, bf0);
-                    step(abuf, r * G::KK, bbuf, af0, bf0);
+                bf16x8 af0[kMI], bf0[G::NI];
+                read_frags(abuf, r * G::KK, bbuf, 0, af0, bf0);
+                __builtin_amdgcn_sched_barrier(0);
+                issue_b(t + 1 < KT ? t + 1 : KT - 1, (t + 1) & 1);
+                if (r == 0) issue_a(p + 1 < KA ? p + 1 : KA - 1, (p + 1) & 1);
+                if (Hook::kActive && hook.ops(t) > 0) {
+                    __builtin_amdgcn_sched_barrier(0);   // not ahead of the stage loads
+                    hook.issue(t);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                step(abuf, r * G::KK, bbuf, af0, bf0);
             }
         }
         hook.end(KT);
@@ -436,7 +402,7 @@ __device__ __forceinline__ void gemm_tile_with(int K, int N, const unsigned shor
                                                const unsigned short* __restrict__ B, int tr, int tc,
                                                f32x16 (&acc)[kMI][G::NI], unsigned short* lds, int lane, int wave,
                                                int wr, int wc, Hook& hook) {
-    gemm_tile_h<G, APOL, false>(K, N, A, B, tr, tc, acc, lds, lane, wave, wr, wc, hook);
+    gemm_tile_h<G, APOL>(K, N, A, B, tr, tc, acc, lds, lane, wave, wr, wc, hook);
 }
 
 template <class G, int APOL = POL_PLAIN>
@@ -445,7 +411,7 @@ __device__ __forceinline__ void gemm_tile(int K, int N, const unsigned short* __
                                           f32x16 (&acc)[kMI][G::NI], unsigned short* lds,
                                           int lane, int wave, int wr, int wc, int kbeg = 0, int kl = -1) {
     NoHook none;
-    gemm_tile_h<G, APOL, false>(K, N, A, B, tr, tc, acc, lds, lane, wave, wr, wc, none, kbeg, kl);
+    gemm_tile_h<G, APOL>(K, N, A, B, tr, tc, acc, lds, lane, wave, wr, wc, none, kbeg, kl);
 }
 
 
@@ -499,124 +465,6 @@ __device__ __forceinline__ u32x2 epi_bf16x4(const u32x4 o) {
     if constexpr (EPI == EPI_GELU_BF16) b = gelu_bf16x4(b);
     return b;
 }
-
-// The MLP's first-layer output of a finished 256-wide tile (computed with
-// SWAP, so lane l holds runs of 4 columns of row l % 32 of each 32 x 32
-// block), stored row-major as bf16(gelu(bf16(product))).  The wave's part is
-// 4 rows of blocks, 32 rows x 64 columns (128 bytes a row) each.  A row of
-// blocks goes out through the wave's own 4 KiB slice of LDS (kSlice bytes
-// past the K loop's stages): 8 writes of 8 bytes a lane, then reads of 16
-// bytes a lane, 8 lanes a row, so each store writes 8 whole 128-byte rows.
-// fill() stores the first kMI - D - 1 rows of blocks at once, leaves the
-// next one staged in the slice and keeps the last D as bf16(product) in
-// registers.  The staged row and then the held ones go out during the next
-// tile's K loop, one store a step (a held row is staged with its first
-// store), so most of every tile's output trickles out behind the next
-// tile's operand loads instead of all workgroups storing it together
-// between tiles while the matrix cores wait (the K loop's registers leave
-// room for D = 2).  Nothing in the launch reads the stored values.  fill()
-// takes a tile once the previous one is flushed; flush() stores what the K
-// loop has not.
-//   Slice layout: row r at r 128 bytes, its 16-byte chunk j (columns 8 j ..)
-//   at chunk j ^ (r & 7), so neither the writes (32 rows, one chunk) nor the
-//   reads (8 rows, all chunks) pile onto a few banks.
-template <class G, int D = 2>
-struct DeferredGeluStore {
-    static_assert(G::WN == 64, "rows of 128 bytes");
-    static constexpr int kSlice = 4096;               // bytes of LDS per wave
-    static constexpr int kLds = G::NW * kSlice;       // LDS the kernel adds past its stages
-    static constexpr int kM0 = kMI - D - 1;           // the row of blocks left staged
-    static constexpr int kPend = D * G::NI * 4;       // register pairs held: (mi, ni, 4-column group)
-    static constexpr bool kActive = true;
-    static constexpr bool kHalfLoads = false;         // its staging work would fall on the loading waves
-    static constexpr int kChunks = (D + 1) * 4;       // a chunk: 8 rows, one store
-    u32x2 pend[kPend];
-    rsrc_t ov;           // the wave's part of the output tile
-    unsigned out_lane;   // byte offset of the lane's 16 bytes in row 0 of it
-    unsigned row8;       // bytes of 8 output rows
-    unsigned wr_base;    // the lane's write address in the slice (before the chunk XOR)
-    unsigned rd_base;    // its read address for rows 0 .. 7
-    unsigned short* lds_;
-    int first, next;     // chunk stored at step 0 of the current K loop; next chunk due
-
-    __device__ __forceinline__ void init(unsigned short* lds, int lane, int wave) {
-        const unsigned slice = (unsigned)(G::kLds + wave * kSlice);
-        // write: row lane % 32, 8-byte half lane / 32 of a chunk
-        wr_base = slice + (unsigned)((lane & 31) * 128 + 8 * (lane >> 5) + 16 * (lane & 7));
-        // read: row lane / 8 (+ 8 i), logical chunk lane % 8
-        rd_base = slice + (unsigned)((lane >> 3) * 128 + 16 * ((lane & 7) ^ (lane >> 3)));
-        first = next = kChunks;
-        lds_ = lds;
-    }
-    __device__ __forceinline__ void begin() { first = next; }
-    __device__ __forceinline__ int ops(int t) const { return first + t < kChunks ? 1 : 0; }
-    __device__ __forceinline__ void end(int steps) { next = first + steps < kChunks ? first + steps : kChunks; }
-
-    // One row of blocks (bf16(product), in (ni, group) order) into the slice,
-    // through gelu.
-    __device__ __forceinline__ void stage(unsigned short* lds, u32x2 (&b)[G::NI * 4]) {
-#pragma unroll
-        for (int k = 0; k < G::NI * 4; ++k) {   // k = 4 ni + group = logical chunk
-            const u32x2 h = gelu_bf16x4(b[k]);
-            *(u32x2*)((char*)lds + (wr_base ^ (unsigned)(16 * k))) = h;
-        }
-    }
-    // Rows 8 i .. 8 i + 7 of row of blocks mi, from the slice to memory.
-    __device__ __forceinline__ void emit(unsigned short* lds, int mi, int i) {
-        const u32x4 v = *(const u32x4*)((const char*)lds + rd_base + (unsigned)(i * 1024));
-        st16<POL_NT>(v, ov, out_lane + (unsigned)(4 * mi + i) * row8);
-    }
-    // Chunk c (wave-uniform): rows 8 (c % 4) .. of row of blocks kM0 + c / 4.
-    // Row kM0 is staged already; a later one is pend[0 ..] when c % 4 == 0,
-    // staged then, and the remaining registers move up.
-    __device__ __forceinline__ void chunk(unsigned short* lds, int c) {
-        if (c >= 4 && (c & 3) == 0) {
-            u32x2 b[G::NI * 4];
-#pragma unroll
-            for (int k = 0; k < G::NI * 4; ++k) b[k] = pend[k];
-            stage(lds, b);
-#pragma unroll
-            for (int k = 0; k + G::NI * 4 < kPend; ++k) pend[k] = pend[k + G::NI * 4];
-        }
-        emit(lds, kM0 + (c >> 2), c & 3);
-    }
-    __device__ __forceinline__ void issue(int t) { chunk(lds_, first + t); }
-    __device__ __forceinline__ void flush() {
-        for (int c = next; c < kChunks; ++c) chunk(lds_, c);
-        next = kChunks;
-    }
-    // The wave's part of a finished tile: element (0, 0) of the part at
-    // `part` (bf16, row stride ld elements).
-    __device__ __forceinline__ void fill(const f32x16 (&acc)[kMI][G::NI], void* part, int ld, int lane) {
-        ov = tile_view(part, ((long long)(kWM - 1) * ld + G::WN) * 2);
-        unsigned lo = (unsigned)(((lane >> 3) * ld + 8 * (lane & 7)) * 2);
-        asm volatile("" : "+v"(lo));
-        out_lane = lo;
-        row8 = (unsigned)(8 * ld * 2);
-#pragma unroll
-        for (int mi = 0; mi < kMI; ++mi) {
-            u32x2 b[G::NI * 4];
-#pragma unroll
-            for (int ni = 0; ni < G::NI; ++ni)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    b[ni * 4 + g][0] = pack_bf16x2(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1]);
-                    b[ni * 4 + g][1] = pack_bf16x2(acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
-                }
-            if (mi <= kM0) {
-                stage(lds_, b);
-                if (mi < kM0) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) emit(lds_, mi, i);
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < G::NI * 4; ++k) pend[(mi - kM0 - 1) * G::NI * 4 + k] = b[k];
-            }
-        }
-        next = 0;
-    }
-};
 
 // Store a wave's part of a finished tile row-major: element (i, j) of the
 // part goes to ob[i * ld + j], fp32 for EPI_F32 and bf16 otherwise.  With
