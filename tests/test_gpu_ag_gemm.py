@@ -204,6 +204,22 @@ def test_more_column_tiles_than_k_pieces(P, M, N, K, tile_n):
     np.testing.assert_array_equal(gc.view(np.uint32), want_c.view(np.uint32))
 
 
+def test_more_than_64_column_tiles():
+    """A panel of more than 64 column tiles: a tile of phase f >= 2 waits for
+    its panel's flags 64 at a time (one lane per flag).  P = 3 so that phase
+    2 waits; 256 x 128 tiles, N = 8448: 66 column tiles."""
+    P, M, Nn, K = 3, 768, 8448, 64
+    N.set_tuning(gemm_tile_n=128)
+    note("ag_gemm 66 column tiles")
+    rng = np.random.default_rng(571)
+    As = inputs.small_int_bf16(rng, (P, M // P, K))
+    B = inputs.small_int_bf16(rng, (P, K, Nn))
+    gf, gc, _ = _run(As, B)
+    want_full, want_c = oracle.all_gather_gemm(As, B)
+    np.testing.assert_array_equal(gf, want_full)
+    np.testing.assert_array_equal(gc.view(np.uint32), want_c.view(np.uint32))
+
+
 def _random_shapes(seed, count):
     """Seeded shapes the kernel accepts: P of 2..8 (5, 6 and 7 included),
     row blocks of one or two 256-row tiles per rank, N a multiple of 128,
