@@ -219,7 +219,9 @@ int ring_all_reduce(const void *const *src, void *const *dst, int P, size_t n,
  * sum_q A[q] B[q].  The per-rank products are accumulated in fp32 on the
  * matrix cores; the sum over ranks follows the fp32 ring reduce-scatter over
  * row-block chunks (chunk c = rows [c M/P, (c+1) M/P)).
- * Shapes this version accepts: M % (256 P) == 0, N % 128 == 0, K % 64 == 0.
+ * Shapes this version accepts: M % (256 P) == 0, N % 128 == 0, K % 64 == 0,
+ * and K N < 2^30, K < 2^22, N < 2^22 (every view a tile uses, B and 256-row
+ * panels of A and of the output, below 2 GiB); others: RING_EUNSUPPORTED.
  * Output tiles are 256 x 256, 256 x 128 or 256 x 64 (see gemm_tile_n
  * below); results are the same bits either way.
  */
@@ -243,7 +245,9 @@ int gemm_reduce_scatter(const void *const *A, const void *const *B, void *const 
  * A_full buffers must not overlap the shards or each other.  Every workgroup
  * of the launch must be resident at once (the grid is sized for an otherwise
  * idle GPU); a wait that outlives the watchdog ends in RING_ETIMEOUT.
- * Shapes this version accepts: M % (256 P) == 0, N % 128 == 0, K % 64 == 0.
+ * Shapes this version accepts: M % (256 P) == 0, N % 128 == 0, K % 64 == 0,
+ * and K N < 2^30, K < 2^22, N < 2^22 (every view a tile uses, B and 256-row
+ * panels of A and of the output, below 2 GiB); others: RING_EUNSUPPORTED.
  */
 int all_gather_gemm(const void *const *A_shard, const void *const *B, void *const *A_full,
                     void *const *C, int P, int M, int N, int K, void *ws, size_t ws_bytes,
@@ -321,7 +325,7 @@ const char *ring_strerror(int code);
  *                  flags (the "inject a barrier between steps" debugging aid
  *                  of "Triton-distributed 语义", best practice 8).
  *   drop_round     test hook: if >= 1, rank 0 never signals round drop_round
- *                  (all_gather_gemm: never flags its slices of that phase),
+ *                  (all_gather_gemm: never flags its tiles of that phase),
  *                  so the waits on it must end in RING_ETIMEOUT.
  *   gemm_tile_n    output tile width of the fused GEMMs: 128 (two 4-wave
  *                  workgroups per compute unit), 64 (one 4-wave workgroup

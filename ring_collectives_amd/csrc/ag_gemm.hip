@@ -306,6 +306,7 @@ int ag_gemm_run(const void* const* A_shard, const void* const* B, void* const* A
     if (!A_shard || !B || !A_full || !C) return RING_EINVAL;
     if (M == 0 || N == 0) return RING_OK;
     if (M % (kBM * P) || N % 128 || K % 64 || K == 0) return RING_EUNSUPPORTED;
+    if (!gemm_views_fit(N, K)) return RING_EUNSUPPORTED;
     const size_t shard_bytes = (size_t)(M / P) * K * 2, full_bytes = (size_t)M * K * 2;
     for (int r = 0; r < P; ++r) {
         if (!A_shard[r] || !B[r] || !A_full[r] || !C[r]) return RING_EINVAL;

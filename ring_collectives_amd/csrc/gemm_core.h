@@ -102,6 +102,14 @@ __device__ __forceinline__ lds_void* lds_at(unsigned short* lds, unsigned byte) 
     return (lds_void*)((__attribute__((address_space(3))) char*)(lds_void*)lds + byte);
 }
 
+// Every buffer view a tile uses spans less than 2 GiB (a view's size is a
+// 32-bit count): B (K x N bf16), a 256-row panel of A (256 x K bf16) and 128
+// rows of an fp32 output tile or partial (128 x N).
+inline bool gemm_views_fit(int N, int K) {
+    const long long lim = 1LL << 31;
+    return (long long)K * N * 2 < lim && (long long)K * kBM * 2 < lim && (long long)N * kWM * 4 < lim;
+}
+
 // Workgroup barrier for the LDS stages only.  __syncthreads() also fences
 // global memory, for which the compiler drains every outstanding load first
 // (s_waitcnt vmcnt(0)), prefetched stages included, which would serialise the

@@ -250,6 +250,7 @@ int gemm_rs_run(const void* const* A, const void* const* B, void* const* out, in
     if (M == 0 || N == 0) return RING_OK;
     const int chunks = batched ? 1 : P;   // row blocks each rank's product splits into
     if (M % (kBM * chunks) || N % 128 || K % 64 || K == 0) return RING_EUNSUPPORTED;
+    if (!gemm_views_fit(N, K)) return RING_EUNSUPPORTED;
     if (ksplit < 1 || (ksplit > 1 && (!batched || !split || epi != EPI_F32 || K % (64 * ksplit))))
         return RING_EINVAL;
     for (int r = 0; r < P; ++r) {

@@ -225,3 +225,18 @@ def test_noalloc_rejects_bad_arguments_before_the_device():
     assert L.ring_all_reduce_noalloc(a, b, 4, 4097, N.RING_F32, None) == N.RING_EINVAL
     assert L.ring_all_reduce_noalloc(a, b, 4, 4096, 7, None) == N.RING_EUNSUPPORTED
     assert L.ring_all_reduce_noalloc(a, b, 4, 0, N.RING_F32, None) == N.RING_OK
+
+
+def test_gemm_shapes_whose_views_exceed_2_gib_are_refused():
+    """Every buffer view a GEMM tile uses must span less than 2 GiB: B (K x N
+    bf16), a 256-row panel of A, 128 rows of an fp32 output.  Shapes past
+    that are refused before the device is touched (fake pointers)."""
+    L = N.lib()
+    P, M = 2, 512
+    A, ka = _fake([0x10000000 + r * 0x1000000 for r in range(P)])
+    B, kb = _fake([0x40000000 + r * 0x1000000 for r in range(P)])
+    C, kc = _fake([0x70000000 + r * 0x1000000 for r in range(P)])
+    F, kf = _fake([0xA0000000 + r * 0x1000000 for r in range(P)])
+    for Nn, K in ((1024, 1 << 20), (1 << 22, 64), (128, 1 << 22)):
+        assert L.gemm_reduce_scatter(A, B, C, P, M, Nn, K, 0x100000, 1 << 40, None) == N.RING_EUNSUPPORTED
+        assert L.all_gather_gemm(A, B, F, C, P, M, Nn, K, 0x100000, 1 << 40, None) == N.RING_EUNSUPPORTED
