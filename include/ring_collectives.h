@@ -347,7 +347,7 @@ const char *ring_strerror(int code);
  *                  a round costs about half the latency.  Not in stepwise
  *                  mode.
  *   check_flags    debug: 1 makes every flag set (ring rounds, psum,
- *                  GEMM tiles, all-gather slices) an atomic add that
+ *                  GEMM tiles, all-gather panel shares) an atomic add that
  *                  returns the flag's old value, which must be 0 -- each
  *                  flag of a launch is set exactly once and cleared by its
  *                  reader ("全归约 3：Ring——每步大小恒定", Walkthrough: a

@@ -19,7 +19,7 @@
 // two launches is the dependency; inside each launch the collective overlaps
 // its GEMM tile by tile.
 //
-// Workspace: [status | all-gather slice flags | reduce-scatter flags and
+// Workspace: [status | all-gather panel flags | reduce-scatter flags and
 // partial tiles].  Both kernels leave their flag tables zeroed, and the
 // regions are disjoint, so one workspace serves any number of layers.
 //
