@@ -79,6 +79,39 @@ def test_in_place_and_one_rank():
     np.testing.assert_array_equal(bits(to_host(out, "f32")), bits(x[:1]))
 
 
+@pytest.mark.parametrize("kind,P,n", [("f32", 4, 4 * (3 * 4096 + 96)), ("f32", 4, 4 * 4096), ("bf16", 4, 655360)])
+def test_captured_in_a_graph(kind, P, n):
+    """The case the entry point is for: captured in a HIP graph (it records
+    no allocation and no memset; the static array's flags are cleared by a
+    fill kernel) and replayed three times, with an eager call of the same
+    entry point on another, smaller input between replays (the one static
+    array serves both, in stream order); every replay bit for bit against
+    the oracle."""
+    note("noalloc graph %s P=%d n=%d" % (kind, P, n))
+    x = _data(kind, P, n, 972)
+    src, dst = to_dev(x, kind), empty_ranks(P, n, kind)
+    other = _data(kind, 3, 3 * 1000, 973)
+    other_src, other_dst = to_dev(other, kind), empty_ranks(3, 3 * 1000, kind)
+    rc.all_reduce_noalloc(src, dst)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rc.all_reduce_noalloc(src, dst)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in src:
+            t.neg_()                                              # eager input change (exact)
+        for t in dst:
+            t.view(torch.int16 if kind == "bf16" else torch.int32).fill_(-1)
+        rc.all_reduce_noalloc(other_src, other_dst)               # eager call, same static array
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(to_host(dst, kind)), bits(_want(kind, to_host(src, kind))),
+                                      err_msg="replay %d" % rep)
+        np.testing.assert_array_equal(bits(to_host(other_dst, kind)), bits(_want(kind, other)))
+
+
 def test_too_large_is_rejected_before_any_launch():
     """P = 8 with 128 Mi fp32 per rank needs a flag table larger than the
     static array: RING_EWORKSPACE, synchronously; a normal call follows."""
