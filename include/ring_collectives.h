@@ -51,7 +51,13 @@
  * RING_EUNSUPPORTED, RING_EWORKSPACE); a failed HIP launch returns RING_EHIP.
  * A rank that waits for its neighbour longer than the watchdog limit
  * (default 5 s) stops, records RING_ETIMEOUT in the workspace and makes the
- * other ranks stop too; ring_last_error() reports it.  Asynchronous errors
+ * other ranks stop too; ring_last_error() reports it.
+ *
+ * Residency: the ring calls' waves wait only within the ring of one tile
+ * position (P consecutive waves of the launch), so they progress with part
+ * of their grid resident, e.g. beside other kernels on other streams.  The
+ * two fused GEMM calls and tp_mlp_layer need every workgroup of a launch
+ * resident at once (their grids are sized for an otherwise idle GPU).  Asynchronous errors
  * (RING_ETIMEOUT, RING_EWORKSPACE from the record above, RING_EPROTOCOL
  * from the debug check_flags knob) leave the outputs undefined; the
  * workspace must then be re-initialised.
@@ -223,7 +229,9 @@ int ring_all_reduce(const void *const *src, void *const *dst, int P, size_t n,
  * and K N < 2^30, K < 2^22, N < 2^22 (every view a tile uses, B and 256-row
  * panels of A and of the output, below 2 GiB); others: RING_EUNSUPPORTED.
  * Output tiles are 256 x 256, 256 x 128 or 256 x 64 (see gemm_tile_n
- * below); results are the same bits either way.
+ * below); results are the same bits either way.  Every workgroup of the
+ * launch must be resident at once (the grid is sized for an otherwise idle
+ * GPU); a wait that outlives the watchdog ends in RING_ETIMEOUT.
  */
 int gemm_reduce_scatter(const void *const *A, const void *const *B, void *const *out,
                         int P, int M, int N, int K, void *ws, size_t ws_bytes,

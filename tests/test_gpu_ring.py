@@ -403,3 +403,45 @@ def test_side_stream_with_a_fresh_workspace():
     side.synchronize()
     np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.all_reduce(x)))
     assert rc.last_error(ws, stream=side)[0] == 0
+
+
+def test_ring_calls_overlap_compute_on_other_streams():
+    """Ring calls on side streams while a chain of vendor GEMMs occupies the
+    main stream.  The ring kernels' waits stay within a tile position's ring
+    of P consecutive waves, so every prefix of a launch's dispatch order
+    holds complete rings and a call progresses with only part of its grid
+    resident: the all-reduce, the bidirectional reduce-scatter and the
+    circulating psum, each on its own stream, must give the oracle's bits
+    and no watchdog error while the GEMMs run."""
+    P, n = 8, 8 * (1 << 20)
+    note("ring calls beside GEMMs on other streams")
+    x = inputs.normal_f32(P, n, seed=1380)
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    calls = [(rc.all_reduce, N.OP_ALL_REDUCE, oracle.all_reduce),
+             (rc.reduce_scatter_bidir, N.OP_REDUCE_SCATTER_BIDIR, oracle.reduce_scatter_bidir),
+             (rc.psum_circulating, N.OP_PSUM_CIRCULATING, lambda v: oracle.psum_circulating(v)[0])]
+    runs = []
+    for fn, op, ref in calls:
+        src, dst = to_dev(x, "f32"), empty_ranks(P, n, "f32")
+        runs.append((fn, ref, src, dst, rc.workspace(op, P, n, torch.float32), torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(main)
+    for _ in range(12):
+        c = a @ b
+    t1.record(main)
+    ends = []
+    for fn, _, src, dst, ws, s in runs:
+        fn(src, dst, ws=ws, stream=s)
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(s)
+        ends.append(e)
+    torch.cuda.synchronize()
+    note("GEMM chain %.2f ms; ring calls ended at %s ms after its start"
+         % (t0.elapsed_time(t1), ", ".join("%.2f" % t0.elapsed_time(e) for e in ends)))
+    del c
+    for fn, ref, src, dst, ws, s in runs:
+        assert rc.last_error(ws, stream=s)[0] == 0
+        np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(ref(x)), err_msg=fn.__name__)
