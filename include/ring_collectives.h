@@ -55,9 +55,12 @@
  *
  * Residency: the ring calls' waves wait only within the ring of one tile
  * position (P consecutive waves of the launch), so they progress with part
- * of their grid resident, e.g. beside other kernels on other streams.  The
- * two fused GEMM calls and tp_mlp_layer need every workgroup of a launch
- * resident at once (their grids are sized for an otherwise idle GPU).  Asynchronous errors
+ * of their grid resident, e.g. beside other kernels on other streams.  In
+ * the two fused GEMM calls and tp_mlp_layer, workgroups wait for other
+ * workgroups of the same launch, so all of them must get to run: beside a
+ * kernel that holds part of the GPU a launch is delayed until that kernel's
+ * workgroups finish (within the watchdog limit), and two such calls must
+ * not run at once on different streams.  Asynchronous errors
  * (RING_ETIMEOUT, RING_EWORKSPACE from the record above, RING_EPROTOCOL
  * from the debug check_flags knob) leave the outputs undefined; the
  * workspace must then be re-initialised.
@@ -229,9 +232,9 @@ int ring_all_reduce(const void *const *src, void *const *dst, int P, size_t n,
  * and K N < 2^30, K < 2^22, N < 2^22 (every view a tile uses, B and 256-row
  * panels of A and of the output, below 2 GiB); others: RING_EUNSUPPORTED.
  * Output tiles are 256 x 256, 256 x 128 or 256 x 64 (see gemm_tile_n
- * below); results are the same bits either way.  Every workgroup of the
- * launch must be resident at once (the grid is sized for an otherwise idle
- * GPU); a wait that outlives the watchdog ends in RING_ETIMEOUT.
+ * below); results are the same bits either way.  Workgroups wait for
+ * other workgroups of the launch (see Residency above); a wait that
+ * outlives the watchdog ends in RING_ETIMEOUT.
  */
 int gemm_reduce_scatter(const void *const *A, const void *const *B, void *const *out,
                         int P, int M, int N, int K, void *ws, size_t ws_bytes,
@@ -250,9 +253,9 @@ int gemm_reduce_scatter(const void *const *A, const void *const *B, void *const 
  * accumulated in fp32 on the matrix cores.  The blocks travel the ring of
  * ring_all_gather (rank r receives block (r - t - 1) mod P in round t); rank
  * r's GEMM handles block r first, then the blocks in the order they arrive.
- * A_full buffers must not overlap the shards or each other.  Every workgroup
- * of the launch must be resident at once (the grid is sized for an otherwise
- * idle GPU); a wait that outlives the watchdog ends in RING_ETIMEOUT.
+ * A_full buffers must not overlap the shards or each other.  Workgroups
+ * wait for other workgroups of the launch (see Residency above); a wait
+ * that outlives the watchdog ends in RING_ETIMEOUT.
  * Shapes this version accepts: M % (256 P) == 0, N % 128 == 0, K % 64 == 0,
  * and K N < 2^30, K < 2^22, N < 2^22 (every view a tile uses, B and 256-row
  * panels of A and of the output, below 2 GiB); others: RING_EUNSUPPORTED.

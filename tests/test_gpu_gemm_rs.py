@@ -275,3 +275,30 @@ def test_random_shapes_integer_exact(P, M, N, K):
     got, _ = _run(A, B)
     want = oracle.gemm_reduce_scatter(A, B)
     np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_beside_vendor_gemms_on_another_stream():
+    """GEMM + RS on a side stream while a chain of vendor GEMMs holds the
+    GPU: its workgroups that start first wait for the rest, which start as
+    the other kernel's workgroups finish, so the call is only delayed (well
+    within the watchdog); integer-valued operands, every element exact."""
+    P, M, Nn, K = 4, 2048, 1024, 512
+    note("gemm_rs beside vendor GEMMs on another stream")
+    rng = np.random.default_rng(1390)
+    A = inputs.small_int_bf16(rng, (P, M, K))
+    B = inputs.small_int_bf16(rng, (P, K, Nn))
+    a, b = _dev_bf16(A), _dev_bf16(B)
+    out = [torch.full((M // P, Nn), float("nan"), dtype=torch.float32, device="cuda") for _ in range(P)]
+    ws = rc.workspace(N.OP_GEMM_REDUCE_SCATTER, P, M * Nn, torch.float32)
+    x = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(8):
+        z = x @ y
+    rc.gemm_reduce_scatter(a, b, out, ws=ws, stream=side)
+    torch.cuda.synchronize()
+    del z
+    assert rc.last_error(ws, stream=side)[0] == 0
+    got = np.stack([o.cpu().numpy() for o in out])
+    np.testing.assert_array_equal(got.view(np.uint32), oracle.gemm_reduce_scatter(A, B).view(np.uint32))
