@@ -285,8 +285,10 @@ static int run_ring(const void* const* src, void* const* dst, int P, size_t n, i
                             extra);
     prm.check_flags = tu.check_flags;
 
-    // Grid: every wave must be resident at once (waves wait on each other).
-    // Stay within half the occupancy limit: margin for anything else resident.
+    // Grid: a wave waits only for waves of its own ring (P consecutive waves
+    // of the dispatch order), so the launch progresses with part of it
+    // resident.  Stay within half the occupancy limit: margin for anything
+    // else resident.
     int occ = cached_blocks_per_cu(dtype, tu.tile_vecs, ll ? 3 : bidir);
     if (occ < 1) return RING_EHIP;
     int bpc = (tu.waves_per_cu + kWavesPerBlock - 1) / kWavesPerBlock;
