@@ -172,6 +172,28 @@ def test_zero_size_is_noop():
     assert L.ring_all_reduce(a, b, 4, 0, N.RING_BF16, 0x100000, 1 << 30, None) == N.RING_OK
 
 
+def test_zero_size_fused_and_two_way_calls_are_noops():
+    """M = 0 or N = 0 for the fused GEMMs and the MLP layer, n = 0 for the
+    bidirectional reduce-scatter and the circulating psum: RING_OK with no
+    launch (the device pointers here are never touched)."""
+    L = N.lib()
+    P = 4
+    a, ka = _fake([0x10000000 + r * 0x1000000 for r in range(P)])
+    b, kb = _fake([0x20000000 + r * 0x1000000 for r in range(P)])
+    c, kc = _fake([0x30000000 + r * 0x1000000 for r in range(P)])
+    d, kd = _fake([0x40000000 + r * 0x1000000 for r in range(P)])
+    e, ke = _fake([0x50000000 + r * 0x1000000 for r in range(P)])
+    f, kf = _fake([0x60000000 + r * 0x1000000 for r in range(P)])
+    ws, wsb = 0x100000, 1 << 30
+    assert L.ring_reduce_scatter_bidir(a, b, P, 0, N.RING_F32, ws, wsb, None) == N.RING_OK
+    assert L.ring_psum_circulating(a, b, P, 0, N.RING_BF16, ws, wsb, None) == N.RING_OK
+    for M, Nn in ((0, 256), (1024, 0)):
+        assert L.gemm_reduce_scatter(a, b, c, P, M, Nn, 64, ws, wsb, None) == N.RING_OK
+        assert L.all_gather_gemm(a, b, c, d, P, M, Nn, 64, ws, wsb, None) == N.RING_OK
+    for M, D, F in ((0, 256, 512), (1024, 0, 512), (1024, 256, 0)):
+        assert L.tp_mlp_layer(a, b, c, d, e, f, P, M, D, F, ws, wsb, None) == N.RING_OK
+
+
 def test_ppermute_rejects_in_place():
     a, ka = _fake([0x10000000 + r * 0x1000000 for r in range(4)])
     assert N.lib().ring_ppermute(a, a, 4, 64, N.RING_F32, None) == N.RING_EINVAL
