@@ -37,11 +37,22 @@ def _ranks(ts: Sequence[torch.Tensor], what: str, numel: int | None = None, dtyp
     for t in ts:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("%s: rank buffers must be contiguous device tensors" % what)
+        if t.device != ts[0].device:
+            raise ValueError("%s: every rank buffer must be on one device" % what)
         if numel is not None and t.numel() != numel:
             raise ValueError("%s: every rank buffer needs %d elements" % (what, numel))
         if dtype is not None and t.dtype != dtype:
             raise TypeError("%s: mixed dtypes" % what)
     return [t.data_ptr() for t in ts]
+
+
+def _wsarg(ws: torch.Tensor, what: str):
+    """(device pointer, size in bytes) of a caller's workspace tensor; a
+    host tensor or a strided view is refused here, before the library could
+    hand the kernels an address they cannot use."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("%s: the workspace must be a contiguous device tensor" % what)
+    return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
 def workspace_bytes(op: int, P: int, n: int, dtype: torch.dtype = torch.float32) -> int:
@@ -96,7 +107,7 @@ def _rs_ar(fn, name, op, src, dst, ws, stream):
     ws = _ws(ws, op, P, n, src[0].dtype, src[0].device, stream)
     a, ka = N.ptr_array(ps)
     b, kb = N.ptr_array(pd)
-    N.check(fn(a, b, P, n, _dtype(src[0]), ws.data_ptr(), ws.numel(), _stream(stream)), name)
+    N.check(fn(a, b, P, n, _dtype(src[0]), *_wsarg(ws, name), _stream(stream)), name)
     return ws
 
 
@@ -159,7 +170,7 @@ def all_gather(dst, src=None, ws=None, stream=None):
         a = None
     ws = _ws(ws, N.OP_ALL_GATHER, P, n, dst[0].dtype, dst[0].device, stream)
     b, kb = N.ptr_array(pd)
-    N.check(N.lib().ring_all_gather(a, b, P, n, _dtype(dst[0]), ws.data_ptr(), ws.numel(),
+    N.check(N.lib().ring_all_gather(a, b, P, n, _dtype(dst[0]), *_wsarg(ws, "ring_all_gather"),
                                     _stream(stream)), "ring_all_gather")
     return ws
 
@@ -180,7 +191,7 @@ def gemm_reduce_scatter(A, B, out, ws=None, stream=None):
     a, ka = N.ptr_array(pa)
     b, kb = N.ptr_array(pb)
     o, ko = N.ptr_array(po)
-    N.check(N.lib().gemm_reduce_scatter(a, b, o, P, M, Nn, K, ws.data_ptr(), ws.numel(),
+    N.check(N.lib().gemm_reduce_scatter(a, b, o, P, M, Nn, K, *_wsarg(ws, "gemm_reduce_scatter"),
                                         _stream(stream)), "gemm_reduce_scatter")
     return ws
 
@@ -205,7 +216,7 @@ def all_gather_gemm(A_shard, B, A_full, C, ws=None, stream=None):
     b, kb = N.ptr_array(pb)
     f, kf = N.ptr_array(pf)
     c, kc = N.ptr_array(pc)
-    N.check(N.lib().all_gather_gemm(a, b, f, c, P, M, Nn, K, ws.data_ptr(), ws.numel(),
+    N.check(N.lib().all_gather_gemm(a, b, f, c, P, M, Nn, K, *_wsarg(ws, "all_gather_gemm"),
                                     _stream(stream)), "all_gather_gemm")
     return ws
 
@@ -237,7 +248,7 @@ def tp_mlp_layer(x_shard, W1, W2, x_full, h, out, ws=None, stream=None):
     if ws is None:
         ws = _ordered(tp_mlp_workspace(P, M, D, F, device=x_shard[0].device), stream)
     arrs = [N.ptr_array(p_) for p_ in ptrs]
-    N.check(N.lib().tp_mlp_layer(*[a_ for a_, _ in arrs], P, M, D, F, ws.data_ptr(), ws.numel(),
+    N.check(N.lib().tp_mlp_layer(*[a_ for a_, _ in arrs], P, M, D, F, *_wsarg(ws, "tp_mlp_layer"),
                                  _stream(stream)), "tp_mlp_layer")
     return ws
 
@@ -246,10 +257,10 @@ def last_error(ws: torch.Tensor, stream=None):
     """(code, info) left in a workspace by the last kernel (synchronises)."""
     import ctypes
     info = ctypes.c_int(0)
-    code = N.lib().ring_last_error(ws.data_ptr(), ws.numel(), _stream(stream), ctypes.byref(info))
+    code = N.lib().ring_last_error(*_wsarg(ws, "ring_last_error"), _stream(stream), ctypes.byref(info))
     return int(code), int(info.value)
 
 
 def workspace_init(ws: torch.Tensor, stream=None) -> None:
-    N.check(N.lib().ring_workspace_init(ws.data_ptr(), ws.numel(), _stream(stream)),
+    N.check(N.lib().ring_workspace_init(*_wsarg(ws, "ring_workspace_init"), _stream(stream)),
             "ring_workspace_init")

@@ -445,3 +445,22 @@ def test_ring_calls_overlap_compute_on_other_streams():
     for fn, ref, src, dst, ws, s in runs:
         assert rc.last_error(ws, stream=s)[0] == 0
         np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(ref(x)), err_msg=fn.__name__)
+
+
+def test_binding_refuses_a_workspace_the_kernels_cannot_use():
+    """A host tensor or a strided view as the workspace is refused by the
+    binding before any call; a workspace of another element type is passed
+    with its size in bytes."""
+    P, n = 4, 4 * 4096
+    note("binding workspace checks")
+    x = inputs.normal_f32(P, n, seed=1395)
+    src, dst = to_dev(x, "f32"), empty_ranks(P, n, "f32")
+    nb = rc.workspace_bytes(N.OP_ALL_REDUCE, P, n, torch.float32)
+    with pytest.raises(ValueError):
+        rc.all_reduce(src, dst, ws=torch.zeros(nb, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        rc.all_reduce(src, dst, ws=torch.zeros(2 * nb, dtype=torch.uint8, device="cuda")[::2])
+    ws32 = torch.zeros((nb + 3) // 4, dtype=torch.int32, device="cuda")
+    rc.all_reduce(src, dst, ws=ws32)
+    assert rc.last_error(ws32)[0] == 0
+    np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.all_reduce(x)))
