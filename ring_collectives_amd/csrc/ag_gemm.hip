@@ -26,8 +26,9 @@
 //
 // Progress.  A phase-f tile waits only for phase f - 1 tiles of the left
 // rank, and every workgroup finishes its tiles of phase f - 1 before it
-// starts phase f; so by induction on f every tile finishes, provided all
-// workgroups are resident (the grid is sized so).  A flag has the tn tiles
+// starts phase f; so by induction on f every tile finishes, provided every
+// workgroup gets to run (the grid is sized for the CUs; beside another
+// kernel the rest start as its workgroups finish).  A flag has the tn tiles
 // of the right rank's panel for readers, so readers leave it set and the last
 // workgroup to finish clears the table for the next call.
 #include "gemm_core.h"
@@ -280,8 +281,9 @@ template <class G, bool GELU>
 static int launch_ag_gemm(AgGemmParams& prm, const DevInfo& di, hipStream_t stream) {
     prm.tn = prm.N / G::BN;
     prm.tpc = prm.tm_chunk * prm.tn;
-    // every workgroup must be resident (tiles wait for the left rank's tiles
-    // of the previous phase)
+    // at most G::kWGsPerCU workgroups per CU, so on an otherwise idle GPU
+    // every workgroup runs at once (tiles wait for the left rank's tiles of
+    // the previous phase); the occupancy query confirms the hardware agrees
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ag_gemm_kernel<G, GELU>, 64 * G::NW, 0) != hipSuccess ||
         occ < G::kWGsPerCU)

@@ -24,10 +24,10 @@
 // are exactly the ring reduce-scatter's: ((C_{c+1} + C_{c+2}) + ...) + C_c.
 //
 // Tiles.  One workgroup computes one 256 x BN fp32 output tile (256 x 256
-// with 8 waves, one workgroup per CU, or 256 x 128 or 256 x 64 with 4 waves,
-// two per CU)
-// with v_mfma_f32_32x32x16_bf16; every wave owns a 128 x 64 part as 32 x 32
-// MFMA blocks.  K advances through LDS buffers filled by direct global->LDS
+// with 8 waves, one workgroup per CU; 256 x 128 with 4 waves, two per CU;
+// 256 x 64 with 4 waves, one per CU) with v_mfma_f32_32x32x16_bf16; every
+// wave owns a 128 x 64 part (128 x 32 for the narrowest) as 32 x 32 MFMA
+// blocks.  K advances through LDS buffers filled by direct global->LDS
 // loads one step ahead of the buffers the matrix cores read.  Partial tiles
 // travel through the workspace in MFMA fragment order (what one instruction
 // of a wave moves is 1 KiB of contiguous memory), and a flag guards each
@@ -38,10 +38,11 @@
 // by phase, position by position, the P ranks of a position consecutive, and
 // workgroup g of G takes items g, g + G, g + 2G, ...  An item waits only for
 // the left rank's item at the same position of the phase before, which has
-// a smaller number.  Every workgroup is resident (G is at most what the CUs
-// hold) and works through its items in increasing order, so the smallest
-// unfinished item always has its input ready and its workgroup at it: the
-// launch always finishes.  Numbering across phases lets a small problem
+// a smaller number.  Every workgroup gets to run (G is at most what the CUs
+// hold; beside another kernel the rest start as its workgroups finish) and
+// works through its items in increasing order, so the smallest unfinished
+// item always has its input ready and its workgroup at it: the launch always
+// finishes.  Numbering across phases lets a small problem
 // (fewer tiles per chunk than workgroup slots) run several phases at once.
 #include "gemm_core.h"
 
@@ -226,8 +227,9 @@ template <class G>
 static int launch_gemm_rs(GemmParams& prm, const DevInfo& di, hipStream_t stream) {
     prm.tn = prm.N / G::BN;
     prm.tpc = prm.tm_chunk * prm.tn;
-    // at most G::kWGsPerCU workgroups per CU, so every workgroup is resident;
-    // the occupancy query confirms the hardware agrees
+    // at most G::kWGsPerCU workgroups per CU, so on an otherwise idle GPU
+    // every workgroup runs at once; the occupancy query confirms the
+    // hardware agrees
     int occ = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, gemm_rs_kernel<G>, 64 * G::NW, 0) != hipSuccess ||
         occ < G::kWGsPerCU)
