@@ -243,3 +243,17 @@ def test_random_shapes_integer_exact(P, M, N, K):
     want_full, want_c = oracle.all_gather_gemm(As, B)
     np.testing.assert_array_equal(gf, want_full)
     np.testing.assert_array_equal(gc.view(np.uint32), want_c.view(np.uint32))
+
+
+@pytest.mark.parametrize("P,M,N,K", [(16, 4096, 256, 128), (32, 8192, 128, 64), (64, 16384, 128, 64)])
+def test_many_ranks_integer_exact(P, M, N, K):
+    """16, 32 and 64 ranks (the library's maximum): the gathered A and every
+    bit of C against the oracle."""
+    note("ag_gemm many ranks P=%d M=%d N=%d K=%d" % (P, M, N, K))
+    rng = np.random.default_rng(1430 + P)
+    As = inputs.small_int_bf16(rng, (P, M // P, K))
+    B = inputs.small_int_bf16(rng, (P, K, N))
+    gf, gc, _ = _run(As, B)
+    want_full, want_c = oracle.all_gather_gemm(As, B)
+    np.testing.assert_array_equal(gf, want_full)
+    np.testing.assert_array_equal(gc.view(np.uint32), want_c.view(np.uint32))

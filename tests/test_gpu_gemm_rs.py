@@ -34,8 +34,8 @@ def _needs_gpu():
 
 @pytest.fixture(params=[64, 128, 256])
 def tile_n(request):
-    """Every output tile width: 256 x 64 and 256 x 128 (two workgroups per
-    compute unit) and 256 x 256 (one)."""
+    """Every output tile width: 256 x 64 (one workgroup per compute unit),
+    256 x 128 (two) and 256 x 256 (one)."""
     old = N.set_tuning(gemm_tile_n=request.param)
     yield request.param
     N.set_tuning(gemm_tile_n=old["gemm_tile_n"])
@@ -301,4 +301,16 @@ def test_beside_vendor_gemms_on_another_stream():
     del z
     assert rc.last_error(ws, stream=side)[0] == 0
     got = np.stack([o.cpu().numpy() for o in out])
+    np.testing.assert_array_equal(got.view(np.uint32), oracle.gemm_reduce_scatter(A, B).view(np.uint32))
+
+
+@pytest.mark.parametrize("P,M,N,K", [(16, 4096, 256, 128), (32, 8192, 128, 64), (64, 16384, 128, 64)])
+def test_many_ranks_integer_exact(P, M, N, K):
+    """16, 32 and 64 ranks (the library's maximum), one 256-row tile per rank
+    and chunk, the automatic tile width: every bit against the oracle."""
+    note("gemm_rs many ranks P=%d M=%d N=%d K=%d" % (P, M, N, K))
+    rng = np.random.default_rng(1420 + P)
+    A = inputs.small_int_bf16(rng, (P, M, K))
+    B = inputs.small_int_bf16(rng, (P, K, N))
+    got, _ = _run(A, B)
     np.testing.assert_array_equal(got.view(np.uint32), oracle.gemm_reduce_scatter(A, B).view(np.uint32))

@@ -408,3 +408,16 @@ def test_plain_normal_operands(P, M, D, F):
     print("h equal to the oracle's: %.5f, out equal: %.5f" % (h_same, o_same))
     assert h_same >= 0.999, h_same
     assert o_same >= 0.98, o_same
+
+
+@pytest.mark.parametrize("P,M,D,F", [(16, 4096, 128, 2048), (32, 8192, 128, 4096)])
+def test_many_ranks_integer_exact(P, M, D, F):
+    """16 and 32 ranks, the fused path (one 256-row tile per rank): the
+    gathered input, h and the output bit for bit."""
+    note("tp_mlp many ranks P=%d M=%d D=%d F=%d" % (P, M, D, F))
+    x, w1, w2 = _int_operands(P, M, D, F, seed=1440 + P)
+    gf, gh, go, _ = _run(x, w1, w2)
+    full, h, out = oracle.tp_mlp_layer(x, w1, w2)
+    np.testing.assert_array_equal(gf, full)
+    np.testing.assert_array_equal(gh, h)
+    np.testing.assert_array_equal(go, out)
