@@ -79,6 +79,14 @@ def build(verbose: bool = False) -> str:
     if verbose and dropped + nd:
         print("(%d host-pass notes about the device-only packed-fp32 switch not shown)" % (dropped + nd),
               flush=True)
+    # A kernel template the host pass failed to instantiate leaves no error,
+    # only an object without it and a library whose launch stubs refer to an
+    # undefined symbol; refuse such a library here rather than at load time.
+    und = subprocess.run(["nm", "-D", "--undefined-only", tmp], stdout=subprocess.PIPE, text=True).stdout
+    missing = [ln.split()[-1] for ln in und.splitlines() if ln.split() and ln.split()[-1].startswith("_ZN5ringc")]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("build: the library leaves its own symbols undefined: %s" % ", ".join(missing))
     os.replace(tmp, LIB)
     return LIB
 
