@@ -421,3 +421,26 @@ def test_many_ranks_integer_exact(P, M, D, F):
     np.testing.assert_array_equal(gf, full)
     np.testing.assert_array_equal(gh, h)
     np.testing.assert_array_equal(go, out)
+
+
+def test_single_layer_form_at_the_chapter_shape():
+    """The chapter's single-layer form ends with an all-gather of the output
+    shards (every device holds the layer's whole output): tp_mlp_layer, then
+    ring_all_gather of its shards, at x [256, 1024], W1 [1024, 16384],
+    W2 [16384, 1024], P = 4, on integer-valued operands; every rank's copy
+    of the output bit for bit against the oracle's shards in rank order."""
+    P, M, D, F = 4, 256, 1024, 16384
+    note("tp_mlp single-layer form P=%d M=%d D=%d F=%d" % (P, M, D, F))
+    x, w1, w2 = _int_operands(P, M, D, F, seed=650)
+    _, _, go, ws = _run(x, w1, w2)
+    Mq = M // P
+    shards = [torch.from_numpy(np.ascontiguousarray(go[r]).view(np.int16)).cuda().view(torch.bfloat16)
+              for r in range(P)]
+    whole = [_nan_bf16((M * D,)) for _ in range(P)]
+    ag_ws = rc.all_gather(whole, src=[s.reshape(-1) for s in shards])
+    torch.cuda.synchronize()
+    assert rc.last_error(ag_ws)[0] == 0
+    _, _, out = oracle.tp_mlp_layer(x, w1, w2)
+    want = out.reshape(P * Mq, D)
+    for r in range(P):
+        np.testing.assert_array_equal(whole[r].view(torch.int16).cpu().numpy().view(np.uint16).reshape(M, D), want)
