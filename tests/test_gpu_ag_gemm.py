@@ -257,3 +257,30 @@ def test_many_ranks_integer_exact(P, M, N, K):
     want_full, want_c = oracle.all_gather_gemm(As, B)
     np.testing.assert_array_equal(gf, want_full)
     np.testing.assert_array_equal(gc.view(np.uint32), want_c.view(np.uint32))
+
+
+def test_repeated_calls_with_new_inputs_on_the_same_buffers(tile_n):
+    """Three calls, each with new shards and weights, into the same gathered
+    buffers, outputs and workspace: the tiles of phases 2 and up read the
+    gathered rows with ordinary (cached) loads, so every call must see the
+    rows its own launch forwarded, not what an earlier call left there.
+    K = 192 splits the forwarding shares inside 128-byte lines (48 or 96
+    elements per column tile), so lines are written piecewise by several
+    tiles before they are read."""
+    P, M, Nn, K = 4, 1024, 512, 192
+    note("ag_gemm repeated calls with new inputs tile_n=%d" % tile_n)
+    full = [torch.empty((M, K), dtype=torch.bfloat16, device="cuda") for _ in range(P)]
+    C = [torch.empty((M, Nn), dtype=torch.float32, device="cuda") for _ in range(P)]
+    ws = None
+    for call in range(3):
+        rng = np.random.default_rng(1450 + call)
+        As = inputs.small_int_bf16(rng, (P, M // P, K))
+        B = inputs.small_int_bf16(rng, (P, K, Nn))
+        ws = rc.all_gather_gemm(_dev_bf16(As), _dev_bf16(B), full, C, ws=ws)
+        torch.cuda.synchronize()
+        assert rc.last_error(ws)[0] == 0
+        want_full, want_c = oracle.all_gather_gemm(As, B)
+        gf = np.stack([t.view(torch.int16).cpu().numpy().view(np.uint16) for t in full])
+        gc = np.stack([t.cpu().numpy() for t in C])
+        np.testing.assert_array_equal(gf, want_full, err_msg="call %d" % call)
+        np.testing.assert_array_equal(gc.view(np.uint32), want_c.view(np.uint32), err_msg="call %d" % call)
