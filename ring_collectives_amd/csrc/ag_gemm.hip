@@ -215,11 +215,8 @@ __device__ void ag_gemm_body(const AgGemmParams& p, unsigned short* lds) {
                 // flags), and no cache on the way holds an older copy: a
                 // launch starts with every L2 invalidated, and in a launch
                 // these rows are read only here, in this phase, after the
-                // flags.  So the loads may be ordinary ones, which let the tn
-                // tiles of the panel share the rows in their XCD's L2
-                // (measured: the MLP layer 1.5-2.5% faster than with
-                // device-scope loads that go to the coherence point every
-                // time).
+                // flags.  So the loads may be ordinary ones (measured: the
+                // MLP layer 1.5-2.5% faster than with device-scope loads).
                 if (!wg_wait(p, ag_flag(p, f - 1, left, pr * p.tn), p.tn, wave, lane, q, f, pos)) return;
                 gemm_tile_with<G, POL_PLAIN>(p.K, p.N, p.Af[left], p.B[q], c * p.tm_chunk + pr, tc, acc, lds, lane,
                                              wave, wr, wc, fw);
