@@ -464,3 +464,55 @@ def test_binding_refuses_a_workspace_the_kernels_cannot_use():
     rc.all_reduce(src, dst, ws=ws32)
     assert rc.last_error(ws32)[0] == 0
     np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.all_reduce(x)))
+
+
+@pytest.mark.parametrize("n", [4 * 1000, 4 * (3 * 4096 + 77)])
+def test_every_collective_on_buffers_4_bytes_off_alignment(n):
+    """Rank buffers that start 4 bytes past a 16-byte boundary (views at
+    element 1 of larger allocations) take the element-wise path: every
+    collective, in the low-latency rounds (small n) and the flag rounds,
+    bit for bit against the oracle."""
+    P = 4
+    note("unaligned bases n=%d" % n)
+    x = inputs.normal_f32(P, n, seed=1460 + n % 97)
+
+    def views(a=None):
+        out = []
+        for r in range(P):
+            big = torch.full((n + 4,), float("nan"), dtype=torch.float32, device="cuda")
+            v = big[1:n + 1]
+            if a is not None:
+                v.copy_(torch.from_numpy(np.ascontiguousarray(a[r])).cuda())
+            out.append(v)
+        return out
+
+    src = views(x)
+    assert all(t.data_ptr() % 16 == 4 for t in src)
+    C = n // P
+    dst = views()
+    rc.ppermute(src, dst)
+    np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.ppermute(x)))
+    dst = views()
+    rc.all_reduce(src, dst)
+    np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.all_reduce(x)))
+    dst = views()
+    rc.reduce_scatter(src, dst)
+    got, want = to_host(dst, "f32"), oracle.reduce_scatter(x)
+    for r, c in rs_written_chunks(P):
+        np.testing.assert_array_equal(bits(got[r, c * C:(c + 1) * C]), bits(want[r, c * C:(c + 1) * C]))
+    pieces = np.stack([x[r, r * C:(r + 1) * C] for r in range(P)])
+    psrc = []
+    for r in range(P):
+        big = torch.zeros(C + 4, dtype=torch.float32, device="cuda")
+        v = big[1:C + 1]
+        v.copy_(torch.from_numpy(pieces[r]).cuda())
+        psrc.append(v)
+    dst = views()
+    rc.all_gather(dst, src=psrc)
+    np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.all_gather_pieces(pieces)))
+    dst = views()
+    rc.reduce_scatter_bidir(src, dst)
+    np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.reduce_scatter_bidir(x)))
+    dst = views()
+    rc.psum_circulating(src, dst)
+    np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.psum_circulating(x)[0]))
