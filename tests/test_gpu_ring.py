@@ -516,3 +516,42 @@ def test_every_collective_on_buffers_4_bytes_off_alignment(n):
     dst = views()
     rc.psum_circulating(src, dst)
     np.testing.assert_array_equal(bits(to_host(dst, "f32")), bits(oracle.psum_circulating(x)[0]))
+
+
+@pytest.mark.parametrize("n", [4 * 2000, 4 * (3 * 8192 + 77)])
+def test_bf16_collectives_on_buffers_2_bytes_off_alignment(n):
+    """bf16 rank buffers that start 2 bytes past a 16-byte boundary: the
+    fp32 carry's element-wise path in every collective that adds, in the
+    low-latency and the flag rounds, bit for bit against the oracle (the
+    reduce-scatters on the owners' chunks)."""
+    P = 4
+    note("bf16 unaligned bases n=%d" % n)
+    x = inputs.normal_bf16(P, n, seed=1470 + n % 89)
+
+    def views(a=None):
+        out = []
+        for r in range(P):
+            big = torch.full((n + 8,), 0x7FC1, dtype=torch.int16, device="cuda")
+            v = big[1:n + 1]
+            if a is not None:
+                v.copy_(torch.from_numpy(np.ascontiguousarray(a[r]).view(np.int16)).cuda())
+            out.append(v.view(torch.bfloat16))
+        return out
+
+    src = views(x)
+    assert all(t.data_ptr() % 16 == 2 for t in src)
+    C = n // P
+    dst = views()
+    rc.all_reduce(src, dst)
+    np.testing.assert_array_equal(to_host(dst, "bf16"), oracle.all_reduce_bf16(x))
+    for fn, ref in ((rc.reduce_scatter, lambda v: oracle.reduce_scatter_bf16(v)[0]),
+                    (rc.reduce_scatter_bidir, lambda v: oracle.reduce_scatter_bidir_bf16(v)[0])):
+        dst = views()
+        fn(src, dst)
+        got, want = to_host(dst, "bf16"), ref(x)
+        for r in range(P):
+            np.testing.assert_array_equal(got[r, r * C:(r + 1) * C], want[r, r * C:(r + 1) * C],
+                                          err_msg="%s rank %d" % (fn.__name__, r))
+    dst = views()
+    rc.psum_circulating(src, dst)
+    np.testing.assert_array_equal(to_host(dst, "bf16"), oracle.psum_circulating_bf16(x))
